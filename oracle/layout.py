@@ -12,17 +12,24 @@ Specification in brief:
 * A slot holds the heads in order; head h starts at byte head_off[h], every
   head is padded to a multiple of 256 bytes and slot_bytes = head_off[H].
   All multi-byte values are little-endian.
-* A code row of d_v codes at b bits takes d_v*b/8 bytes; code j occupies
-  bits [j*b, j*b+b) of the row, bit n being bit (n mod 8) of byte n//8;
-  the field is z in b-bit two's complement.  An FP16 row takes 2*d_v bytes.
-* uniform head: d_k code rows, then d_k FP16 row scales s.
-* STEP GDN head (b in {2,4,6,8}): d_k code rows, d_k FP16 r, d_v FP16 c.
-  Pivot head (b = 16): d_k FP16 rows and nothing else.
+* Tile-uniform code regions (uniform heads, STEP GDN heads including FP16
+  pivot heads, the window's INT8 boundary) use a column-pair blocked order:
+  row block rb = 32 rows, column pair p; the chunk (rb, p) holds value
+  n = 2m + c = element (32 rb + m, 2 p + c) at bits [n b, n b + b) of a
+  little-endian bit stream of 8 b bytes, cut into b/2 pieces of 16 bytes;
+  piece q sits at byte (rb (b/2) (d_v/2) + q (d_v/2) + p) 16 of the region.
+  KDA rows are stored row-major: a code row of d_v codes at b bits takes
+  d_v*b/8 bytes, code j at bits [j*b, j*b+b).  Codes are b-bit two's
+  complement; b = 16 stores binary16 values.
+* uniform head: code region, then d_k FP16 row scales s.
+* STEP GDN head (b in {2,4,6,8}): code region, d_k FP16 r, d_v FP16 c.
+  Pivot head (b = 16): the region of FP16 values and nothing else.
 * STEP KDA head: storage rows ordered by width (ascending, ties by key row),
   so FP16 pivot rows come last; then d_k FP16 r in storage order (0 for a
   pivot row) and d_v FP16 c.
 * window head: int32 l at byte 0 (bytes 4..15 zero), float32 alpha[p] at
-  byte 16, INT8 Z [d_k, d_v] at round_up(16 + 4p, 128), then float32 C[d_k],
+  byte 16, INT8 Z [d_k, d_v] (blocked order) at round_up(16 + 4p, 128), then
+  float32 C[d_k],
   float32 B[d_v], float32 K~[p, d_k], float32 U[p, d_v].
 """
 from __future__ import annotations
@@ -116,6 +123,53 @@ def unpack_code_row(buf: bytes, bits: int, n: int) -> np.ndarray:
     return np.where(vals >= (1 << (bits - 1)), vals - (1 << bits), vals).astype(np.float64)
 
 
+# ------------------------------------------------------- blocked code region
+def _field_bits(vals: np.ndarray, bits: int) -> np.ndarray:
+    """b-bit fields of integer codes (two's complement) or binary16 values."""
+    if bits == PIVOT_BITS:
+        return np.asarray(vals, dtype=np.float64).astype("<f2").view("<u2").astype(np.int64)
+    return np.asarray(np.rint(vals), dtype=np.int64) & ((1 << bits) - 1)
+
+
+def _from_fields(f: np.ndarray, bits: int) -> np.ndarray:
+    if bits == PIVOT_BITS:
+        return f.astype("<u2").view("<f2").astype(np.float64)
+    return np.where(f >= (1 << (bits - 1)), f - (1 << bits), f).astype(np.float64)
+
+
+def pack_blocked(vals: np.ndarray, bits: int) -> bytes:
+    """Column-pair blocked region of a d_k x d_v tile of codes (or FP16 values)."""
+    d_k, d_v = vals.shape
+    P = d_v // 2
+    half = bits // 2                                  # pieces per chunk
+    fields = _field_bits(vals, bits)
+    out = bytearray(d_k * d_v * bits // 8)
+    for rb in range(d_k // 32):
+        for p in range(P):
+            blk = fields[32 * rb:32 * rb + 32, 2 * p:2 * p + 2].reshape(-1)  # n = 2m + c
+            bitarr = ((blk[:, None] >> np.arange(bits)) & 1).astype(np.uint8).reshape(-1)
+            chunk = np.packbits(bitarr, bitorder="little").tobytes()
+            for q in range(half):
+                o = (rb * half * P + q * P + p) * 16
+                out[o:o + 16] = chunk[16 * q:16 * q + 16]
+    return bytes(out)
+
+
+def parse_blocked(buf: bytes, bits: int, d_k: int, d_v: int) -> np.ndarray:
+    P = d_v // 2
+    half = bits // 2
+    out = np.zeros((d_k, d_v))
+    for rb in range(d_k // 32):
+        for p in range(P):
+            chunk = b"".join(buf[(rb * half * P + q * P + p) * 16:
+                                 (rb * half * P + q * P + p) * 16 + 16] for q in range(half))
+            arr = np.unpackbits(np.frombuffer(chunk, dtype=np.uint8), bitorder="little")
+            arr = arr[:64 * bits].reshape(64, bits).astype(np.int64)
+            f = (arr << np.arange(bits)).sum(-1)
+            out[32 * rb:32 * rb + 32, 2 * p:2 * p + 2] = _from_fields(f, bits).reshape(32, 2)
+    return out
+
+
 def _f16_bytes(x: np.ndarray) -> bytes:
     return np.asarray(x, dtype=np.float64).astype(np.float16).astype("<f2").tobytes()
 
@@ -134,18 +188,14 @@ def pack_head(desc: dict, h: int, st: dict) -> bytes:
     mode = desc["mode"]
     if mode == "uniform":
         b = int(desc["bits"])
-        rb = row_bytes(d_v, b)
-        for i in range(d_k):
-            out[i * rb:(i + 1) * rb] = pack_code_row(st["z"][i], b)
+        out[0:f["s"]] = pack_blocked(st["z"], b)
         out[f["s"]:f["s"] + 2 * d_k] = _f16_bytes(st["s"])
     elif mode == "step" and desc["kind"] == "gdn":
         b = int(desc["head_bits"][h])
         if b == PIVOT_BITS:
-            out[0:2 * d_k * d_v] = _f16_bytes(st["h"].reshape(-1))
+            out[0:2 * d_k * d_v] = pack_blocked(st["h"], PIVOT_BITS)
         else:
-            rb = row_bytes(d_v, b)
-            for i in range(d_k):
-                out[i * rb:(i + 1) * rb] = pack_code_row(st["z"][i], b)
+            out[0:f["r"]] = pack_blocked(st["z"], b)
             out[f["r"]:f["r"] + 2 * d_k] = _f16_bytes(st["r"])
             out[f["c"]:f["c"] + 2 * d_v] = _f16_bytes(st["c"])
     elif mode == "step":
@@ -168,7 +218,7 @@ def pack_head(desc: dict, h: int, st: dict) -> bytes:
         p = int(desc["p"])
         out[0:4] = np.int32(st["ell"]).tobytes()
         out[f["alpha"]:f["alpha"] + 4 * p] = np.asarray(st["alpha"], "<f4").tobytes()
-        out[f["Z"]:f["Z"] + d_k * d_v] = np.asarray(np.rint(st["Z"]), np.int8).tobytes()
+        out[f["Z"]:f["Z"] + d_k * d_v] = pack_blocked(st["Z"], 8)
         out[f["C"]:f["C"] + 4 * d_k] = np.asarray(st["C"], "<f4").tobytes()
         out[f["B"]:f["B"] + 4 * d_v] = np.asarray(st["B"], "<f4").tobytes()
         out[f["K"]:f["K"] + 4 * p * d_k] = np.asarray(st["kt"], "<f4").tobytes()
@@ -184,21 +234,17 @@ def parse_head(desc: dict, h: int, buf: bytes) -> dict:
     st: Dict[str, np.ndarray] = {}
     if mode == "uniform":
         b = int(desc["bits"])
-        rb = row_bytes(d_v, b)
-        st["z"] = np.stack([unpack_code_row(buf[i * rb:(i + 1) * rb], b, d_v)
-                            for i in range(d_k)])
+        st["z"] = parse_blocked(buf[0:f["s"]], b, d_k, d_v)
         st["s"] = _f16(buf[f["s"]:f["s"] + 2 * d_k])
     elif mode == "step" and desc["kind"] == "gdn":
         b = int(desc["head_bits"][h])
         if b == PIVOT_BITS:
-            st["h"] = _f16(buf[0:2 * d_k * d_v]).reshape(d_k, d_v)
+            st["h"] = parse_blocked(buf[0:2 * d_k * d_v], PIVOT_BITS, d_k, d_v)
             st["z"] = np.zeros((d_k, d_v))
             st["r"] = np.zeros(d_k)
             st["c"] = np.zeros(d_v)
         else:
-            rb = row_bytes(d_v, b)
-            st["z"] = np.stack([unpack_code_row(buf[i * rb:(i + 1) * rb], b, d_v)
-                                for i in range(d_k)])
+            st["z"] = parse_blocked(buf[0:f["r"]], b, d_k, d_v)
             st["r"] = _f16(buf[f["r"]:f["r"] + 2 * d_k])
             st["c"] = _f16(buf[f["c"]:f["c"] + 2 * d_v])
             st["h"] = np.zeros((d_k, d_v))
@@ -224,8 +270,7 @@ def parse_head(desc: dict, h: int, buf: bytes) -> dict:
         p = int(desc["p"])
         st["ell"] = int(np.frombuffer(buf[0:4], "<i4")[0])
         st["alpha"] = np.frombuffer(buf[f["alpha"]:f["alpha"] + 4 * p], "<f4").astype(np.float64)
-        st["Z"] = np.frombuffer(buf[f["Z"]:f["Z"] + d_k * d_v], np.int8).astype(
-            np.float64).reshape(d_k, d_v)
+        st["Z"] = parse_blocked(buf[f["Z"]:f["Z"] + d_k * d_v], 8, d_k, d_v)
         st["C"] = np.frombuffer(buf[f["C"]:f["C"] + 4 * d_k], "<f4").astype(np.float64)
         st["B"] = np.frombuffer(buf[f["B"]:f["B"] + 4 * d_v], "<f4").astype(np.float64)
         st["kt"] = np.frombuffer(buf[f["K"]:f["K"] + 4 * p * d_k], "<f4").astype(

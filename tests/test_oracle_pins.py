@@ -560,9 +560,32 @@ def test_layout_hand_computed_bytes():
         assert np.array_equal(L.unpack_code_row(L.pack_code_row(zz, b), b, len(zz)), zz)
 
 
+def test_layout_blocked_positions():
+    """Column-pair blocked order on a hand-worked 64 x 4 tile at 4 bits: element
+    (row 32 rb + m, col 2 p + c) is value n = 2 m + c of chunk (rb, p); piece q
+    of that chunk sits at byte (rb * 2 * 2 + q * 2 + p) * 16."""
+    z = np.zeros((64, 4))
+    z[0, 0] = 3          # rb 0, p 0, n 0  -> piece 0 of chunk (0,0), low nibble of byte 0
+    z[0, 1] = -1         # rb 0, p 0, n 1  -> high nibble of byte 0
+    z[17, 3] = -7        # rb 0, p 1, m 17, c 1 -> n 35 -> piece 1, byte 1, high nibble
+    z[40, 2] = 5         # rb 1, p 1, m 8, c 0 -> n 16 -> piece 0, byte 8, low nibble
+    buf = L.pack_blocked(z, 4)
+    assert len(buf) == 64 * 4 * 4 // 8
+    expect = bytearray(len(buf))
+    expect[0] = 0xF3
+    expect[(0 * 4 + 1 * 2 + 1) * 16 + 1] = 0x90
+    expect[(1 * 4 + 0 * 2 + 1) * 16 + 8] = 0x05
+    assert buf == bytes(expect)
+    np.testing.assert_array_equal(L.parse_blocked(buf, 4, 64, 4), z)
+    h = np.zeros((32, 2))
+    h[1, 0] = 1.5        # n 2 -> bits 32..47 of chunk (0,0) -> piece 0 bytes 4..5
+    buf = L.pack_blocked(h, 16)
+    assert buf[4:6] == np.float16(1.5).tobytes() and sum(buf) == sum(np.float16(1.5).tobytes())
+
+
 @pytest.mark.parametrize("mode", ["uniform", "gdn", "kda", "window"])
 def test_layout_round_trip(rng, mode):
-    d = 16
+    d = 32
     if mode == "uniform":
         desc = {"mode": "uniform", "heads": 2, "d_k": d, "d_v": d, "bits": 8}
         sts = [{"z": rng.integers(-127, 128, (d, d)).astype(float),
