@@ -1,0 +1,563 @@
+// Host side of the C ABI: plans, lifetime-aware calibration, argument checks
+// and kernel dispatch.  No device memory is allocated here; the caller owns
+// pools, plan tables, inputs and outputs.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <vector>
+
+#include "sq_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+sq_status fail(sq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+sq_status ok() {
+  g_err.clear();
+  return SQ_OK;
+}
+
+sq_status hip_fail(hipError_t e, const char* what) {
+  return fail(SQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+long long round_up(long long n, long long a) { return (n + a - 1) / a * a; }
+
+bool supported_dim(int d) { return d == 64 || d == 128; }
+bool code_bits(int b) { return b == 2 || b == 4 || b == 6 || b == 8; }
+
+// Bytes of one stored row of d_v values at width b (FP16 for pivots).
+int row_bytes(int dv, int b) { return b == SQ_PIVOT_BITS ? 2 * dv : dv * b / 8; }
+
+template <class T>
+size_t put(std::vector<unsigned char>& img, const std::vector<T>& v) {
+  size_t off = round_up((long long)img.size(), 16);
+  img.resize(off + std::max<size_t>(v.size() * sizeof(T), 16), 0);
+  if (!v.empty()) std::memcpy(img.data() + off, v.data(), v.size() * sizeof(T));
+  return off;
+}
+
+// Per-head byte offsets, the device-table image and derived sizes.
+void finish_plan(sq_plan* P) {
+  const int H = P->H, dk = P->dk, dv = P->dv;
+  P->head_off.assign(H, 0);
+  P->r_off.assign(H, 0);
+  P->c_off.assign(H, 0);
+  long long off = 0, payload = 0, analytic = 0;
+  int maxh = 0;
+  for (int h = 0; h < H; ++h) {
+    long long used = 0;
+    if (P->mode == SQ_MODE_UNIFORM) {
+      P->r_off[h] = dk * dv * P->ubits / 8;
+      used = P->r_off[h] + 2LL * dk;
+      analytic += used;
+    } else if (P->mode == SQ_MODE_WINDOW) {
+      const long long z = round_up(16 + 4LL * P->p, 128);
+      used = z + (long long)dk * dv + 4LL * dk + 4LL * dv + 4LL * P->p * (dk + dv);
+      P->r_off[h] = (int)z;  // start of Z
+      analytic += used;
+    } else if (P->kind == SQ_KIND_GDN) {
+      const int b = P->head_bits[h];
+      if (b == SQ_PIVOT_BITS) {
+        used = 2LL * dk * dv;
+        analytic += used + 2LL * dk + 2LL * dv;  // scale slots kept in the analytic count
+      } else {
+        P->r_off[h] = dk * dv * b / 8;
+        P->c_off[h] = P->r_off[h] + 2 * dk;
+        used = P->c_off[h] + 2LL * dv;
+        analytic += used;
+      }
+    } else {
+      long long codes = 0;
+      for (int s = 0; s < dk; ++s) {
+        P->row_off[h * dk + s] = (int)codes;
+        codes += row_bytes(dv, P->row_bits[h * dk + s]);
+      }
+      P->r_off[h] = (int)codes;
+      P->c_off[h] = (int)codes + 2 * dk;
+      used = codes + 2LL * dk + 2LL * dv;
+      analytic += used;
+    }
+    const long long padded = round_up(used, 256);
+    P->head_off[h] = off;
+    off += padded;
+    payload += used;
+    maxh = std::max<int>(maxh, (int)padded);
+  }
+  P->slot_bytes = off;
+  P->payload_bytes = payload;
+  P->analytic_bytes = analytic;
+  P->max_head_bytes = maxh;
+
+  std::vector<unsigned char>& img = P->image;
+  img.clear();
+  P->o_head_off = put(img, P->head_off);
+  P->o_head_bits = put(img, P->head_bits);
+  P->o_w = put(img, P->w);
+  P->o_row_key = put(img, P->row_key);
+  P->o_row_bits = put(img, P->row_bits);
+  P->o_row_off = put(img, P->row_off);
+  P->o_r_off = put(img, P->r_off);
+  P->o_c_off = put(img, P->c_off);
+  img.resize(round_up((long long)img.size(), 256), 0);
+}
+
+DevPlan dev_view(const sq_plan* P, const void* dev) {
+  const unsigned char* b = static_cast<const unsigned char*>(dev);
+  DevPlan d;
+  d.mode = P->mode;
+  d.kind = P->kind;
+  d.H = P->H;
+  d.dk = P->dk;
+  d.dv = P->dv;
+  d.ubits = P->ubits;
+  d.p = P->p;
+  d.c_floor = P->c_floor;
+  d.slot_bytes = P->slot_bytes;
+  d.max_head_bytes = P->max_head_bytes;
+  d.head_off = reinterpret_cast<const long long*>(b + P->o_head_off);
+  d.head_bits = reinterpret_cast<const int*>(b + P->o_head_bits);
+  d.w = reinterpret_cast<const float*>(b + P->o_w);
+  d.row_key = reinterpret_cast<const int*>(b + P->o_row_key);
+  d.row_bits = reinterpret_cast<const int*>(b + P->o_row_bits);
+  d.row_off = reinterpret_cast<const int*>(b + P->o_row_off);
+  d.r_off = reinterpret_cast<const int*>(b + P->o_r_off);
+  d.c_off = reinterpret_cast<const int*>(b + P->o_c_off);
+  return d;
+}
+
+sq_status check_dims(int H, int dk, int dv) {
+  if (H <= 0) return fail(SQ_EINVAL, "heads must be positive (got %d)", H);
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(SQ_EUNSUPPORTED, "d_k, d_v must be 64 or 128 (got %d, %d)", dk, dv);
+  return SQ_OK;
+}
+
+// Optional host-side check of slot ids (needs a device-to-host copy).
+sq_status validate_slots(const int32_t* slots, int B, long long n_slots, hipStream_t st) {
+  const char* env = std::getenv("SQ_VALIDATE");
+  if (!env || std::strcmp(env, "1") != 0) return SQ_OK;
+  std::vector<int32_t> h(B);
+  hipError_t e = hipMemcpyAsync(h.data(), slots, sizeof(int32_t) * B, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "copying slot ids");
+  std::vector<int32_t> s(h);
+  for (int i = 0; i < B; ++i)
+    if (h[i] < 0 || h[i] >= n_slots)
+      return fail(SQ_ESLOT_RANGE, "slot id %d at position %d outside [0, %lld)", h[i], i, n_slots);
+  std::sort(s.begin(), s.end());
+  for (int i = 1; i < B; ++i)
+    if (s[i] == s[i - 1]) return fail(SQ_EDUP_SLOT, "slot id %d repeated in one call", s[i]);
+  return SQ_OK;
+}
+
+hipError_t dispatch(const sq_plan* P, const TileArgs& a, hipStream_t st) {
+  if (P->mode == SQ_MODE_WINDOW) return launch_tile_window(a, st);
+  if (P->mode == SQ_MODE_STEP && P->kind == SQ_KIND_KDA) return launch_tile_kda(a, st);
+  return launch_tile_gdn(a, st);
+}
+
+TileArgs base_args(const sq_plan* P, const void* dev_plan, int op) {
+  TileArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.P = dev_view(P, dev_plan);
+  a.op = op;
+  return a;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ plans
+extern "C" sq_status sq_plan_create_uniform(int32_t heads, int32_t d_k, int32_t d_v,
+                                            int32_t bits, sq_plan** out) {
+  if (!out) return fail(SQ_EINVAL, "out is null");
+  *out = nullptr;
+  sq_status s = check_dims(heads, d_k, d_v);
+  if (s) return s;
+  if (!code_bits(bits)) return fail(SQ_EUNSUPPORTED, "uniform bits must be 2, 4, 6 or 8 (got %d)", bits);
+  sq_plan* P = new (std::nothrow) sq_plan;
+  if (!P) return fail(SQ_ENOMEM, "plan allocation");
+  P->mode = SQ_MODE_UNIFORM;
+  P->kind = SQ_KIND_GDN;
+  P->H = heads;
+  P->dk = d_k;
+  P->dv = d_v;
+  P->ubits = bits;
+  P->head_bits.assign(heads, bits);
+  finish_plan(P);
+  *out = P;
+  return ok();
+}
+
+extern "C" sq_status sq_plan_create_window(int32_t heads, int32_t d_k, int32_t d_v, int32_t p,
+                                           float c_floor, sq_plan** out) {
+  if (!out) return fail(SQ_EINVAL, "out is null");
+  *out = nullptr;
+  sq_status s = check_dims(heads, d_k, d_v);
+  if (s) return s;
+  if (p < 1 || p > 32) return fail(SQ_EUNSUPPORTED, "window length must be in [1, 32] (got %d)", p);
+  if (!(c_floor > 0.0f) || !std::isfinite(c_floor))
+    return fail(SQ_EINVAL, "smoothing floor must be positive and finite");
+  sq_plan* P = new (std::nothrow) sq_plan;
+  if (!P) return fail(SQ_ENOMEM, "plan allocation");
+  P->mode = SQ_MODE_WINDOW;
+  P->kind = SQ_KIND_GDN;
+  P->H = heads;
+  P->dk = d_k;
+  P->dv = d_v;
+  P->p = p;
+  P->c_floor = c_floor;
+  P->head_bits.assign(heads, 8);
+  finish_plan(P);
+  *out = P;
+  return ok();
+}
+
+extern "C" sq_status sq_plan_create_step(int32_t kind, int32_t heads, int32_t d_k, int32_t d_v,
+                                         const int32_t* unit_bits, const float* w,
+                                         sq_plan** out) {
+  if (!out) return fail(SQ_EINVAL, "out is null");
+  *out = nullptr;
+  if (!unit_bits || !w) return fail(SQ_EINVAL, "unit_bits and w must be given");
+  if (kind != SQ_KIND_GDN && kind != SQ_KIND_KDA) return fail(SQ_EINVAL, "bad kind %d", kind);
+  sq_status s = check_dims(heads, d_k, d_v);
+  if (s) return s;
+  const int U = kind == SQ_KIND_GDN ? heads : heads * d_k;
+  for (int u = 0; u < U; ++u)
+    if (!code_bits(unit_bits[u]) && unit_bits[u] != SQ_PIVOT_BITS)
+      return fail(SQ_EUNSUPPORTED, "unit %d: width %d not in {2,4,6,8,16}", u, unit_bits[u]);
+  for (int i = 0; i < heads * d_k; ++i)
+    if (!(w[i] > 0.0f) || !std::isfinite(w[i]))
+      return fail(SQ_EINVAL, "impact factor %d must be positive and finite", i);
+  sq_plan* P = new (std::nothrow) sq_plan;
+  if (!P) return fail(SQ_ENOMEM, "plan allocation");
+  P->mode = SQ_MODE_STEP;
+  P->kind = kind;
+  P->H = heads;
+  P->dk = d_k;
+  P->dv = d_v;
+  P->n_units = U;
+  P->unit_bits.assign(unit_bits, unit_bits + U);
+  P->w.assign(w, w + heads * d_k);
+  if (kind == SQ_KIND_GDN) {
+    P->head_bits = P->unit_bits;
+  } else {
+    P->head_bits.assign(heads, 0);
+    P->row_key.resize(heads * d_k);
+    P->row_bits.resize(heads * d_k);
+    P->row_off.resize(heads * d_k);
+    for (int h = 0; h < heads; ++h) {
+      std::vector<int> ord(d_k);
+      std::iota(ord.begin(), ord.end(), 0);
+      const int32_t* rb = unit_bits + h * d_k;
+      std::stable_sort(ord.begin(), ord.end(), [&](int a, int b) { return rb[a] < rb[b]; });
+      for (int s2 = 0; s2 < d_k; ++s2) {
+        P->row_key[h * d_k + s2] = ord[s2];
+        P->row_bits[h * d_k + s2] = rb[ord[s2]];
+      }
+    }
+  }
+  finish_plan(P);
+  *out = P;
+  return ok();
+}
+
+extern "C" sq_status sq_calibrate_bits(const sq_calib_stats* st, const sq_calib_opts* op,
+                                       sq_plan** out) {
+  if (!out) return fail(SQ_EINVAL, "out is null");
+  *out = nullptr;
+  if (!st || !op) return fail(SQ_EINVAL, "stats and opts must be given");
+  if (st->kind != SQ_KIND_GDN && st->kind != SQ_KIND_KDA) return fail(SQ_EINVAL, "bad kind");
+  sq_status s = check_dims(st->heads, st->d_k, st->d_v);
+  if (s) return s;
+  if (st->n_cand < 1 || !st->cand_bits || !st->ell || !st->dist || !st->omega)
+    return fail(SQ_EINVAL, "incomplete statistics");
+  for (int c = 0; c < st->n_cand; ++c) {
+    if (!code_bits(st->cand_bits[c])) return fail(SQ_EUNSUPPORTED, "candidate width %d", st->cand_bits[c]);
+    if (c && st->cand_bits[c] <= st->cand_bits[c - 1]) return fail(SQ_EINVAL, "candidates must ascend");
+  }
+  if (op->horizon < 1 || !(op->pivot_frac >= 0.0 && op->pivot_frac <= 1.0) ||
+      !std::isfinite(op->nominal_bits) || !std::isfinite(op->gamma) || !(op->omega_floor_rel >= 0))
+    return fail(SQ_EINVAL, "bad calibration options");
+  const int H = st->heads, dk = st->d_k, dv = st->d_v, nc = st->n_cand;
+  const bool gdn = st->kind == SQ_KIND_GDN;
+  const int U = gdn ? H : H * dk;
+  const double n_unit = gdn ? (double)dk * dv : (double)dv;
+  for (int u = 0; u < U; ++u) {
+    if (!std::isfinite(st->ell[u])) return fail(SQ_ENONFINITE, "ell[%d] is not finite", u);
+    for (int c = 0; c < nc; ++c)
+      if (!std::isfinite(st->dist[u * nc + c])) return fail(SQ_ENONFINITE, "dist[%d][%d] is not finite", u, c);
+  }
+  for (int i = 0; i < H * dk; ++i)
+    if (!std::isfinite(st->omega[i]) || st->omega[i] < 0)
+      return fail(SQ_ENONFINITE, "omega[%d] must be finite and non-negative", i);
+
+  // lifetime weights L_u = sum_{j<horizon} exp(2 j ell_u)   ([SQ] Sec. 4, Eq. 7)
+  std::vector<double> L(U);
+  for (int u = 0; u < U; ++u) {
+    double acc = 0.0;
+    for (int j = 0; j < op->horizon; ++j) acc += std::exp(2.0 * j * st->ell[u]);
+    if (!std::isfinite(acc)) return fail(SQ_ENONFINITE, "lifetime weight of unit %d overflows", u);
+    L[u] = acc;
+  }
+  // pivots: largest L_u d_u(b_max), ties to the lower index   ([SQ] Sec. 4, App. D)
+  const int n_piv = (int)std::ceil(op->pivot_frac * U - 1e-12);
+  std::vector<int> ord(U);
+  std::iota(ord.begin(), ord.end(), 0);
+  std::stable_sort(ord.begin(), ord.end(), [&](int a, int b) {
+    return L[a] * st->dist[a * nc + nc - 1] > L[b] * st->dist[b * nc + nc - 1];
+  });
+  std::vector<char> piv(U, 0);
+  for (int i = 0; i < n_piv; ++i) piv[ord[i]] = 1;
+  // greedy under the residual budget b_bar N - 8 N_piv   ([SQ] Eq. 8, App. D)
+  double budget = op->nominal_bits * n_unit * U;
+  double used = 0.0;
+  std::vector<int> level(U, 0);
+  for (int u = 0; u < U; ++u) {
+    if (piv[u]) budget -= 8.0 * n_unit;
+    else used += n_unit * st->cand_bits[0];
+  }
+  if (used > budget + 1e-9)
+    return fail(SQ_EBUDGET, "budget %.1f bits below the smallest width (%.1f bits needed)", budget, used);
+  for (;;) {
+    int best = -1;
+    double best_gain = 0.0;
+    for (int u = 0; u < U; ++u) {
+      if (piv[u] || level[u] + 1 >= nc) continue;
+      const double cost = n_unit * (st->cand_bits[level[u] + 1] - st->cand_bits[level[u]]);
+      if (used + cost > budget + 1e-9) continue;
+      const double gain = L[u] * (st->dist[u * nc + level[u]] - st->dist[u * nc + level[u] + 1]) / cost;
+      if (best < 0 || gain > best_gain) {
+        best = u;
+        best_gain = gain;
+      }
+    }
+    if (best < 0) break;
+    used += n_unit * (st->cand_bits[level[best] + 1] - st->cand_bits[level[best]]);
+    ++level[best];
+  }
+  std::vector<int32_t> bits(U);
+  for (int u = 0; u < U; ++u) bits[u] = piv[u] ? SQ_PIVOT_BITS : st->cand_bits[level[u]];
+
+  // row impact factors w = (omega / geomean_head(omega))^(gamma/2)   ([SQ] App. B, C)
+  std::vector<float> w(H * dk);
+  for (int h = 0; h < H; ++h) {
+    const double* om = st->omega + (size_t)h * dk;
+    double mx = 0.0;
+    for (int i = 0; i < dk; ++i) mx = std::max(mx, om[i]);
+    if (mx <= 0.0) {
+      for (int i = 0; i < dk; ++i) w[h * dk + i] = 1.0f;
+      continue;
+    }
+    std::vector<double> f(dk);
+    double lsum = 0.0;
+    for (int i = 0; i < dk; ++i) {
+      f[i] = std::max(om[i], op->omega_floor_rel * mx);
+      lsum += std::log(f[i]);
+    }
+    const double gm = std::exp(lsum / dk);
+    for (int i = 0; i < dk; ++i) w[h * dk + i] = (float)std::pow(f[i] / gm, op->gamma / 2.0);
+  }
+  return sq_plan_create_step(st->kind, H, dk, dv, bits.data(), w.data(), out);
+}
+
+extern "C" sq_status sq_plan_query(const sq_plan* P, sq_plan_desc* d) {
+  if (!P || !d) return fail(SQ_EINVAL, "plan and desc must be given");
+  std::memset(d, 0, sizeof(*d));
+  d->mode = P->mode;
+  d->kind = P->kind;
+  d->heads = P->H;
+  d->d_k = P->dk;
+  d->d_v = P->dv;
+  d->uniform_bits = P->ubits;
+  d->window = P->p;
+  d->n_units = P->n_units;
+  d->slot_bytes = P->slot_bytes;
+  d->payload_bytes = P->payload_bytes;
+  d->analytic_bytes = P->analytic_bytes;
+  d->head_off = reinterpret_cast<const int64_t*>(P->head_off.data());
+  d->unit_bits = P->unit_bits.empty() ? nullptr : P->unit_bits.data();
+  d->w = P->w.empty() ? nullptr : P->w.data();
+  d->window_c_floor = P->c_floor;
+  return ok();
+}
+
+extern "C" sq_status sq_plan_destroy(sq_plan* P) {
+  delete P;
+  return ok();
+}
+
+extern "C" sq_status sq_plan_device_bytes(const sq_plan* P, size_t* bytes) {
+  if (!P || !bytes) return fail(SQ_EINVAL, "plan and bytes must be given");
+  *bytes = P->image.size();
+  return ok();
+}
+
+extern "C" sq_status sq_plan_upload(const sq_plan* P, void* dev, hipStream_t st) {
+  if (!P || !dev) return fail(SQ_EINVAL, "plan and device buffer must be given");
+  if (reinterpret_cast<uintptr_t>(dev) % 256) return fail(SQ_EINVAL, "device plan buffer must be 256-byte aligned");
+  hipError_t e = hipMemcpyAsync(dev, P->image.data(), P->image.size(), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "uploading plan tables");
+  return ok();
+}
+
+extern "C" sq_status sq_max_head_bytes(const sq_plan* P, size_t* bytes) {
+  if (!P || !bytes) return fail(SQ_EINVAL, "plan and bytes must be given");
+  *bytes = (size_t)P->max_head_bytes;
+  return ok();
+}
+
+// ------------------------------------------------------------------ pools
+extern "C" sq_status sq_pool_bytes(const sq_plan* P, int64_t n_slots, size_t* bytes) {
+  if (!P || !bytes || n_slots < 0) return fail(SQ_EINVAL, "bad arguments");
+  *bytes = (size_t)(P->slot_bytes * n_slots);
+  return ok();
+}
+
+extern "C" sq_status sq_pool_init(const sq_plan* P, const void* dev_plan, void* pool,
+                                  int64_t n_slots, hipStream_t st) {
+  if (!P || !dev_plan || !pool || n_slots <= 0) return fail(SQ_EINVAL, "bad arguments");
+  hipError_t e = hipMemsetAsync(pool, 0, (size_t)(P->slot_bytes * n_slots), st);
+  if (e != hipSuccess) return hip_fail(e, "clearing pool");
+  return ok();
+}
+
+extern "C" sq_status sq_pool_pack(const sq_plan* P, const void* dev_plan, void* pool,
+                                  int64_t n_slots, const int32_t* slots, int32_t B,
+                                  const float* S, hipStream_t st) {
+  if (!P || !dev_plan || !pool || !slots || !S || n_slots <= 0 || B < 0)
+    return fail(SQ_EINVAL, "bad arguments to sq_pool_pack");
+  if (B == 0) return ok();
+  sq_status s = validate_slots(slots, B, n_slots, st);
+  if (s) return s;
+  TileArgs a = base_args(P, dev_plan, OP_PACK);
+  a.pool = static_cast<unsigned char*>(pool);
+  a.n_slots = n_slots;
+  a.slots = slots;
+  a.B = B;
+  a.X = S;
+  a.n_tiles = B * P->H;
+  hipError_t e = dispatch(P, a, st);
+  if (e != hipSuccess) return hip_fail(e, "launching pack");
+  return ok();
+}
+
+extern "C" sq_status sq_pool_unpack(const sq_plan* P, const void* dev_plan, const void* pool,
+                                    int64_t n_slots, const int32_t* slots, int32_t B,
+                                    float* S_out, hipStream_t st) {
+  if (!P || !dev_plan || !pool || !slots || !S_out || n_slots <= 0 || B < 0)
+    return fail(SQ_EINVAL, "bad arguments to sq_pool_unpack");
+  if (B == 0) return ok();
+  sq_status s = validate_slots(slots, B, n_slots, st);
+  if (s) return s;
+  TileArgs a = base_args(P, dev_plan, OP_UNPACK);
+  a.pool = static_cast<unsigned char*>(const_cast<void*>(pool));
+  a.n_slots = n_slots;
+  a.slots = slots;
+  a.B = B;
+  a.S_out = S_out;
+  a.n_tiles = B * P->H;
+  hipError_t e = dispatch(P, a, st);
+  if (e != hipSuccess) return hip_fail(e, "launching unpack");
+  return ok();
+}
+
+extern "C" sq_status sq_decode_step(const sq_plan* P, const void* dev_plan, void* pool,
+                                    int64_t n_slots, const int32_t* slots, int32_t B,
+                                    const float* q, const float* k, const float* v,
+                                    const float* beta, const float* gate, float* y,
+                                    hipStream_t st) {
+  if (!P || !dev_plan || !pool || !slots || !q || !k || !v || !beta || !gate || !y ||
+      n_slots <= 0 || B < 0)
+    return fail(SQ_EINVAL, "bad arguments to sq_decode_step");
+  if (B == 0) return ok();
+  sq_status s = validate_slots(slots, B, n_slots, st);
+  if (s) return s;
+  TileArgs a = base_args(P, dev_plan, OP_DECODE);
+  a.pool = static_cast<unsigned char*>(pool);
+  a.n_slots = n_slots;
+  a.slots = slots;
+  a.B = B;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.gate = gate;
+  a.y = y;
+  a.n_tiles = B * P->H;
+  hipError_t e = dispatch(P, a, st);
+  if (e != hipSuccess) return hip_fail(e, "launching decode step");
+  return ok();
+}
+
+extern "C" sq_status sq_window_flush(const sq_plan* P, const void* dev_plan, void* pool,
+                                     int64_t n_slots, const int32_t* slots, int32_t B,
+                                     hipStream_t st) {
+  if (!P || !dev_plan || !pool || !slots || n_slots <= 0 || B < 0)
+    return fail(SQ_EINVAL, "bad arguments to sq_window_flush");
+  if (P->mode != SQ_MODE_WINDOW) return fail(SQ_EPLAN_MISMATCH, "sq_window_flush needs a window plan");
+  if (B == 0) return ok();
+  sq_status s = validate_slots(slots, B, n_slots, st);
+  if (s) return s;
+  TileArgs a = base_args(P, dev_plan, OP_FLUSH);
+  a.pool = static_cast<unsigned char*>(pool);
+  a.n_slots = n_slots;
+  a.slots = slots;
+  a.B = B;
+  a.n_tiles = B * P->H;
+  hipError_t e = launch_tile_window(a, st);
+  if (e != hipSuccess) return hip_fail(e, "launching window flush");
+  return ok();
+}
+
+extern "C" sq_status sq_quantize_tiles(const sq_plan* P, const void* dev_plan, const float* X,
+                                       int32_t n_tiles, const int32_t* head_ids, void* out,
+                                       hipStream_t st) {
+  if (!P || !dev_plan || !X || !head_ids || !out || n_tiles < 0)
+    return fail(SQ_EINVAL, "bad arguments to sq_quantize_tiles");
+  if (n_tiles == 0) return ok();
+  TileArgs a = base_args(P, dev_plan, OP_PACK);
+  a.X = X;
+  a.head_ids = head_ids;
+  a.out = static_cast<unsigned char*>(out);
+  a.out_stride = P->max_head_bytes;
+  a.n_tiles = n_tiles;
+  hipError_t e = dispatch(P, a, st);
+  if (e != hipSuccess) return hip_fail(e, "launching quantize-only");
+  return ok();
+}
+
+extern "C" sq_status sq_dense_step(int32_t kind, int32_t H, int32_t dk, int32_t dv, float* S,
+                                   int64_t n_slots, const int32_t* slots, int32_t B,
+                                   const float* q, const float* k, const float* v,
+                                   const float* beta, const float* gate, float* y,
+                                   hipStream_t st) {
+  if (kind != SQ_KIND_GDN && kind != SQ_KIND_KDA) return fail(SQ_EINVAL, "bad kind %d", kind);
+  sq_status s = check_dims(H, dk, dv);
+  if (s) return s;
+  if (!S || !slots || !q || !k || !v || !beta || !gate || !y || n_slots <= 0 || B < 0)
+    return fail(SQ_EINVAL, "bad arguments to sq_dense_step");
+  if (B == 0) return ok();
+  s = validate_slots(slots, B, n_slots, st);
+  if (s) return s;
+  hipError_t e = launch_dense_step(kind, H, dk, dv, S, n_slots, slots, B, q, k, v, beta, gate, y, st);
+  if (e != hipSuccess) return hip_fail(e, "launching dense step");
+  return ok();
+}
+
+extern "C" const char* sq_last_error(void) { return g_err.c_str(); }

@@ -1,0 +1,70 @@
+// Internal declarations shared by the host library and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "stepq.h"
+
+// Device view of a plan: pointers into the caller-owned device table buffer.
+struct DevPlan {
+  int mode, kind, H, dk, dv, ubits, p;
+  float c_floor;
+  long long slot_bytes;
+  int max_head_bytes;
+  const long long* head_off;  // [H]
+  const int* head_bits;       // [H] GDN/uniform width (16 = FP16 pivot head)
+  const float* w;             // [H*dk] impact factors (STEP)
+  const int* row_key;         // [H*dk] KDA: key row held by storage row s
+  const int* row_bits;        // [H*dk] KDA: width of storage row s
+  const int* row_off;         // [H*dk] KDA: byte offset of storage row s in its head
+  const int* r_off;           // [H] byte offset of the r (or s) array in the head
+  const int* c_off;           // [H] byte offset of the c array in the head
+};
+
+struct sq_plan {
+  int mode = 0, kind = 0, H = 0, dk = 0, dv = 0, ubits = 0, p = 0;
+  float c_floor = 1e-6f;
+  int n_units = 0;
+  long long slot_bytes = 0, payload_bytes = 0, analytic_bytes = 0;
+  int max_head_bytes = 0;
+  std::vector<long long> head_off;
+  std::vector<int> head_bits, unit_bits, row_key, row_bits, row_off, r_off, c_off;
+  std::vector<float> w;
+  // image of the device tables and the offsets of each array in it
+  std::vector<unsigned char> image;
+  size_t o_head_off = 0, o_head_bits = 0, o_w = 0, o_row_key = 0, o_row_bits = 0,
+         o_row_off = 0, o_r_off = 0, o_c_off = 0;
+};
+
+// Arguments of every tile kernel (one workgroup per (slot, head) tile).
+enum { OP_DECODE = 0, OP_PACK = 1, OP_UNPACK = 2, OP_FLUSH = 3 };
+
+struct TileArgs {
+  DevPlan P;
+  int op;
+  unsigned char* pool;
+  long long n_slots;
+  const int* slots;          // [B] (null for quantize-only)
+  int B;
+  const float *q, *k, *v, *beta, *gate;
+  float* y;                  // [B][H][dv]
+  const float* X;            // pack: dense tiles [B*H][dk][dv]
+  float* S_out;              // unpack: dense tiles [B*H][dk][dv]
+  const int* head_ids;       // quantize-only: head of tile t (null otherwise)
+  unsigned char* out;        // quantize-only: packed head t at out + t*out_stride
+  long long out_stride;
+  int n_tiles;
+};
+
+// Kernel launchers (defined in the .hip files).
+hipError_t launch_tile_gdn(const TileArgs& a, hipStream_t s);     // uniform + STEP GDN
+hipError_t launch_tile_kda(const TileArgs& a, hipStream_t s);     // STEP KDA
+hipError_t launch_tile_window(const TileArgs& a, hipStream_t s);  // per-window variant
+hipError_t launch_dense_step(int kind, int H, int dk, int dv, float* S, long long n_slots,
+                             const int* slots, int B, const float* q, const float* k,
+                             const float* v, const float* beta, const float* gate, float* y,
+                             hipStream_t s);
