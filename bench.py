@@ -1,0 +1,264 @@
+"""Throughput of the fused quantized recurrent-state decode step on one MI355X.
+
+A step is one sq_decode_step call: every (slot, head) tile of the live batch
+is reconstructed, updated, read out, refit, requantised and written back in
+place.  The default workload is the high-concurrency GDN pool: 512 live
+requests drawn from a 1024-slot pool by a seeded random permutation, 48 heads
+of 128 x 128, nominal 4 bits with FP16 pivot heads, allocation from the
+library's lifetime-aware calibration.
+
+The timed loop cycles through `--layers` independent pools (one per layer, as
+a model would) and `--input-sets` input batches, so that a pool is touched
+again only after more bytes than the 256 MB Infinity Cache holds: the
+achieved bandwidth is HBM bandwidth, not cache bandwidth.
+
+Output: one JSON line (metric, value = steps/s, roofline of the decode kernel
+with its launch duration from HIP events, the CPU oracle on a bounded sample).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "state-update steps/s and HBM GB/s (% of peak) at batch 512, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+
+
+def _plan(sq, w):
+    if w.mode == "uniform":
+        return sq.sq_plan_create_uniform(w.heads, w.d_k, w.d_v, w.bits)
+    if w.mode == "window":
+        return sq.sq_plan_create_window(w.heads, w.d_k, w.d_v, w.window)
+    with open(os.path.join(ROOT, "tests", "golden", f"calib_{w.name}.json")) as f:
+        st = json.load(f)
+    stats = {"kind": 0 if st["kind"] == "gdn" else 1, "heads": st["heads"], "d_k": st["d_k"],
+             "d_v": st["d_v"], "cand_bits": st["cand_bits"], "ell": np.array(st["ell"]),
+             "dist": np.array(st["dist"]), "omega": np.array(st["omega"])}
+    return sq.sq_calibrate_bits(stats, {"nominal_bits": st["nominal_bits"],
+                                        "pivot_frac": st["pivot_frac"], "gamma": st["gamma"],
+                                        "horizon": st["horizon"]})
+
+
+def algorithmic_bytes(desc, w) -> int:
+    """Bytes one decode step must move: the packed state of every live slot
+    read and written once (payload, no padding), q, k, v, beta, gate in, y out,
+    slot ids.  Window mode: the boundary and C, B are read, the records held
+    (mean (p-1)/2 per token) are read, one record is written, the boundary is
+    rewritten once per p tokens."""
+    B, H, dk, dv = w.batch, w.heads, w.d_k, w.d_v
+    gate = B * H * (dk if w.kind == "kda" else 1) * 4
+    io = B * H * (2 * dk + dv) * 4 + B * H * 4 + gate + B * H * dv * 4 + B * 4
+    if w.mode != "window":
+        return 2 * B * desc["payload_bytes"] + io
+    p = w.window
+    base = dk * dv + 4 * (dk + dv)
+    rec = 4 * (dk + dv) + 4
+    per_tile = base + rec * (p - 1) / 2.0 + rec + base / p + 16
+    return int(B * H * per_tile) + io
+
+
+def build_state(sq, w, pools, slots_dev):
+    """Warm-up state: `warmup_steps` fp32 dense steps from S = 0 with the
+    library's dense kernel, then packed into every pool."""
+    import torch
+    from synth import inputs as SI
+    params = SI.gate_params(w)
+    S = torch.zeros((w.batch, w.heads, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+    ident = torch.arange(w.batch, dtype=torch.int32, device="cuda")
+    y = torch.empty((w.batch, w.heads, w.d_v), dtype=torch.float32, device="cuda")
+    for t in range(w.warmup_steps):
+        inp = {k: torch.from_numpy(v).cuda() for k, v in SI.warmup_inputs(w, t, params).items()}
+        sq.sq_dense_step(0 if w.kind == "gdn" else 1, w.heads, w.d_k, w.d_v, S, w.batch, ident,
+                         w.batch, inp["q"], inp["k"], inp["v"], inp["beta"], inp["gate"], y)
+    for pl in pools:
+        sq.sq_pool_pack(pl["plan"], pl["dev_plan"], pl["pool"], w.n_slots, slots_dev, w.batch, S)
+    torch.cuda.synchronize()
+    return S
+
+
+def cpu_baseline(w, desc, pool_bytes: bytes, slots, budget_s: float) -> dict:
+    """The float64 oracle, as it stands, on a bounded sample of the same
+    workload: the first slots of the live batch (all heads), teacher-forced
+    from the GPU's packed state, decode steps repeated until the time budget
+    is spent.  Reported as equivalent full-batch steps/s."""
+    from oracle import layout as OL
+    from oracle import quantizers as Q
+    from oracle import recurrence as R
+    from oracle import window as OW
+    from synth import inputs as SI
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import oracle_desc, row_bits_of
+    od = oracle_desc(desc)
+    nb = 1
+    sb = desc["slot_bytes"]
+    states = []
+    for b in range(nb):
+        s = int(slots[b])
+        states.append(OL.parse_slot(od, pool_bytes[b * sb:(b + 1) * sb]))
+    params = SI.gate_params(w)
+    tiles = 0
+    t0 = time.perf_counter()
+    step = 0
+    while time.perf_counter() - t0 < budget_s:
+        inp = SI.step_inputs(w, step, params)
+        for b in range(nb):
+            for h in range(w.heads):
+                st = states[b][h]
+                q, k, v = (inp[x][b, h].astype(np.float64) for x in ("q", "k", "v"))
+                beta = float(inp["beta"][b, h])
+                if w.mode == "window":
+                    r = OW.window_step(st, q, k, v, beta, float(inp["gate"][b, h]), w.window)
+                    states[b][h] = r["state"]
+                    continue
+                dvec = R.gate_vector(inp["gate"][b, h].astype(np.float64),
+                                     "gdn" if w.mode == "uniform" else w.kind, w.d_k)
+                if w.mode == "uniform":
+                    S_hat = Q.dequant_uniform(st["z"], st["s"])
+                    X = R.delta_update(R.retained(S_hat, dvec), k, v, beta)
+                    R.readout(X, q)
+                    e = Q.quantize_uniform(X, w.bits)
+                    states[b][h] = {"z": e["z"], "s": e["s"]}
+                else:
+                    rb = row_bits_of(od, h)
+                    S_hat = Q.dequant_step(st["z"], st["r"], st["c"], rb, st["h"])
+                    X = R.delta_update(R.retained(S_hat, dvec), k, v, beta)
+                    R.readout(X, q)
+                    e = Q.quantize_step(X, desc["w"][h].astype(np.float64), rb)
+                    states[b][h] = {"z": e["z"], "r": e["r"], "c": e["c"], "h": e["h"]}
+                tiles += 1
+        step += 1
+    dt = time.perf_counter() - t0
+    tiles_per_s = tiles / dt
+    return {"value": tiles_per_s / (w.batch * w.heads), "unit": "steps/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{nb} slot x {w.heads} heads, {step} steps ({tiles} tiles) in "
+                      f"{dt:.1f} s, float64 numpy, one process; value = tiles/s / "
+                      f"({w.batch} x {w.heads}) tiles per step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gdn_pool_step4")
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--input-sets", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the decode step has no cross-GPU exchange; see the sharding notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_recurrent_state_decode_amd as sq
+    from synth import inputs as SI
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = SI.workload(args.workload)
+    plan = _plan(sq, w)
+    desc = sq.sq_plan_query(plan)
+    slots = SI.slot_ids(w)
+    slots_dev = torch.from_numpy(slots).cuda()
+    pools = []
+    for _ in range(args.layers):
+        dp = sq.device_plan(plan)
+        pool = torch.empty(sq.sq_pool_bytes(plan, w.n_slots), dtype=torch.uint8, device="cuda")
+        sq.sq_pool_init(plan, dp, pool, w.n_slots)
+        pools.append({"plan": plan, "dev_plan": dp, "pool": pool})
+    build_state(sq, w, pools, slots_dev)
+    params = SI.gate_params(w)
+    sets = []
+    for i in range(args.input_sets):
+        inp = SI.step_inputs(w, i, params)
+        sets.append({k: torch.from_numpy(v).cuda() for k, v in inp.items()})
+    y = torch.empty((args.input_sets, w.batch, w.heads, w.d_v), dtype=torch.float32,
+                    device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        pl = pools[i % len(pools)]
+        s = sets[i % len(sets)]
+        sq.sq_decode_step(plan, pl["dev_plan"], pl["pool"], w.n_slots, slots_dev, w.batch,
+                          s["q"], s["k"], s["v"], s["beta"], s["gate"], y[i % len(sets)],
+                          stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    elapsed_ms = start.elapsed_time(end)
+    ms_per_step = elapsed_ms / args.steps
+
+    # per-launch durations with events on the launch stream (second pass)
+    n_ev = min(args.steps, 64)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_ev)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    abytes = algorithmic_bytes(desc, w)
+    gbs_step = abytes / (ms_per_step * 1e-3) / 1e9
+    gbs_kernel = abytes / (launch_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": 1e3 / ms_per_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_slots": w.n_slots,
+                   "heads": w.heads, "d_k": w.d_k, "d_v": w.d_v, "mode": w.mode,
+                   "kind": w.kind, "nominal_bits": w.nominal_bits if w.mode == "step" else
+                   (w.bits if w.mode == "uniform" else 8),
+                   "unit_bits_histogram": (None if desc["unit_bits"] is None else
+                                           {str(b): int(c) for b, c in zip(
+                                               *np.unique(desc["unit_bits"], return_counts=True))}),
+                   "slot_bytes": desc["slot_bytes"], "layers_rotated": args.layers,
+                   "input_sets": args.input_sets, "algorithmic_bytes_per_step": abytes,
+                   "state_gbs": gbs_step, "pct_of_hbm_peak": 100.0 * gbs_step / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "achieved": gbs_kernel, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gbs_kernel / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gdn_tile_kernel<128,128>" if w.mode != "window" else
+                     "window_tile_kernel<128,128>", "launch_ms": launch_ms,
+                     "bytes_per_launch": abytes},
+    }
+    if not args.no_cpu:
+        torch.cuda.synchronize()
+        sb = desc["slot_bytes"]
+        pb = pools[0]["pool"]
+        s0 = int(slots[0])
+        host = pb[s0 * sb:(s0 + 1) * sb].cpu().numpy().tobytes()
+        out["cpu_baseline"] = cpu_baseline(w, desc, host, slots, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
