@@ -1,0 +1,132 @@
+"""GPU parity of the STEP KDA path (per-key-row widths, channel-wise gates,
+FP16 pivot rows, one shared column scale) against the oracle, teacher-forced."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import quantized_recurrent_state_decode_amd as sq
+from conftest import GOLDEN
+from oracle import calibration as C
+from synth import inputs as SI
+
+from gpu_util import Pool, head_inputs, inputs_dev, oracle_warmup, to_dev
+from parity import Report, check_decode_head, check_quantized_head, dequant_head, oracle_desc
+
+pytestmark = pytest.mark.gpu
+
+
+def _plan(rng, heads, dk, dv, choices=(2, 4, 6, 8, 16)):
+    bits = rng.choice(choices, size=heads * dk)
+    bits[:3] = 16                       # at least a few pivot rows
+    w = C.impact_factors(rng.lognormal(0.0, 1.5, (heads, dk))).astype(np.float32)
+    return sq.sq_plan_create_step(sq.SQ_KIND_KDA, heads, dk, dv, bits, w)
+
+
+def _compare_steps(pool, w, slots, steps, tiles):
+    import torch
+    desc = oracle_desc(pool.desc)
+    sdev = to_dev(slots.astype(np.int32))
+    params = SI.gate_params(w)
+    y = torch.empty((w.batch, w.heads, w.d_v), dtype=torch.float32, device="cuda")
+    rep = Report()
+    for t in range(steps):
+        inp = SI.step_inputs(w, t, params)
+        before = {b: pool.slot_bytes_of(int(slots[b])) for b, _ in tiles}
+        pool.decode(sdev, w.batch, inputs_dev(inp), y)
+        torch.cuda.synchronize()
+        yh = y.cpu().numpy()
+        for b, h in tiles:
+            after = pool.slot_bytes_of(int(slots[b]))
+            check_decode_head(f"step {t} b {b} h {h}", desc, h, pool.head_bytes(before[b], h),
+                              pool.head_bytes(after, h), head_inputs(inp, b, h),
+                              yh[b, h].astype(np.float64), pool.desc["w"][h].astype(np.float64),
+                              rep)
+    return rep
+
+
+@pytest.mark.parametrize("shape", [(128, 128), (64, 64)])
+def test_kda_decode_teacher_forced(shape):
+    rng = np.random.default_rng(40 + shape[0])
+    dk, dv = shape
+    w = SI.workload("kda_step6", batch=5, n_slots=7, heads=3, d_k=dk, d_v=dv, steps=4)
+    pool = Pool(_plan(rng, 3, dk, dv), 7)
+    slots = SI.slot_ids(w)
+    pool.pack(to_dev(slots), to_dev(oracle_warmup(w, 24).astype(np.float32)), w.batch)
+    rep = _compare_steps(pool, w, slots, w.steps,
+                         [(b, h) for b in range(w.batch) for h in range(w.heads)])
+    print("adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
+    rep.assert_ok()
+
+
+def test_kda_quantize_only_and_unpack():
+    import torch
+    rng = np.random.default_rng(8)
+    H = 4
+    plan = _plan(rng, H, 128, 128)
+    pool = Pool(plan, 3)
+    desc = oracle_desc(pool.desc)
+    n = 8
+    X = (rng.standard_normal((n, 128, 128)) * rng.lognormal(0, 1.2, (n, 128, 1))
+         * rng.lognormal(0, 1.2, (n, 1, 128))).astype(np.float32)
+    heads = (np.arange(n) % H).astype(np.int32)
+    mhb = sq.sq_max_head_bytes(plan)
+    out = torch.zeros(n * mhb, dtype=torch.uint8, device="cuda")
+    sq.sq_quantize_tiles(plan, pool.dev_plan, to_dev(X), n, to_dev(heads), out)
+    torch.cuda.synchronize()
+    ob = out.cpu().numpy().tobytes()
+    rep = Report()
+    for t in range(n):
+        check_quantized_head(f"tile {t}", desc, int(heads[t]), X[t].astype(np.float64),
+                             ob[t * mhb:(t + 1) * mhb],
+                             pool.desc["w"][heads[t]].astype(np.float64), rep)
+    rep.assert_ok()
+    slots = to_dev(np.array([2, 0], dtype=np.int32))
+    pool.pack(slots, to_dev(X.reshape(2, H, 128, 128)), 2)
+    S = torch.empty((2, H, 128, 128), dtype=torch.float32, device="cuda")
+    sq.sq_pool_unpack(plan, pool.dev_plan, pool.pool, 3, slots, 2, S)
+    torch.cuda.synchronize()
+    S = S.cpu().numpy()
+    for b, slot in enumerate([2, 0]):
+        buf = pool.slot_bytes_of(slot)
+        for h in range(H):
+            np.testing.assert_allclose(S[b, h], dequant_head(desc, h, pool.head_bytes(buf, h)),
+                                       rtol=1e-6, atol=1e-30)
+
+
+def test_full_size_kda_sampled():
+    """The 256-request, 32-head KDA workload at full size with the calibrated
+    allocation (rows in {4,6,8}, 1.4% FP16 rows), in the launch configuration
+    the bench times: 3 steps, 24 sampled tiles compared on the last."""
+    import torch
+    with open(os.path.join(GOLDEN, "calib_kda_step6.json")) as f:
+        st = json.load(f)
+    stats = {"kind": 1, "heads": 32, "d_k": 128, "d_v": 128, "cand_bits": st["cand_bits"],
+             "ell": np.array(st["ell"]), "dist": np.array(st["dist"]),
+             "omega": np.array(st["omega"])}
+    plan = sq.sq_calibrate_bits(stats, {"nominal_bits": 6.0, "pivot_frac": st["pivot_frac"]})
+    w = SI.workload("kda_step6")
+    pool = Pool(plan, w.n_slots)
+    assert pool.desc["payload_bytes"] == 417024
+    slots = SI.slot_ids(w)
+    sdev = to_dev(slots)
+    S = torch.zeros((w.batch, 32, 128, 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((w.batch, 32, 128), dtype=torch.float32, device="cuda")
+    params = SI.gate_params(w)
+    for t in range(16):
+        d = inputs_dev(SI.warmup_inputs(w, t, params))
+        sq.sq_dense_step(1, 32, 128, 128, S, w.batch, sdev, w.batch, d["q"], d["k"], d["v"],
+                         d["beta"], d["gate"], y)
+    pool.pack(sdev, S, w.batch)
+    del S
+    rng = np.random.default_rng(3)
+    piv_heads = sorted(set(np.nonzero(pool.desc["unit_bits"] == 16)[0] // 128))
+    sample = [(int(b), int(h)) for b, h in zip(rng.choice(w.batch, 20), rng.choice(32, 20))]
+    sample += [(7, int(h)) for h in piv_heads[:4]]
+    for t in range(2):
+        pool.decode(sdev, w.batch, inputs_dev(SI.step_inputs(w, 100 + t, params)), y)
+    w2 = SI.workload("kda_step6")
+    rep = _compare_steps(pool, w2, slots, 1, sample)
+    print("adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
+    rep.assert_ok()
