@@ -1,0 +1,148 @@
+"""GPU parity of the per-window variant (INT8 boundary with key-row smoothing,
+float32 records, dense rebuild every p tokens) against the oracle,
+teacher-forced, across window flushes."""
+import numpy as np
+import pytest
+
+import quantized_recurrent_state_decode_amd as sq
+from oracle import window as W
+from synth import inputs as SI
+
+from gpu_util import Pool, head_inputs, inputs_dev, oracle_warmup, to_dev
+from parity import (Report, check_decode_head, check_quantized_head, check_window_quant,
+                    dequant_head, oracle_desc)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(pool, w, slots, steps, tiles=None, compare=None):
+    import torch
+    desc = oracle_desc(pool.desc)
+    sdev = to_dev(slots.astype(np.int32))
+    params = SI.gate_params(w)
+    y = torch.empty((w.batch, w.heads, w.d_v), dtype=torch.float32, device="cuda")
+    tiles = tiles or [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    rep = Report()
+    for t in range(steps):
+        inp = SI.step_inputs(w, t, params)
+        cmp = compare is None or t in compare
+        before = {b: pool.slot_bytes_of(int(slots[b])) for b, _ in tiles} if cmp else None
+        pool.decode(sdev, w.batch, inputs_dev(inp), y)
+        if not cmp:
+            continue
+        torch.cuda.synchronize()
+        yh = y.cpu().numpy()
+        for b, h in tiles:
+            after = pool.slot_bytes_of(int(slots[b]))
+            check_decode_head(f"step {t} b {b} h {h}", desc, h, pool.head_bytes(before[b], h),
+                              pool.head_bytes(after, h), head_inputs(inp, b, h),
+                              yh[b, h].astype(np.float64), None, rep)
+    return rep
+
+
+@pytest.mark.parametrize("p,steps", [(4, 10), (16, 34), (1, 3)])
+def test_window_decode_across_flushes(p, steps):
+    w = SI.workload("gdn_window16", batch=3, n_slots=5, heads=2, window=p, steps=steps)
+    pool = Pool(sq.sq_plan_create_window(2, 128, 128, p), 5)
+    slots = SI.slot_ids(w)
+    pool.pack(to_dev(slots), to_dev(oracle_warmup(w, 32).astype(np.float32)), w.batch)
+    rep = _run(pool, w, slots, w.steps)
+    print("adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
+    rep.assert_ok()
+
+
+def test_window_64_and_rectangular():
+    for dk, dv in ((64, 64), (128, 64), (64, 128)):
+        w = SI.workload("gdn_window16", batch=2, n_slots=2, heads=2, d_k=dk, d_v=dv, window=3,
+                        steps=7)
+        pool = Pool(sq.sq_plan_create_window(2, dk, dv, 3), 2)
+        slots = SI.slot_ids(w)
+        pool.pack(to_dev(slots), to_dev(oracle_warmup(w, 16).astype(np.float32)), w.batch)
+        rep = _run(pool, w, slots, w.steps)
+        rep.assert_ok()
+
+
+def test_window_flush_unpack_pack():
+    """sq_window_flush rebuilds partial windows (l = 0 heads untouched),
+    sq_pool_unpack returns S_l, sq_pool_pack / quantize-only encode the
+    boundary."""
+    import torch
+    rng = np.random.default_rng(12)
+    w = SI.workload("gdn_window16", batch=4, n_slots=4, heads=2, window=8, steps=5)
+    pool = Pool(sq.sq_plan_create_window(2, 128, 128, 8), 4)
+    desc = oracle_desc(pool.desc)
+    slots = SI.slot_ids(w)
+    sdev = to_dev(slots)
+    pool.pack(sdev, to_dev(oracle_warmup(w, 16).astype(np.float32)), w.batch)
+    params = SI.gate_params(w)
+    y = torch.empty((4, 2, 128), dtype=torch.float32, device="cuda")
+    for t in range(5):                       # slots 0, 1 get 5 tokens; 2, 3 get 3
+        bsz = 4 if t < 3 else 2
+        inp = {k: v[:bsz] for k, v in SI.step_inputs(w, t, params).items()}
+        pool.decode(to_dev(slots[:bsz]), bsz, inputs_dev(inp), y[:bsz])
+    # unpack of open windows
+    S = torch.empty((4, 2, 128, 128), dtype=torch.float32, device="cuda")
+    sq.sq_pool_unpack(pool.plan, pool.dev_plan, pool.pool, 4, sdev, 4, S)
+    torch.cuda.synchronize()
+    Sh = S.cpu().numpy()
+    bufs = [pool.slot_bytes_of(int(s)) for s in slots]
+    for b in range(4):
+        for h in range(2):
+            ref = dequant_head(desc, h, pool.head_bytes(bufs[b], h))
+            np.testing.assert_allclose(Sh[b, h], ref, rtol=2e-6, atol=2e-6 * np.abs(ref).max())
+    # explicit flush of the partial windows
+    from oracle.layout import parse_head
+    sq.sq_window_flush(pool.plan, pool.dev_plan, pool.pool, 4, sdev, 4)
+    rep = Report()
+    for b in range(4):
+        after = pool.slot_bytes_of(int(slots[b]))
+        for h in range(2):
+            st0 = parse_head(desc, h, pool.head_bytes(bufs[b], h))
+            assert st0["ell"] == (5 if b < 2 else 3)
+            st1 = parse_head(desc, h, pool.head_bytes(after, h))
+            assert st1["ell"] == 0
+            check_window_quant(f"flush b {b} h {h}", W.window_state_dense(st0), st1, rep)
+    rep.assert_ok()
+    # a second flush is a no-op (l = 0)
+    snap = pool.pool.cpu().numpy().copy()
+    sq.sq_window_flush(pool.plan, pool.dev_plan, pool.pool, 4, sdev, 4)
+    assert np.array_equal(pool.pool.cpu().numpy(), snap)
+    # quantize-only
+    n = 4
+    X = (rng.standard_normal((n, 128, 128)) * rng.lognormal(0, 1, (n, 128, 1))).astype(np.float32)
+    X[1, :, 7] = 0.0                          # an all-zero column
+    heads = (np.arange(n) % 2).astype(np.int32)
+    mhb = sq.sq_max_head_bytes(pool.plan)
+    out = torch.zeros(n * mhb, dtype=torch.uint8, device="cuda")
+    sq.sq_quantize_tiles(pool.plan, pool.dev_plan, to_dev(X), n, to_dev(heads), out)
+    torch.cuda.synchronize()
+    ob = out.cpu().numpy().tobytes()
+    rep = Report()
+    for t in range(n):
+        check_quantized_head(f"tile {t}", desc, int(heads[t]), X[t].astype(np.float64),
+                             ob[t * mhb:(t + 1) * mhb], None, rep)
+    rep.assert_ok()
+
+
+def test_full_size_window_sampled():
+    """Batch 256, 32 heads, p = 16 at full size: 20 tokens (one flush at token
+    16), 16 sampled tiles compared at the flush and at the last token."""
+    import torch
+    w = SI.workload("gdn_window16")
+    pool = Pool(sq.sq_plan_create_window(32, 128, 128, 16), w.n_slots)
+    slots = SI.slot_ids(w)
+    sdev = to_dev(slots)
+    S = torch.zeros((w.batch, 32, 128, 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((w.batch, 32, 128), dtype=torch.float32, device="cuda")
+    params = SI.gate_params(w)
+    for t in range(16):
+        d = inputs_dev(SI.warmup_inputs(w, t, params))
+        sq.sq_dense_step(0, 32, 128, 128, S, w.batch, sdev, w.batch, d["q"], d["k"], d["v"],
+                         d["beta"], d["gate"], y)
+    pool.pack(sdev, S, w.batch)
+    del S
+    rng = np.random.default_rng(5)
+    tiles = [(int(b), int(h)) for b, h in zip(rng.choice(w.batch, 16), rng.choice(32, 16))]
+    rep = _run(pool, w, slots, 20, tiles=tiles, compare={15, 19})
+    print("adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
+    rep.assert_ok()
