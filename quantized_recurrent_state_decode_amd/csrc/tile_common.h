@@ -69,6 +69,100 @@ __device__ __forceinline__ void pack_codes(const float (&u)[64], uint32_t (&w)[2
   for (int i = 0; i < 2 * BITS; ++i) w[i] ^= sign_mask<BITS>(i);
 }
 
+// ---------------------------------------------------------------------------
+// Fast code paths.  unpack_offset<BITS> gives the 64 values of a lane chunk as
+// offset-binary floats u = z + 2^(BITS-1) (value n = 2m + c).  Codes are
+// rounded with the magic constant 1.5 * 2^23: m = fma(P, tau, kMagic) rounds
+// the exact product P * tau to the nearest integer (ties to even) and leaves
+// it, in two's complement, in the low bits of m; pack_magic<BITS> packs those
+// bits without converting back.
+constexpr float kMagic = 12582912.0f;
+
+__device__ __forceinline__ float ubyte(uint32_t w, int k) {
+  return (float)((w >> (8 * k)) & 0xffu);
+}
+
+template <int BITS>
+__device__ __forceinline__ void unpack_offset(const uint32_t (&w)[2 * BITS], float (&x)[64]) {
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {              // dword d: rows 4d..4d+3, both columns
+      const uint32_t f = w[d] ^ 0x88888888u;
+      const uint32_t lo = f & 0x0f0f0f0fu, hi = (f >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * d + 2 * k] = ubyte(lo, k);
+        x[8 * d + 2 * k + 1] = ubyte(hi, k);
+      }
+    }
+  } else if constexpr (BITS == 8) {
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      const uint32_t f = w[d] ^ 0x80808080u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[4 * d + k] = ubyte(f, k);
+    }
+  } else if constexpr (BITS == 2) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {              // dword d: values 16d .. 16d+15
+      const uint32_t f = w[d] ^ 0xaaaaaaaau;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t g = (f >> (2 * s)) & 0x03030303u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[16 * d + 4 * k + s] = ubyte(g, k);
+      }
+    }
+  } else {
+    unpack_codes<BITS>(w, x);
+  }
+}
+
+// dword of the low bytes of four floats' bit patterns
+__device__ __forceinline__ uint32_t low_bytes4(float a, float b, float c, float d) {
+  const uint32_t ab = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0c0c0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x0c0c0400u);
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+template <int BITS>
+__device__ __forceinline__ void pack_magic(const float (&mg)[64], uint32_t (&w)[2 * BITS]) {
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t lo = low_bytes4(mg[8 * d], mg[8 * d + 2], mg[8 * d + 4], mg[8 * d + 6]);
+      const uint32_t hi = low_bytes4(mg[8 * d + 1], mg[8 * d + 3], mg[8 * d + 5], mg[8 * d + 7]);
+      w[d] = (lo & 0x0f0f0f0fu) | ((hi << 4) & 0xf0f0f0f0u);
+    }
+  } else if constexpr (BITS == 8) {
+#pragma unroll
+    for (int d = 0; d < 16; ++d)
+      w[d] = low_bytes4(mg[4 * d], mg[4 * d + 1], mg[4 * d + 2], mg[4 * d + 3]);
+  } else if constexpr (BITS == 2) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t acc = 0u;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t g = low_bytes4(mg[16 * d + s], mg[16 * d + 4 + s], mg[16 * d + 8 + s],
+                                      mg[16 * d + 12 + s]);
+        acc |= (g & 0x03030303u) << (2 * s);
+      }
+      w[d] = acc;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2 * BITS; ++i) w[i] = 0u;
+#pragma unroll
+    for (int n = 0; n < 64; ++n) {
+      const uint32_t val = __float_as_uint(mg[n]) & ((1u << BITS) - 1u);
+      const int pos = n * BITS, wi = pos >> 5, off = pos & 31;
+      w[wi] |= val << off;
+      if (off + BITS > 32) w[wi + 1] |= val >> (32 - off);
+    }
+  }
+}
+
 // Byte offset of piece q of the chunk owned by (row block rb, column pair p).
 template <int BITS, int NP>
 __device__ __forceinline__ int piece_off(int rb, int p, int q) {

@@ -26,16 +26,122 @@ namespace {
 
 template <int DK, int DV>
 struct SmemGdn {
-  float rowc[5][DK];                          // per-row constants of the current pass
-  float rho[DK];                              // row factor of Xt
+  // per-row constants: 0 kappa, 1 gamma, 2 theta, 3 rho (row factor of Xt),
+  // 4 pi (X / r = Xt pi) or sigma (uniform), 5 lambda (refit weight)
+  float rowc[6][DK];
   float2 colA[DK / 32][DV / 2];               // column partials per row block
   float2 colB[DK / 32][DV / 2];
+  float2 colM[DK / 32][DV / 2];
   float4 colC[DK / 32][DV / 2];
-  float rowt[DK / 32][32][DV / 2 + 1];        // row partials, transposed
+  float rowt[DK / 32][16][DV / 2 + 1];        // row partials of 16 rows, transposed
 };
 
+// Rows are owned by one wave (or half-wave), so row-wise LDS traffic only
+// needs ordering inside the wave.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+// Rows m .. m + R - 1 of both columns go into one output dword: R = 4 at 4 bits
+// (rows 4d .. 4d+3), 2 at 8 bits, 8 at 2 bits.  6-bit fields straddle dwords
+// and are packed after the loop.
+template <int BITS>
+__device__ __forceinline__ uint32_t pack_rows(const float* mg) {
+  if constexpr (BITS == 4) {
+    const uint32_t lo = low_bytes4(mg[0], mg[2], mg[4], mg[6]);
+    const uint32_t hi = low_bytes4(mg[1], mg[3], mg[5], mg[7]);
+    return (lo & 0x0f0f0f0fu) | ((hi << 4) & 0xf0f0f0f0u);
+  } else if constexpr (BITS == 8) {
+    return low_bytes4(mg[0], mg[1], mg[2], mg[3]);
+  } else {
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc |= (low_bytes4(mg[s], mg[4 + s], mg[8 + s], mg[12 + s]) & 0x03030303u) << (2 * s);
+    return acc;
+  }
+}
+
+// Codes by magic rounding and the fixed-code weighted least-squares column
+// sums (N_j, D_j), packed into w as they are produced.
+template <int BITS>
+__device__ __forceinline__ void codes_refit(float (&x)[64], const float* lam, float tau0,
+                                            float tau1, float4& nd, uint32_t (&w)[2 * BITS]) {
+  constexpr float QB = (float)((1 << (BITS - 1)) - 1);
+  constexpr int R = BITS == 6 ? 4 : 16 / BITS;   // rows per output dword
+  constexpr int RG = R < 4 ? 4 : R;              // rows per ordered group
+  float N0 = 0.f, N1 = 0.f, D0 = 0.f, D1 = 0.f;
+#pragma unroll
+  for (int g = 0; g < 32; g += RG) {
+    // order the work group by group so that rounded values are packed while
+    // their rows are still the only ones in flight
+#pragma unroll
+    for (int k = 0; k < 2 * RG; ++k) asm volatile("" : "+v"(x[2 * g + k]));
+#pragma unroll
+    for (int m = g; m < g + RG; m += 4) {
+      const float4 l4 = ld4(lam + m);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float pv0 = x[2 * (m + u)], pv1 = x[2 * (m + u) + 1];
+        // the clamp only acts when a column scale saturated at the FP16 maximum
+        const float mg0 = __builtin_amdgcn_fmed3f(fmaf(pv0, tau0, kMagic), kMagic - QB, kMagic + QB);
+        const float mg1 = __builtin_amdgcn_fmed3f(fmaf(pv1, tau1, kMagic), kMagic - QB, kMagic + QB);
+        const float z0 = mg0 - kMagic, z1 = mg1 - kMagic;
+        const float t0 = lv[u] * z0, t1 = lv[u] * z1;
+        N0 = fmaf(t0, pv0, N0);
+        N1 = fmaf(t1, pv1, N1);
+        D0 = fmaf(t0, z0, D0);
+        D1 = fmaf(t1, z1, D1);
+        x[2 * (m + u)] = mg0;
+        x[2 * (m + u) + 1] = mg1;
+      }
+    }
+    if constexpr (BITS != 6) {
+#pragma unroll
+      for (int d = g / R; d < (g + RG) / R; ++d) {
+        w[d] = pack_rows<BITS>(&x[2 * R * d]);
+        asm volatile("" : "+v"(w[d]));
+      }
+    }
+    asm volatile("" : "+v"(N0), "+v"(N1), "+v"(D0), "+v"(D1));
+  }
+  if constexpr (BITS == 6) pack_magic<6>(x, w);
+  nd = make_float4(N0, N1, D0, D1);
+}
+
+// Uniform rowwise codes: magic rounding of Xt * sigma_i, packed into w.
+template <int BITS>
+__device__ __forceinline__ void codes_rowwise(float (&x)[64], const float* sig,
+                                              uint32_t (&w)[2 * BITS]) {
+  constexpr float QB = (float)((1 << (BITS - 1)) - 1);
+  constexpr int R = BITS == 6 ? 4 : 16 / BITS;
+#pragma unroll
+  for (int m = 0; m < 32; m += 4) {
+    const float4 s4 = ld4(sig + m);
+    const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        x[2 * (m + u) + c] =
+            __builtin_amdgcn_fmed3f(fmaf(x[2 * (m + u) + c], sv[u], kMagic), kMagic - QB, kMagic + QB);
+      }
+      if constexpr (BITS != 6) {
+        const int row = m + u;
+        if ((row + 1) % R == 0) w[row / R] = pack_rows<BITS>(&x[2 * (row + 1 - R)]);
+      }
+    }
+  }
+  if constexpr (BITS == 6) pack_magic<6>(x, w);
+}
+
 // Quantized (b in {2,4,6,8}) head: uniform (UNI) or STEP dual-axis.
-template <int DK, int DV, int BITS, bool UNI>
+template <int DK, int DV, int BITS, bool UNI, int OP>
 __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, const int h,
                                            unsigned char* base, SmemGdn<DK, DV>& sm) {
   using G = Geo<DK, DV>;
@@ -43,21 +149,24 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
   constexpr float QB = (float)((1 << (BITS - 1)) - 1);
   constexpr float OFF = (float)(1 << (BITS - 1));
   const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p;
-  const int op = a.op;
+  const int r0 = 32 * rb;                     // first row of this lane's block
+  constexpr int op = OP;
   __half* rs_ptr = reinterpret_cast<__half*>(base + a.P.r_off[h]);
   __half* c_ptr = UNI ? nullptr : reinterpret_cast<__half*>(base + a.P.c_off[h]);
   const long long tk = (long long)tile * DK, tv = (long long)tile * DV;
 
   float x[64];
+  float y0 = 0.f, y1 = 0.f;
   if (op == OP_PACK) {
     const float* X = a.X + (long long)tile * DK * DV;
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
-      const float2 v2 = *reinterpret_cast<const float2*>(X + (32 * rb + m) * DV + j0);
+      const float2 v2 = *reinterpret_cast<const float2*>(X + (r0 + m) * DV + j0);
       x[2 * m] = v2.x;
       x[2 * m + 1] = v2.y;
     }
-    if (t < DK) sm.rho[t] = 1.0f;
+    if (p < 32) sm.rowc[3][r0 + p] = 1.0f;
+    wave_sync();
   } else {
     uint32_t wd[2 * BITS];
     load_chunk<BITS, NP>(base, rb, p, wd);
@@ -66,33 +175,33 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
       c0 = __half2float(c_ptr[j0]);
       c1 = __half2float(c_ptr[j0 + 1]);
     }
-    if (t < DK) {
-      const float rsi = __half2float(rs_ptr[t]);
+    if (p < 32) {
+      const int i = r0 + p;
+      const float rsi = __half2float(rs_ptr[i]);
       const float sc = UNI ? rsi : rsi / QB;  // dequantisation row factor
       if (op == OP_UNPACK) {
-        sm.rho[t] = sc;
+        sm.rowc[3][i] = sc;
       } else {
         const float alpha = a.gate[tile];
-        const float kk = a.k[tk + t], qq = a.q[tk + t], bk = a.beta[tile] * kk;
+        const float kk = a.k[tk + i], qq = a.q[tk + i], bk = a.beta[tile] * kk;
         const float rho = alpha * sc;
         // a vanishing retention keeps the division finite; the dropped part
         // (rp - rho) c_j z_ij is below 2^-60 of the write term
         const float rp = fmaxf(rho, fmaxf(fabsf(bk) * 0x1p-60f, 0x1p-100f));
-        sm.rowc[0][t] = kk * rho;  // kappa: key retrieval weight
-        sm.rowc[1][t] = bk / rp;   // gamma
-        sm.rowc[2][t] = qq * rp;   // theta: readout weight on Xt
-        sm.rho[t] = rp;
+        sm.rowc[0][i] = kk * rho;  // kappa: key retrieval weight
+        sm.rowc[1][i] = bk / rp;   // gamma
+        sm.rowc[2][i] = qq * rp;   // theta: readout weight on Xt
+        sm.rowc[3][i] = rp;
       }
     }
-    unpack_codes<BITS>(wd, x);
-    __syncthreads();
+    unpack_offset<BITS>(wd, x);
+    wave_sync();
     if (op == OP_UNPACK) {
       float* S = a.S_out + (long long)tile * DK * DV;
 #pragma unroll
       for (int m = 0; m < 32; ++m) {
-        const int i = 32 * rb + m;
-        const float sc = sm.rho[i];
-        *reinterpret_cast<float2*>(S + i * DV + j0) =
+        const float sc = sm.rowc[3][r0 + m];
+        *reinterpret_cast<float2*>(S + (r0 + m) * DV + j0) =
             make_float2(sc * c0 * (x[2 * m] - OFF), sc * c1 * (x[2 * m + 1] - OFF));
       }
       return;
@@ -100,11 +209,15 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
     // pass 1: key retrieval delta_j = c_j sum_i kappa_i (u_ij - off)
     float a0 = 0.f, a1 = 0.f, ks = 0.f;
 #pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      const float kap = sm.rowc[0][32 * rb + m];
-      a0 = fmaf(kap, x[2 * m], a0);
-      a1 = fmaf(kap, x[2 * m + 1], a1);
-      ks += kap;
+    for (int m = 0; m < 32; m += 4) {
+      const float4 k4 = ld4(&sm.rowc[0][r0 + m]);
+      const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a0 = fmaf(kv[u], x[2 * (m + u)], a0);
+        a1 = fmaf(kv[u], x[2 * (m + u) + 1], a1);
+        ks += kv[u];
+      }
     }
     sm.colA[rb][p] = make_float2(fmaf(-OFF, ks, a0), fmaf(-OFF, ks, a1));
     __syncthreads();
@@ -117,116 +230,121 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
     }
     const float2 vv = *reinterpret_cast<const float2*>(a.v + tv + j0);
     const float e0 = vv.x - c0 * d0, e1 = vv.y - c1 * d1;
-    // pass 2: Xt, readout partials
+    // pass 2: Xt = c_j (u - off) + gamma_i e_j, readout partials
     const float o0 = -OFF * c0, o1 = -OFF * c1;
-    float y0 = 0.f, y1 = 0.f;
 #pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      const int i = 32 * rb + m;
-      const float gam = sm.rowc[1][i], th = sm.rowc[2][i];
-      const float v0 = fmaf(c0, x[2 * m], fmaf(gam, e0, o0));
-      const float v1 = fmaf(c1, x[2 * m + 1], fmaf(gam, e1, o1));
-      x[2 * m] = v0;
-      x[2 * m + 1] = v1;
-      y0 = fmaf(th, v0, y0);
-      y1 = fmaf(th, v1, y1);
+    for (int m = 0; m < 32; m += 4) {
+      const float4 g4 = ld4(&sm.rowc[1][r0 + m]), t4 = ld4(&sm.rowc[2][r0 + m]);
+      const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, tv4[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float v0 = fmaf(c0, x[2 * (m + u)], fmaf(gv[u], e0, o0));
+        const float v1 = fmaf(c1, x[2 * (m + u) + 1], fmaf(gv[u], e1, o1));
+        x[2 * (m + u)] = v0;
+        x[2 * (m + u) + 1] = v1;
+        y0 = fmaf(tv4[u], v0, y0);
+        y1 = fmaf(tv4[u], v1, y1);
+      }
     }
     sm.colB[rb][p] = make_float2(y0, y1);
   }
-  // row statistics of Xt: sum |.| (STEP) or max |.| (uniform)
+  // row statistics of Xt (sum |.| for STEP, max |.| for uniform), 16 rows at a
+  // time through a per-wave transpose; the owner lane of each row then derives
+  // the row's stored scale and its constants for the next passes
+  uint32_t wd[2 * BITS];
 #pragma unroll
-  for (int m = 0; m < 32; ++m) {
-    const float u0 = fabsf(x[2 * m]), u1 = fabsf(x[2 * m + 1]);
-    sm.rowt[rb][m][p] = UNI ? fmaxf(u0, u1) : u0 + u1;
-  }
-  __syncthreads();
-  if (op == OP_DECODE && rb == 0) {
-    float y0 = 0.f, y1 = 0.f;
+  for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-    for (int r = 0; r < NRB; ++r) {
-      const float2 c = sm.colB[r][p];
-      y0 += c.x;
-      y1 += c.y;
+    for (int m = 0; m < 16; ++m) {
+      const float u0 = fabsf(x[2 * (16 * hf + m)]), u1 = fabsf(x[2 * (16 * hf + m) + 1]);
+      sm.rowt[rb][m][p] = UNI ? fmaxf(u0, u1) : u0 + u1;
     }
-    *reinterpret_cast<float2*>(a.y + tv + j0) = make_float2(y0, y1);
-  }
-  {
-    constexpr int LPR = NP / 32;  // lanes per row in the transpose step
-    const int m = p & 31, part = p >> 5;
+    wave_sync();
+    const int mm = p & 15, part = p >> 4;
     float s = 0.f;
-#pragma unroll 8
-    for (int pp = 0; pp < 32; ++pp) {
-      const float vv = sm.rowt[rb][m][part * 32 + pp];
+#pragma unroll
+    for (int pp = 0; pp < 16; ++pp) {
+      const float vv = sm.rowt[rb][mm][part * 16 + pp];
       s = UNI ? fmaxf(s, vv) : s + vv;
     }
-    if constexpr (LPR == 2) {
-      const float o = __shfl_xor(s, 32);
-      s = UNI ? fmaxf(s, o) : s + o;
+#pragma unroll
+    for (int o = 16; o < NP; o <<= 1) {
+      const float ov = __shfl_xor(s, o);
+      s = UNI ? fmaxf(s, ov) : s + ov;
     }
     if (part == 0) {
-      const int i = 32 * rb + m;
-      const float rp = sm.rho[i];
+      const int i = r0 + 16 * hf + mm;
+      const float rp = sm.rowc[3][i];
       if (UNI) {
-        const float si = fp16_scale(rp * s / QB);
+        const float pre = rp * s / QB;
+        const float si = fp16_scale(pre);
         rs_ptr[i] = __float2half_rn(si);
-        sm.rowc[3][i] = rp / si;  // code pre-value = Xt * sigma_i
+        sm.rowc[4][i] = rp / si;  // code pre-value = Xt * sigma_i
       } else {
         const float wi = a.P.w[h * DK + i];
         const float ri = fp16_scale(sqrtf(rp * s / (float)DV / wi));
         rs_ptr[i] = __float2half_rn(ri);
-        sm.rowc[3][i] = rp / ri;                  // pi: X / r_i = Xt * pi_i
-        sm.rowc[4][i] = wi * wi * ri * ri / QB;   // lambda: refit weight
+        sm.rowc[4][i] = rp / ri;                 // pi: X / r_i = Xt * pi_i
+        sm.rowc[5][i] = wi * wi * ri * ri / QB;  // lambda: refit weight
       }
     }
+    wave_sync();
   }
-  __syncthreads();
   if constexpr (UNI) {
+    if (op == OP_DECODE) {
+      __syncthreads();
+      if (rb == 0) {
+        float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      const float sg = sm.rowc[3][32 * rb + m];
-      x[2 * m] = fminf(fmaxf(rintf(fmaf(x[2 * m], sg, OFF)), OFF - QB), OFF + QB);
-      x[2 * m + 1] = fminf(fmaxf(rintf(fmaf(x[2 * m + 1], sg, OFF)), OFF - QB), OFF + QB);
+        for (int r = 0; r < NRB; ++r) {
+          s0 += sm.colB[r][p].x;
+          s1 += sm.colB[r][p].y;
+        }
+        *reinterpret_cast<float2*>(a.y + tv + j0) = make_float2(s0, s1);
+      }
     }
+    codes_rowwise<BITS>(x, &sm.rowc[4][r0], wd);
   } else {
     // pass 3: P = X / r_i and the column absmax
     float mx0 = 0.f, mx1 = 0.f;
 #pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      const float pi = sm.rowc[3][32 * rb + m];
-      x[2 * m] *= pi;
-      x[2 * m + 1] *= pi;
-      mx0 = fmaxf(mx0, fabsf(x[2 * m]));
-      mx1 = fmaxf(mx1, fabsf(x[2 * m + 1]));
+    for (int m = 0; m < 32; m += 4) {
+      const float4 p4 = ld4(&sm.rowc[4][r0 + m]);
+      const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        x[2 * (m + u)] *= pv[u];
+        x[2 * (m + u) + 1] *= pv[u];
+      }
+      mx0 = fmaxf(mx0, fmaxf(fmaxf(fabsf(x[2 * m]), fabsf(x[2 * m + 2])),
+                             fmaxf(fabsf(x[2 * m + 4]), fabsf(x[2 * m + 6]))));
+      mx1 = fmaxf(mx1, fmaxf(fmaxf(fabsf(x[2 * m + 1]), fabsf(x[2 * m + 3])),
+                             fmaxf(fabsf(x[2 * m + 5]), fabsf(x[2 * m + 7]))));
     }
-    sm.colA[rb][p] = make_float2(mx0, mx1);
+    sm.colM[rb][p] = make_float2(mx0, mx1);
     __syncthreads();
+    if (op == OP_DECODE && rb == 0) {
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < NRB; ++r) {
+        s0 += sm.colB[r][p].x;
+        s1 += sm.colB[r][p].y;
+      }
+      *reinterpret_cast<float2*>(a.y + tv + j0) = make_float2(s0, s1);
+    }
     float m0 = 0.f, m1 = 0.f;
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
-      const float2 c = sm.colA[r][p];
+      const float2 c = sm.colM[r][p];
       m0 = fmaxf(m0, c.x);
       m1 = fmaxf(m1, c.y);
     }
     const float cz0 = fp16_scale(m0), cz1 = fp16_scale(m1);
     const float tau0 = QB / cz0, tau1 = QB / cz1;
-    // pass 4: codes and the fixed-code weighted least-squares column sums
-    float N0 = 0.f, N1 = 0.f, D0 = 0.f, D1 = 0.f;
-#pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      const float lam = sm.rowc[4][32 * rb + m];
-      const float pv0 = x[2 * m], pv1 = x[2 * m + 1];
-      const float u0 = fminf(fmaxf(rintf(fmaf(pv0, tau0, OFF)), OFF - QB), OFF + QB);
-      const float u1 = fminf(fmaxf(rintf(fmaf(pv1, tau1, OFF)), OFF - QB), OFF + QB);
-      const float z0 = u0 - OFF, z1 = u1 - OFF;
-      const float t0 = lam * z0, t1 = lam * z1;
-      N0 = fmaf(t0, pv0, N0);
-      N1 = fmaf(t1, pv1, N1);
-      D0 = fmaf(t0, z0, D0);
-      D1 = fmaf(t1, z1, D1);
-      x[2 * m] = u0;
-      x[2 * m + 1] = u1;
-    }
-    sm.colC[rb][p] = make_float4(N0, N1, D0, D1);
+    // pass 4: codes by magic rounding, fixed-code weighted least-squares sums
+    float4 nd;
+    codes_refit<BITS>(x, &sm.rowc[5][r0], tau0, tau1, nd, wd);
+    sm.colC[rb][p] = nd;
     __syncthreads();
     if (rb == 0) {
       float n0 = 0.f, n1 = 0.f, dd0 = 0.f, dd1 = 0.f;
@@ -244,19 +362,17 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
       c_ptr[j0 + 1] = __float2half_rn(cf1);
     }
   }
-  uint32_t wd[2 * BITS];
-  pack_codes<BITS>(x, wd);
   store_chunk<BITS, NP>(base, rb, p, wd);
 }
 
 // FP16 pivot head of a STEP GDN plan: the state is kept as FP16 values.
-template <int DK, int DV>
+template <int DK, int DV, int OP>
 __device__ __forceinline__ void pivot_tile(const TileArgs& a, const int tile, const int h,
                                            unsigned char* base, SmemGdn<DK, DV>& sm) {
   using G = Geo<DK, DV>;
   constexpr int NP = G::NP, NRB = G::NRB;
   const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p;
-  const int op = a.op;
+  constexpr int op = OP;
   const long long tk = (long long)tile * DK, tv = (long long)tile * DV;
   float x[64];
   if (op == OP_PACK) {
@@ -339,14 +455,15 @@ __device__ __forceinline__ void pivot_tile(const TileArgs& a, const int tile, co
   store_chunk<16, NP>(base, rb, p, wd);
 }
 
-template <int DK, int DV>
-__global__ __launch_bounds__((DK / 32) * (DV / 2)) void gdn_tile_kernel(TileArgs a) {
+template <int DK, int DV, int OP>
+__global__ __launch_bounds__((DK / 32) * (DV / 2))
+__attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_tile_kernel(TileArgs a) {
   __shared__ SmemGdn<DK, DV> sm;
   const int tile = blockIdx.x;
   int h = 0;
   unsigned char* base = nullptr;
   if (!resolve_tile(a, tile, h, base)) {
-    if (a.op == OP_DECODE) {
+    if (OP == OP_DECODE) {
       const int t = threadIdx.x;
       if (t < DV) a.y[(long long)tile * DV + t] = __builtin_nanf("");
     }
@@ -356,23 +473,23 @@ __global__ __launch_bounds__((DK / 32) * (DV / 2)) void gdn_tile_kernel(TileArgs
   const bool uni = a.P.mode == SQ_MODE_UNIFORM;
   switch (bits) {
     case 2:
-      if (uni) quant_tile<DK, DV, 2, true>(a, tile, h, base, sm);
-      else quant_tile<DK, DV, 2, false>(a, tile, h, base, sm);
+      if (uni) quant_tile<DK, DV, 2, true, OP>(a, tile, h, base, sm);
+      else quant_tile<DK, DV, 2, false, OP>(a, tile, h, base, sm);
       break;
     case 4:
-      if (uni) quant_tile<DK, DV, 4, true>(a, tile, h, base, sm);
-      else quant_tile<DK, DV, 4, false>(a, tile, h, base, sm);
+      if (uni) quant_tile<DK, DV, 4, true, OP>(a, tile, h, base, sm);
+      else quant_tile<DK, DV, 4, false, OP>(a, tile, h, base, sm);
       break;
     case 6:
-      if (uni) quant_tile<DK, DV, 6, true>(a, tile, h, base, sm);
-      else quant_tile<DK, DV, 6, false>(a, tile, h, base, sm);
+      if (uni) quant_tile<DK, DV, 6, true, OP>(a, tile, h, base, sm);
+      else quant_tile<DK, DV, 6, false, OP>(a, tile, h, base, sm);
       break;
     case 8:
-      if (uni) quant_tile<DK, DV, 8, true>(a, tile, h, base, sm);
-      else quant_tile<DK, DV, 8, false>(a, tile, h, base, sm);
+      if (uni) quant_tile<DK, DV, 8, true, OP>(a, tile, h, base, sm);
+      else quant_tile<DK, DV, 8, false, OP>(a, tile, h, base, sm);
       break;
     case 16:
-      if (!uni) pivot_tile<DK, DV>(a, tile, h, base, sm);
+      if (!uni) pivot_tile<DK, DV, OP>(a, tile, h, base, sm);
       break;
     default:
       break;
@@ -381,7 +498,11 @@ __global__ __launch_bounds__((DK / 32) * (DV / 2)) void gdn_tile_kernel(TileArgs
 
 template <int DK, int DV>
 hipError_t launch(const TileArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gdn_tile_kernel<DK, DV>), dim3(a.n_tiles), dim3((DK / 32) * (DV / 2)), 0, s, a);
+  const dim3 grid(a.n_tiles), block((DK / 32) * (DV / 2));
+  if (a.op == OP_DECODE) hipLaunchKernelGGL((gdn_tile_kernel<DK, DV, OP_DECODE>), grid, block, 0, s, a);
+  else if (a.op == OP_PACK) hipLaunchKernelGGL((gdn_tile_kernel<DK, DV, OP_PACK>), grid, block, 0, s, a);
+  else if (a.op == OP_UNPACK) hipLaunchKernelGGL((gdn_tile_kernel<DK, DV, OP_UNPACK>), grid, block, 0, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
