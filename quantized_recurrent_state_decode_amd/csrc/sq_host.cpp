@@ -104,16 +104,29 @@ void finish_plan(sq_plan* P) {
   P->analytic_bytes = analytic;
   P->max_head_bytes = maxh;
 
+  // heads grouped by code width for the per-width decode launches
+  const int widths[5] = {2, 4, 6, 8, 16};
+  P->cls_heads.clear();
+  for (int c = 0; c < 5; ++c) {
+    P->cls_start[c] = (int)P->cls_heads.size();
+    for (int h = 0; h < H; ++h)
+      if (P->head_bits[h] == widths[c]) P->cls_heads.push_back(h);
+    P->cls_count[c] = (int)P->cls_heads.size() - P->cls_start[c];
+  }
   std::vector<unsigned char>& img = P->image;
   img.clear();
   P->o_head_off = put(img, P->head_off);
   P->o_head_bits = put(img, P->head_bits);
+  P->winv.resize(P->w.size());
+  for (size_t i = 0; i < P->w.size(); ++i) P->winv[i] = 1.0f / P->w[i];
   P->o_w = put(img, P->w);
+  P->o_winv = put(img, P->winv);
   P->o_row_key = put(img, P->row_key);
   P->o_row_bits = put(img, P->row_bits);
   P->o_row_off = put(img, P->row_off);
   P->o_r_off = put(img, P->r_off);
   P->o_c_off = put(img, P->c_off);
+  P->o_cls = put(img, P->cls_heads);
   img.resize(round_up((long long)img.size(), 256), 0);
 }
 
@@ -133,11 +146,13 @@ DevPlan dev_view(const sq_plan* P, const void* dev) {
   d.head_off = reinterpret_cast<const long long*>(b + P->o_head_off);
   d.head_bits = reinterpret_cast<const int*>(b + P->o_head_bits);
   d.w = reinterpret_cast<const float*>(b + P->o_w);
+  d.winv = reinterpret_cast<const float*>(b + P->o_winv);
   d.row_key = reinterpret_cast<const int*>(b + P->o_row_key);
   d.row_bits = reinterpret_cast<const int*>(b + P->o_row_bits);
   d.row_off = reinterpret_cast<const int*>(b + P->o_row_off);
   d.r_off = reinterpret_cast<const int*>(b + P->o_r_off);
   d.c_off = reinterpret_cast<const int*>(b + P->o_c_off);
+  d.cls_heads = reinterpret_cast<const int*>(b + P->o_cls);
   return d;
 }
 
@@ -169,7 +184,20 @@ sq_status validate_slots(const int32_t* slots, int B, long long n_slots, hipStre
 hipError_t dispatch(const sq_plan* P, const TileArgs& a, hipStream_t st) {
   if (P->mode == SQ_MODE_WINDOW) return launch_tile_window(a, st);
   if (P->mode == SQ_MODE_STEP && P->kind == SQ_KIND_KDA) return launch_tile_kda(a, st);
-  return launch_tile_gdn(a, st);
+  if (a.op != OP_DECODE || a.head_ids) return launch_tile_gdn(a, st);
+  // decode: one launch per code width, largest class first
+  int order[5] = {0, 1, 2, 3, 4};
+  std::sort(order, order + 5, [&](int x, int y) { return P->cls_count[x] > P->cls_count[y]; });
+  for (int c : order) {
+    if (!P->cls_count[c]) continue;
+    TileArgs b = a;
+    b.cls_first = P->cls_start[c];
+    b.cls_n = P->cls_count[c];
+    b.n_tiles = a.B * b.cls_n;
+    hipError_t e = launch_decode_gdn(b, (const int[]){2, 4, 6, 8, 16}[c], st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 TileArgs base_args(const sq_plan* P, const void* dev_plan, int op) {

@@ -18,11 +18,13 @@ struct DevPlan {
   const long long* head_off;  // [H]
   const int* head_bits;       // [H] GDN/uniform width (16 = FP16 pivot head)
   const float* w;             // [H*dk] impact factors (STEP)
+  const float* winv;          // [H*dk] 1 / w
   const int* row_key;         // [H*dk] KDA: key row held by storage row s
   const int* row_bits;        // [H*dk] KDA: width of storage row s
   const int* row_off;         // [H*dk] KDA: byte offset of storage row s in its head
   const int* r_off;           // [H] byte offset of the r (or s) array in the head
   const int* c_off;           // [H] byte offset of the c array in the head
+  const int* cls_heads;       // [H] heads grouped by code width (2, 4, 6, 8, 16)
 };
 
 struct sq_plan {
@@ -33,10 +35,14 @@ struct sq_plan {
   int max_head_bytes = 0;
   std::vector<long long> head_off;
   std::vector<int> head_bits, unit_bits, row_key, row_bits, row_off, r_off, c_off;
-  std::vector<float> w;
+  std::vector<float> w, winv;
   // image of the device tables and the offsets of each array in it
   std::vector<unsigned char> image;
-  size_t o_head_off = 0, o_head_bits = 0, o_w = 0, o_row_key = 0, o_row_bits = 0,
+  std::vector<int> cls_heads;           // heads grouped by width
+  int cls_start[5] = {0, 0, 0, 0, 0};   // per width class: first index in cls_heads
+  int cls_count[5] = {0, 0, 0, 0, 0};   // per width class: number of heads
+  size_t o_cls = 0;
+  size_t o_head_off = 0, o_head_bits = 0, o_w = 0, o_winv = 0, o_row_key = 0, o_row_bits = 0,
          o_row_off = 0, o_r_off = 0, o_c_off = 0;
 };
 
@@ -58,10 +64,12 @@ struct TileArgs {
   unsigned char* out;        // quantize-only: packed head t at out + t*out_stride
   long long out_stride;
   int n_tiles;
+  int cls_first, cls_n;      // decode by width class: heads cls_heads[cls_first ..+cls_n)
 };
 
 // Kernel launchers (defined in the .hip files).
 hipError_t launch_tile_gdn(const TileArgs& a, hipStream_t s);     // uniform + STEP GDN
+hipError_t launch_decode_gdn(const TileArgs& a, int bits, hipStream_t s);  // one width class
 hipError_t launch_tile_kda(const TileArgs& a, hipStream_t s);     // STEP KDA
 hipError_t launch_tile_window(const TileArgs& a, hipStream_t s);  // per-window variant
 hipError_t launch_dense_step(int kind, int H, int dk, int dv, float* S, long long n_slots,

@@ -78,9 +78,17 @@ __device__ __forceinline__ void pack_codes(const float (&u)[64], uint32_t (&w)[2
 // bits without converting back.
 constexpr float kMagic = 12582912.0f;
 
+// byte k of w as a float: one v_cvt_f32_ubyte{k} (written out so that the
+// compiler does not narrow it to a bit-field extract plus a conversion)
 __device__ __forceinline__ float ubyte(uint32_t w, int k) {
-  return (float)((w >> (8 * k)) & 0xffu);
+  float r;
+  if (k == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(w));
+  else if (k == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(w));
+  else if (k == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(w));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(w));
+  return r;
 }
+__device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 template <int BITS>
 __device__ __forceinline__ void unpack_offset(const uint32_t (&w)[2 * BITS], float (&x)[64]) {

@@ -29,6 +29,7 @@ struct SmemGdn {
   // per-row constants: 0 kappa, 1 gamma, 2 theta, 3 rho (row factor of Xt),
   // 4 pi (X / r = Xt pi) or sigma (uniform), 5 lambda (refit weight)
   float rowc[6][DK];
+  float ksum[DK / 32];                        // sum of kappa per row block
   float2 colA[DK / 32][DV / 2];               // column partials per row block
   float2 colB[DK / 32][DV / 2];
   float2 colM[DK / 32][DV / 2];
@@ -66,13 +67,23 @@ __device__ __forceinline__ uint32_t pack_rows(const float* mg) {
   }
 }
 
+// 16 six-bit fields (rows m .. m+7, both columns) fill exactly 3 dwords.
+__device__ __forceinline__ void pack_rows6(const float* mg, uint32_t* w) {
+  uint32_t v[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) v[n] = __float_as_uint(mg[n]) & 63u;
+  w[0] = v[0] | (v[1] << 6) | (v[2] << 12) | (v[3] << 18) | (v[4] << 24) | (v[5] << 30);
+  w[1] = (v[5] >> 2) | (v[6] << 4) | (v[7] << 10) | (v[8] << 16) | (v[9] << 22) | (v[10] << 28);
+  w[2] = (v[10] >> 4) | (v[11] << 2) | (v[12] << 8) | (v[13] << 14) | (v[14] << 20) | (v[15] << 26);
+}
+
 // Codes by magic rounding and the fixed-code weighted least-squares column
 // sums (N_j, D_j), packed into w as they are produced.
-template <int BITS>
+template <int BITS, bool CLAMP>
 __device__ __forceinline__ void codes_refit(float (&x)[64], const float* lam, float tau0,
                                             float tau1, float4& nd, uint32_t (&w)[2 * BITS]) {
   constexpr float QB = (float)((1 << (BITS - 1)) - 1);
-  constexpr int R = BITS == 6 ? 4 : 16 / BITS;   // rows per output dword
+  constexpr int R = BITS == 6 ? 8 : 16 / BITS;   // rows per output dword (3 dwords at 6 bits)
   constexpr int RG = R < 4 ? 4 : R;              // rows per ordered group
   float N0 = 0.f, N1 = 0.f, D0 = 0.f, D1 = 0.f;
 #pragma unroll
@@ -88,9 +99,11 @@ __device__ __forceinline__ void codes_refit(float (&x)[64], const float* lam, fl
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float pv0 = x[2 * (m + u)], pv1 = x[2 * (m + u) + 1];
-        // the clamp only acts when a column scale saturated at the FP16 maximum
-        const float mg0 = __builtin_amdgcn_fmed3f(fmaf(pv0, tau0, kMagic), kMagic - QB, kMagic + QB);
-        const float mg1 = __builtin_amdgcn_fmed3f(fmaf(pv1, tau1, kMagic), kMagic - QB, kMagic + QB);
+        float mg0 = fmaf(pv0, tau0, kMagic), mg1 = fmaf(pv1, tau1, kMagic);
+        if constexpr (CLAMP) {  // a column scale saturated at the FP16 maximum
+          mg0 = __builtin_amdgcn_fmed3f(mg0, kMagic - QB, kMagic + QB);
+          mg1 = __builtin_amdgcn_fmed3f(mg1, kMagic - QB, kMagic + QB);
+        }
         const float z0 = mg0 - kMagic, z1 = mg1 - kMagic;
         const float t0 = lv[u] * z0, t1 = lv[u] * z1;
         N0 = fmaf(t0, pv0, N0);
@@ -101,7 +114,11 @@ __device__ __forceinline__ void codes_refit(float (&x)[64], const float* lam, fl
         x[2 * (m + u) + 1] = mg1;
       }
     }
-    if constexpr (BITS != 6) {
+    if constexpr (BITS == 6) {
+      pack_rows6(&x[2 * g], &w[3 * (g / 8)]);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) asm volatile("" : "+v"(w[3 * (g / 8) + k]));
+    } else {
 #pragma unroll
       for (int d = g / R; d < (g + RG) / R; ++d) {
         w[d] = pack_rows<BITS>(&x[2 * R * d]);
@@ -110,7 +127,6 @@ __device__ __forceinline__ void codes_refit(float (&x)[64], const float* lam, fl
     }
     asm volatile("" : "+v"(N0), "+v"(N1), "+v"(D0), "+v"(D1));
   }
-  if constexpr (BITS == 6) pack_magic<6>(x, w);
   nd = make_float4(N0, N1, D0, D1);
 }
 
@@ -188,10 +204,16 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
         // a vanishing retention keeps the division finite; the dropped part
         // (rp - rho) c_j z_ij is below 2^-60 of the write term
         const float rp = fmaxf(rho, fmaxf(fabsf(bk) * 0x1p-60f, 0x1p-100f));
-        sm.rowc[0][i] = kk * rho;  // kappa: key retrieval weight
-        sm.rowc[1][i] = bk / rp;   // gamma
-        sm.rowc[2][i] = qq * rp;   // theta: readout weight on Xt
+        const float kap = kk * rho;
+        sm.rowc[0][i] = kap;               // kappa: key retrieval weight
+        sm.rowc[1][i] = bk * frcp(rp);     // gamma
+        sm.rowc[2][i] = qq * rp;           // theta: readout weight on Xt
         sm.rowc[3][i] = rp;
+        // sum of kappa over the block's 32 rows (offset of the unpacked codes)
+        float ksum = kap;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) ksum += __shfl_xor(ksum, o);
+        if (p == 0) sm.ksum[rb] = ksum;
       }
     }
     unpack_offset<BITS>(wd, x);
@@ -207,7 +229,8 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
       return;
     }
     // pass 1: key retrieval delta_j = c_j sum_i kappa_i (u_ij - off)
-    float a0 = 0.f, a1 = 0.f, ks = 0.f;
+    const float ks = sm.ksum[rb];
+    float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int m = 0; m < 32; m += 4) {
       const float4 k4 = ld4(&sm.rowc[0][r0 + m]);
@@ -216,7 +239,6 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
       for (int u = 0; u < 4; ++u) {
         a0 = fmaf(kv[u], x[2 * (m + u)], a0);
         a1 = fmaf(kv[u], x[2 * (m + u) + 1], a1);
-        ks += kv[u];
       }
     }
     sm.colA[rb][p] = make_float2(fmaf(-OFF, ks, a0), fmaf(-OFF, ks, a1));
@@ -276,16 +298,15 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
       const int i = r0 + 16 * hf + mm;
       const float rp = sm.rowc[3][i];
       if (UNI) {
-        const float pre = rp * s / QB;
-        const float si = fp16_scale(pre);
+        const float si = fp16_scale(rp * s * (1.0f / QB));
         rs_ptr[i] = __float2half_rn(si);
-        sm.rowc[4][i] = rp / si;  // code pre-value = Xt * sigma_i
+        sm.rowc[4][i] = rp * frcp(si);  // code pre-value = Xt * sigma_i
       } else {
         const float wi = a.P.w[h * DK + i];
-        const float ri = fp16_scale(sqrtf(rp * s / (float)DV / wi));
+        const float ri = fp16_scale(sqrtf(rp * s * (1.0f / (float)DV) * a.P.winv[h * DK + i]));
         rs_ptr[i] = __float2half_rn(ri);
-        sm.rowc[4][i] = rp / ri;                 // pi: X / r_i = Xt * pi_i
-        sm.rowc[5][i] = wi * wi * ri * ri / QB;  // lambda: refit weight
+        sm.rowc[4][i] = rp * frcp(ri);                  // pi: X / r_i = Xt * pi_i
+        sm.rowc[5][i] = wi * wi * ri * ri * (1.0f / QB);  // lambda: refit weight
       }
     }
     wave_sync();
@@ -322,7 +343,9 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
                              fmaxf(fabsf(x[2 * m + 5]), fabsf(x[2 * m + 7]))));
     }
     sm.colM[rb][p] = make_float2(mx0, mx1);
-    __syncthreads();
+    // below the FP16 maximum, c0 >= max |P| (1 - 2^-11) keeps every code within
+    // +-q_b without a clamp; a saturated column anywhere switches the tile to it
+    const bool sat = __syncthreads_or(fmaxf(mx0, mx1) > kFp16Max) != 0;
     if (op == OP_DECODE && rb == 0) {
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
@@ -340,10 +363,11 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
       m1 = fmaxf(m1, c.y);
     }
     const float cz0 = fp16_scale(m0), cz1 = fp16_scale(m1);
-    const float tau0 = QB / cz0, tau1 = QB / cz1;
+    const float tau0 = QB * frcp(cz0), tau1 = QB * frcp(cz1);
     // pass 4: codes by magic rounding, fixed-code weighted least-squares sums
     float4 nd;
-    codes_refit<BITS>(x, &sm.rowc[5][r0], tau0, tau1, nd, wd);
+    if (sat) codes_refit<BITS, true>(x, &sm.rowc[5][r0], tau0, tau1, nd, wd);
+    else codes_refit<BITS, false>(x, &sm.rowc[5][r0], tau0, tau1, nd, wd);
     sm.colC[rb][p] = nd;
     __syncthreads();
     if (rb == 0) {
@@ -356,8 +380,8 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
         dd0 += c.z;
         dd1 += c.w;
       }
-      const float cf0 = dd0 > 0.f ? fp16_scale(QB * n0 / dd0) : cz0;
-      const float cf1 = dd1 > 0.f ? fp16_scale(QB * n1 / dd1) : cz1;
+      const float cf0 = dd0 > 0.f ? fp16_scale(QB * n0 * frcp(dd0)) : cz0;
+      const float cf1 = dd1 > 0.f ? fp16_scale(QB * n1 * frcp(dd1)) : cz1;
       c_ptr[j0] = __float2half_rn(cf0);
       c_ptr[j0 + 1] = __float2half_rn(cf1);
     }
@@ -496,17 +520,73 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_tile_kernel(TileArgs a) {
   }
 }
 
+
+// Decode of one code-width class: the heads of the class are
+// cls_heads[cls_first .. cls_first + cls_n); tile t = (batch row t / cls_n,
+// class head t % cls_n).  One kernel per width keeps each width's register
+// allocation separate.
+template <int DK, int DV, int BITS, bool UNI>
+__global__ __launch_bounds__((DK / 32) * (DV / 2))
+__attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_decode_kernel(TileArgs a) {
+  __shared__ SmemGdn<DK, DV> sm;
+  const int t = blockIdx.x;
+  const int bi = t / a.cls_n;
+  const int h = a.P.cls_heads[a.cls_first + (t - bi * a.cls_n)];
+  const int tile = bi * a.P.H + h;
+  const int slot = a.slots[bi];
+  if (slot < 0 || (long long)slot >= a.n_slots) {
+    if (threadIdx.x < DV) a.y[(long long)tile * DV + threadIdx.x] = __builtin_nanf("");
+    return;
+  }
+  unsigned char* base = a.pool + (long long)slot * a.P.slot_bytes + a.P.head_off[h];
+  if constexpr (BITS == 16) pivot_tile<DK, DV, OP_DECODE>(a, tile, h, base, sm);
+  else quant_tile<DK, DV, BITS, UNI, OP_DECODE>(a, tile, h, base, sm);
+}
+
+template <int DK, int DV, int BITS>
+hipError_t launch_class(const TileArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_tiles), block((DK / 32) * (DV / 2));
+  if (a.P.mode == SQ_MODE_UNIFORM) {
+    if constexpr (BITS == 16) return hipErrorInvalidValue;
+    else hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, BITS, true>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, BITS, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_class_bits(const TileArgs& a, int bits, hipStream_t s) {
+  switch (bits) {
+    case 2: return launch_class<DK, DV, 2>(a, s);
+    case 4: return launch_class<DK, DV, 4>(a, s);
+    case 6: return launch_class<DK, DV, 6>(a, s);
+    case 8: return launch_class<DK, DV, 8>(a, s);
+    case 16: return launch_class<DK, DV, 16>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int DK, int DV>
 hipError_t launch(const TileArgs& a, hipStream_t s) {
   const dim3 grid(a.n_tiles), block((DK / 32) * (DV / 2));
-  if (a.op == OP_DECODE) hipLaunchKernelGGL((gdn_tile_kernel<DK, DV, OP_DECODE>), grid, block, 0, s, a);
-  else if (a.op == OP_PACK) hipLaunchKernelGGL((gdn_tile_kernel<DK, DV, OP_PACK>), grid, block, 0, s, a);
+  if (a.op == OP_DECODE) return hipErrorInvalidValue;  // decode goes through the width classes
+  if (a.op == OP_PACK) hipLaunchKernelGGL((gdn_tile_kernel<DK, DV, OP_PACK>), grid, block, 0, s, a);
   else if (a.op == OP_UNPACK) hipLaunchKernelGGL((gdn_tile_kernel<DK, DV, OP_UNPACK>), grid, block, 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_decode_gdn(const TileArgs& a, int bits, hipStream_t s) {
+  const int dk = a.P.dk, dv = a.P.dv;
+  if (dk == 128 && dv == 128) return launch_class_bits<128, 128>(a, bits, s);
+  if (dk == 64 && dv == 64) return launch_class_bits<64, 64>(a, bits, s);
+  if (dk == 128 && dv == 64) return launch_class_bits<128, 64>(a, bits, s);
+  if (dk == 64 && dv == 128) return launch_class_bits<64, 128>(a, bits, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_tile_gdn(const TileArgs& a, hipStream_t s) {
   const int dk = a.P.dk, dv = a.P.dv;
