@@ -30,6 +30,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "state-update steps/s and HBM GB/s (% of peak) at batch 512, 1 GPU"
+# kernels one decode step launches (GDN STEP / uniform: one per code-width class)
+KERNEL = {"step": "gdn_decode_kernel<128,128,b> (one launch per code width)",
+          "uniform": "gdn_decode_kernel<d,d,b,uniform>", "window": "window_tile_kernel<128,128>",
+          "kda": "kda_tile_kernel<128,128>"}
 HBM_PEAK_GBS = 8000.0
 
 
@@ -46,6 +50,28 @@ def _plan(sq, w):
     return sq.sq_calibrate_bits(stats, {"nominal_bits": st["nominal_bits"],
                                         "pivot_frac": st["pivot_frac"], "gamma": st["gamma"],
                                         "horizon": st["horizon"]})
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per step from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary of this workload, if the decode kernel sources are still the ones
+    the counters were taken on (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_step", "kernel_source_sha256_16"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    csrc = os.path.join(ROOT, "quantized_recurrent_state_decode_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("tile_gdn.hip", "tile_common.h", "sq_internal.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    if fields.get("kernel_source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    return int(fields["traffic_bytes_per_step"])
 
 
 def algorithmic_bytes(desc, w) -> int:
@@ -66,16 +92,16 @@ def algorithmic_bytes(desc, w) -> int:
     return int(B * H * per_tile) + io
 
 
-def build_state(sq, w, pools, slots_dev):
-    """Warm-up state: `warmup_steps` fp32 dense steps from S = 0 with the
-    library's dense kernel, then packed into every pool."""
+def build_state(sq, w, pools, slots_dev, steps):
+    """Warm-up state: `steps` fp32 dense steps from S = 0 with the library's
+    dense kernel, then packed into every pool."""
     import torch
     from synth import inputs as SI
     params = SI.gate_params(w)
     S = torch.zeros((w.batch, w.heads, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
     ident = torch.arange(w.batch, dtype=torch.int32, device="cuda")
     y = torch.empty((w.batch, w.heads, w.d_v), dtype=torch.float32, device="cuda")
-    for t in range(w.warmup_steps):
+    for t in range(steps):
         inp = {k: torch.from_numpy(v).cuda() for k, v in SI.warmup_inputs(w, t, params).items()}
         sq.sq_dense_step(0 if w.kind == "gdn" else 1, w.heads, w.d_k, w.d_v, S, w.batch, ident,
                          w.batch, inp["q"], inp["k"], inp["v"], inp["beta"], inp["gate"], y)
@@ -118,6 +144,7 @@ def cpu_baseline(w, desc, pool_bytes: bytes, slots, budget_s: float) -> dict:
                 if w.mode == "window":
                     r = OW.window_step(st, q, k, v, beta, float(inp["gate"][b, h]), w.window)
                     states[b][h] = r["state"]
+                    tiles += 1
                     continue
                 dvec = R.gate_vector(inp["gate"][b, h].astype(np.float64),
                                      "gdn" if w.mode == "uniform" else w.kind, w.d_k)
@@ -155,6 +182,11 @@ def main():
     ap.add_argument("--input-sets", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--state-warmup", type=int, default=None,
+                    help="fp32 steps that build the initial state (default: the workload's 128)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before timing, copy MIB MiB device-to-device once (a plain copy of "
+                         "known size for scaling HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -178,7 +210,15 @@ def main():
         pool = torch.empty(sq.sq_pool_bytes(plan, w.n_slots), dtype=torch.uint8, device="cuda")
         sq.sq_pool_init(plan, dp, pool, w.n_slots)
         pools.append({"plan": plan, "dev_plan": dp, "pool": pool})
-    build_state(sq, w, pools, slots_dev)
+    build_state(sq, w, pools, slots_dev,
+                w.warmup_steps if args.state_warmup is None else args.state_warmup)
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     params = SI.gate_params(w)
     sets = []
     for i in range(args.input_sets):
@@ -245,10 +285,12 @@ def main():
                    "input_sets": args.input_sets, "algorithmic_bytes_per_step": abytes,
                    "state_gbs": gbs_step, "pct_of_hbm_peak": 100.0 * gbs_step / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": gbs_kernel, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": gbs_kernel / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "gdn_tile_kernel<128,128>" if w.mode != "window" else
-                     "window_tile_kernel<128,128>", "launch_ms": launch_ms,
-                     "bytes_per_launch": abytes},
+                     "unit": "GB/s", "frac": gbs_kernel / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name),
+                     "kernel": KERNEL[w.mode if w.kind == "gdn" else "kda"],
+                     "launch_ms": launch_ms, "bytes_per_launch": abytes,
+                     "launch": "one sq_decode_step call (all its kernel launches), HIP events "
+                               "on the launch stream"},
     }
     if not args.no_cpu:
         torch.cuda.synchronize()
