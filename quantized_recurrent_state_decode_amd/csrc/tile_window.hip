@@ -13,30 +13,37 @@
 // (Sec. 2.5, App. B.3): C_a = max(sqrt(mean_j |S_aj|), c_floor),
 // T = diag(C)^-1 S, B_j = max_a |T_aj|, Z = clamp(rne(127 T / B), +-127).
 //
-// S0^T x costs one fused multiply-add per boundary element for each of the
-// two read vectors; lanes own 2 columns x 32 rows of the INT8 boundary
-// (blocked layout), so the reduction over rows is lane-local plus one LDS
-// combine across row blocks.
+// Lanes own 2 columns x 32 rows of the INT8 boundary (blocked layout), so
+// S0^T x costs one fused multiply-add per element for each of the two read
+// vectors and the reduction over rows is lane-local plus one LDS combine.
+// The records held are staged in LDS with 16-byte loads issued together
+// with the boundary load; record dot products run one lane per record over
+// the wave's own rows; the rebuild at a flush reads the records from LDS.
 #include "tile_common.h"
 
 using namespace sqk;
 
 namespace {
 
-constexpr int kMaxP = 32;
-
-template <int DK, int DV>
+template <int DK, int DV, int PM>
 struct SmemWin {
-  float x1[DK], qv[DK], ktn[DK];   // alpha_i k_i, q_i, beta_i k_i (float32)
-  float cx1[DK], cq[DK];           // C_a x1_a, C_a q_a
-  float rowf[DK];                  // per-row factor of the rebuild / 1 / C_a
-  float kr[kMaxP][DK];             // Gamma_{j+1:L} kt_j for the rebuild
-  float al[kMaxP];                 // record decays
-  float g1[kMaxP + 1], g2[kMaxP + 1];
-  float dots[2 * kMaxP];
+  float x1[DK], qv[DK], ktn[DK];  // alpha_i k_i, q_i, beta_i k_i (float32)
+  float cx1[DK], cq[DK];          // C_a x1_a, C_a q_a
+  float rowf[DK];                 // rebuild row factor, then 1 / C_a
+  float csum[DK / 32][2];         // per row block: sum_a C_a x1_a, sum_a C_a q_a
+  float al[PM];                   // record decays
+  float g1[PM + 1], g2[PM + 1];   // suffix products of the decays
+  float2 dots[DK / 32][PM];       // per row block: kt_j . x1, kt_j . q
   float unew[DV];
   float2 colA[DK / 32][DV / 2];
-  float rowt[DK / 32][32][DV / 2 + 1];
+  float2 colB[DK / 32][DV / 2];
+  union {
+    struct {
+      float K[PM][DK];
+      float U[PM][DV];
+    } rec;                                   // records held, staged from the head
+    float rowt[DK / 32][16][DV / 2 + 1];     // re-encode row transpose (after the rebuild)
+  } u;
 };
 
 struct WinPtrs {
@@ -58,44 +65,59 @@ __device__ __forceinline__ WinPtrs win_ptrs(unsigned char* base, int zoff, int D
   return w;
 }
 
-// Wave-wide sum of a float (64 lanes).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// x holds S (fp32) in the lane layout; re-encode it into the head and reset
-// the window.  All threads of the workgroup call this.
-template <int DK, int DV>
+// Copy the first n records (K rows, then U rows) of the head into LDS.
+template <int DK, int DV, int PM>
+__device__ __forceinline__ void stage_records(const WinPtrs& wp, int n, SmemWin<DK, DV, PM>& sm) {
+  constexpr int NT = (DK / 32) * (DV / 2);
+  const int t = threadIdx.x;
+  const int nk = n * DK / 4, nu = n * DV / 4;
+  for (int i = t; i < nk; i += NT)
+    reinterpret_cast<float4*>(&sm.u.rec.K[0][0])[i] = reinterpret_cast<const float4*>(wp.K)[i];
+  for (int i = t; i < nu; i += NT)
+    reinterpret_cast<float4*>(&sm.u.rec.U[0][0])[i] = reinterpret_cast<const float4*>(wp.U)[i];
+}
+
+// x holds S (fp32, lane layout); re-encode it into the head and reset the
+// window.  All threads call this; it begins with a barrier, after which the
+// record buffer may be reused.
+template <int DK, int DV, int PM>
 __device__ __forceinline__ void encode_boundary(float (&x)[64], const WinPtrs& wp, float c_floor,
-                                                SmemWin<DK, DV>& sm, int P, bool clear_records) {
+                                                SmemWin<DK, DV, PM>& sm, int P, bool clear_records) {
   using G = Geo<DK, DV>;
   constexpr int NP = G::NP, NRB = G::NRB, NT = G::NT;
-  const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p;
+  const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p, r0 = 32 * rb;
   __syncthreads();
+  // C_a = max(sqrt(mean_j |S_aj|), floor): row sums through a per-wave transpose
 #pragma unroll
-  for (int m = 0; m < 32; ++m) sm.rowt[rb][m][p] = fabsf(x[2 * m]) + fabsf(x[2 * m + 1]);
-  __syncthreads();
-  {
-    constexpr int LPR = NP / 32;
-    const int m = p & 31, part = p >> 5;
+  for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+      sm.u.rowt[rb][m][p] = fabsf(x[2 * (16 * hf + m)]) + fabsf(x[2 * (16 * hf + m) + 1]);
+    wave_sync();
+    const int mm = p & 15, part = p >> 4;
     float s = 0.f;
-#pragma unroll 8
-    for (int pp = 0; pp < 32; ++pp) s += sm.rowt[rb][m][part * 32 + pp];
-    if constexpr (LPR == 2) s += __shfl_xor(s, 32);
+#pragma unroll
+    for (int pp = 0; pp < 16; ++pp) s += sm.u.rowt[rb][mm][part * 16 + pp];
+#pragma unroll
+    for (int o = 16; o < NP; o <<= 1) s += __shfl_xor(s, o);
     if (part == 0) {
-      const int a = 32 * rb + m;
+      const int a = r0 + 16 * hf + mm;
       const float ca = fmaxf(sqrtf(s / (float)DV), c_floor);
       wp.C[a] = ca;
       sm.rowf[a] = 1.0f / ca;
     }
+    wave_sync();
   }
-  __syncthreads();
   float m0 = 0.f, m1 = 0.f;
 #pragma unroll
   for (int m = 0; m < 32; ++m) {
-    const float ic = sm.rowf[32 * rb + m];
+    const float ic = sm.rowf[r0 + m];
     x[2 * m] *= ic;
     x[2 * m + 1] *= ic;
     m0 = fmaxf(m0, fabsf(x[2 * m]));
@@ -127,77 +149,82 @@ __device__ __forceinline__ void encode_boundary(float (&x)[64], const WinPtrs& w
   }
 }
 
-// Rebuild the dense state of L records into x (lane layout).  Records 0..L-2
-// come from the head; record L-1 comes from LDS when `last_in_lds`.
-template <int DK, int DV>
-__device__ __forceinline__ void rebuild(float (&x)[64], const WinPtrs& wp, int L, bool last_in_lds,
-                                        SmemWin<DK, DV>& sm) {
+// Rebuild the dense state of L records (staged in LDS; record L-1 replaced by
+// the current token's when `last_new`) into x, which holds Z + 128 on entry.
+template <int DK, int DV, int PM>
+__device__ __forceinline__ void rebuild(float (&x)[64], const WinPtrs& wp, int L, bool last_new,
+                                        SmemWin<DK, DV, PM>& sm) {
   using G = Geo<DK, DV>;
   constexpr int NP = G::NP, NT = G::NT;
-  const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p;
-  // suffix products: factor of record j is prod_{m=j+1}^{L-1} al[m]
+  const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p, r0 = 32 * rb;
+  // factor of record j: prod_{m=j+1}^{L-1} al[m]; Gamma over all L records
   if (t == 0) {
     float g = 1.f;
     for (int j = L - 1; j >= 0; --j) {
       sm.g1[j] = g;
       g *= sm.al[j];
     }
-    sm.g1[kMaxP] = g;  // Gamma over all L records
+    sm.g1[PM] = g;
   }
   __syncthreads();
   for (int i = t; i < L * DK; i += NT) {
     const int j = i / DK, a = i - j * DK;
-    const float kt = (last_in_lds && j == L - 1) ? sm.ktn[a] : wp.K[j * DK + a];
-    sm.kr[j][a] = sm.g1[j] * kt;
+    const float kt = (last_new && j == L - 1) ? sm.ktn[a] : sm.u.rec.K[j][a];
+    sm.u.rec.K[j][a] = sm.g1[j] * kt;
   }
-  if (t < DK) sm.rowf[t] = sm.g1[kMaxP] * wp.C[t] * (1.0f / 127.0f);
+  if (last_new)
+    for (int i = t; i < DV; i += NT) sm.u.rec.U[L - 1][i] = sm.unew[i];
+  if (t < DK) sm.rowf[t] = sm.g1[PM] * wp.C[t] * (1.0f / 127.0f);
   __syncthreads();
   const float2 bb = *reinterpret_cast<const float2*>(wp.B + j0);
 #pragma unroll
   for (int m = 0; m < 32; ++m) {
-    const float f = sm.rowf[32 * rb + m];
+    const float f = sm.rowf[r0 + m];
     x[2 * m] = f * bb.x * (x[2 * m] - 128.f);
     x[2 * m + 1] = f * bb.y * (x[2 * m + 1] - 128.f);
   }
   for (int j = 0; j < L; ++j) {
-    const float2 u = (last_in_lds && j == L - 1)
-                         ? make_float2(sm.unew[j0], sm.unew[j0 + 1])
-                         : *reinterpret_cast<const float2*>(wp.U + j * DV + j0);
+    const float2 u = *reinterpret_cast<const float2*>(&sm.u.rec.U[j][j0]);
 #pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      const float k = sm.kr[j][32 * rb + m];
-      x[2 * m] = fmaf(k, u.x, x[2 * m]);
-      x[2 * m + 1] = fmaf(k, u.y, x[2 * m + 1]);
+    for (int m = 0; m < 32; m += 4) {
+      const float4 k4 = *reinterpret_cast<const float4*>(&sm.u.rec.K[j][r0 + m]);
+      const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[2 * (m + q)] = fmaf(kv[q], u.x, x[2 * (m + q)]);
+        x[2 * (m + q) + 1] = fmaf(kv[q], u.y, x[2 * (m + q) + 1]);
+      }
     }
   }
 }
 
-template <int DK, int DV>
-__global__ __launch_bounds__((DK / 32) * (DV / 2)) void window_tile_kernel(TileArgs a) {
+template <int DK, int DV, int PM, int OP>
+__global__ __launch_bounds__((DK / 32) * (DV / 2))
+__attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
   using G = Geo<DK, DV>;
-  constexpr int NP = G::NP, NRB = G::NRB, NT = G::NT, NW = NT / 64;
-  __shared__ SmemWin<DK, DV> sm;
+  constexpr int NP = G::NP, NRB = G::NRB;
+  __shared__ SmemWin<DK, DV, PM> sm;
   const int tile = blockIdx.x;
-  const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p;
+  const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p, r0 = 32 * rb;
   int h = 0;
   unsigned char* base = nullptr;
   if (!resolve_tile(a, tile, h, base)) {
-    if (a.op == OP_DECODE && t < DV) a.y[(long long)tile * DV + t] = __builtin_nanf("");
+    if (OP == OP_DECODE && t < DV) a.y[(long long)tile * DV + t] = __builtin_nanf("");
     return;
   }
   const int P = a.P.p;
   const WinPtrs wp = win_ptrs(base, a.P.r_off[h], DK, DV, P);
-  const int op = a.op;
+  constexpr int op = OP;
   float x[64];
-  if (op == OP_PACK) {
+  if constexpr (op == OP_PACK) {
     const float* X = a.X + (long long)tile * DK * DV;
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
-      const float2 v2 = *reinterpret_cast<const float2*>(X + (32 * rb + m) * DV + j0);
+      const float2 v2 = *reinterpret_cast<const float2*>(X + (r0 + m) * DV + j0);
       x[2 * m] = v2.x;
       x[2 * m + 1] = v2.y;
     }
-    encode_boundary<DK, DV>(x, wp, a.P.c_floor, sm, P, true);
+    encode_boundary<DK, DV, PM>(x, wp, a.P.c_floor, sm, P, true);
     return;
   }
   // records held; a value outside [0, p) is not a state this library writes,
@@ -206,89 +233,95 @@ __global__ __launch_bounds__((DK / 32) * (DV / 2)) void window_tile_kernel(TileA
   {
     uint32_t wd[16];
     load_chunk<8, NP>(wp.Z, rb, p, wd);
-    unpack_codes<8>(wd, x);  // Z + 128
+    stage_records<DK, DV, PM>(wp, ell, sm);
+    unpack_offset<8>(wd, x);  // Z + 128
   }
-  if (op == OP_UNPACK || op == OP_FLUSH) {
+  if (t < ell) sm.al[t] = wp.alpha[t];
+  if constexpr (op == OP_UNPACK || op == OP_FLUSH) {
     if (op == OP_FLUSH && ell == 0) return;
-    if (t < ell) sm.al[t] = wp.alpha[t];
     __syncthreads();
-    rebuild<DK, DV>(x, wp, ell, false, sm);
-    if (op == OP_FLUSH) {
-      encode_boundary<DK, DV>(x, wp, a.P.c_floor, sm, P, false);
+    rebuild<DK, DV, PM>(x, wp, ell, false, sm);
+    if constexpr (op == OP_FLUSH) {
+      encode_boundary<DK, DV, PM>(x, wp, a.P.c_floor, sm, P, false);
       return;
     }
     float* S = a.S_out + (long long)tile * DK * DV;
 #pragma unroll
     for (int m = 0; m < 32; ++m)
-      *reinterpret_cast<float2*>(S + (32 * rb + m) * DV + j0) = make_float2(x[2 * m], x[2 * m + 1]);
+      *reinterpret_cast<float2*>(S + (r0 + m) * DV + j0) = make_float2(x[2 * m], x[2 * m + 1]);
     return;
   }
   // ---- decode token i = ell + 1 (record index ell, 0-based)
   const long long tk = (long long)tile * DK, tv = (long long)tile * DV;
   const float alpha = a.gate[tile], beta = a.beta[tile];
-  if (t < ell) sm.al[t] = wp.alpha[t];
   if (t == 0) sm.al[ell] = alpha;
-  if (t < DK) {
-    const float kk = a.k[tk + t], qq = a.q[tk + t], ca = wp.C[t];
+  if (p < 32) {  // per-row constants of this wave's rows
+    const int r = r0 + p;
+    const float kk = a.k[tk + r], qq = a.q[tk + r], ca = wp.C[r];
     const float x1 = alpha * kk, kn = beta * kk;
-    sm.x1[t] = x1;
-    sm.qv[t] = qq;
-    sm.ktn[t] = kn;
-    sm.cx1[t] = ca * x1;
-    sm.cq[t] = ca * qq;
-    wp.K[ell * DK + t] = kn;  // the new record's key (record slot ell is free)
+    sm.x1[r] = x1;
+    sm.qv[r] = qq;
+    sm.ktn[r] = kn;
+    float c1 = ca * x1, c2 = ca * qq;
+    sm.cx1[r] = c1;
+    sm.cq[r] = c2;
+    wp.K[ell * DK + r] = kn;  // the new record's key (record slot ell is free)
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      c1 += __shfl_xor(c1, o);
+      c2 += __shfl_xor(c2, o);
+    }
+    if (p == 0) {
+      sm.csum[rb][0] = c1;
+      sm.csum[rb][1] = c2;
+    }
   }
   __syncthreads();
   if (t == 0) {
-    // g1[j] = prod_{m=j+1}^{ell-1} al[m] (for u_i), g2[j] = prod_{m=j+1}^{ell} al[m] (for o_i);
-    // index kMaxP holds the products over all records (Gamma_{1:i-1}, Gamma_{1:i})
+    // g1[j] = prod_{m=j+1}^{ell-1} al[m] (for u_i), g2[j] = prod_{m=j+1}^{ell} al[m]
+    // (for o_i); index PM holds the products over all records
     float g = 1.f;
     for (int j = ell - 1; j >= 0; --j) {
       sm.g1[j] = g;
       g *= sm.al[j];
     }
-    sm.g1[kMaxP] = g;
+    sm.g1[PM] = g;
     g = 1.f;
     for (int j = ell; j >= 0; --j) {
       sm.g2[j] = g;
       g *= sm.al[j];
     }
-    sm.g2[kMaxP] = g;
+    sm.g2[PM] = g;
   }
-  // dot products kt_j . x1 (j < ell) and kt_j . q (j <= ell), one task per wave
-  {
-    const int w = t >> 6, lane = t & 63;
-    for (int task = w; task < 2 * ell + 2; task += NW) {
-      const int j = task >> 1;
-      const float* xv = (task & 1) ? sm.qv : sm.x1;
-      float s = 0.f;
-      for (int r = lane; r < DK; r += 64) {
-        const float kt = j == ell ? sm.ktn[r] : wp.K[j * DK + r];
-        s = fmaf(kt, xv[r], s);
-      }
-      s = wave_sum(s);
-      if (lane == 0) sm.dots[task] = s;
+  // record dot products over this wave's rows: lane j handles record j
+  if (p <= ell && p < PM) {
+    float d1 = 0.f, d2 = 0.f;
+#pragma unroll 8
+    for (int m = 0; m < 32; ++m) {
+      const float kt = p == ell ? sm.ktn[r0 + m] : sm.u.rec.K[p][r0 + m];
+      d1 = fmaf(kt, sm.x1[r0 + m], d1);
+      d2 = fmaf(kt, sm.qv[r0 + m], d2);
+    }
+    sm.dots[rb][p] = make_float2(d1, d2);
+  }
+  // boundary readouts: sum_a Z_aj (C_a x_a) = sum_a (u_aj - 128) C_a x_a
+  float s10 = 0.f, s11 = 0.f, s20 = 0.f, s21 = 0.f;
+#pragma unroll
+  for (int m = 0; m < 32; m += 4) {
+    const float4 f1 = *reinterpret_cast<const float4*>(&sm.cx1[r0 + m]);
+    const float4 f2 = *reinterpret_cast<const float4*>(&sm.cq[r0 + m]);
+    const float v1[4] = {f1.x, f1.y, f1.z, f1.w}, v2[4] = {f2.x, f2.y, f2.z, f2.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s10 = fmaf(v1[q], x[2 * (m + q)], s10);
+      s11 = fmaf(v1[q], x[2 * (m + q) + 1], s11);
+      s20 = fmaf(v2[q], x[2 * (m + q)], s20);
+      s21 = fmaf(v2[q], x[2 * (m + q) + 1], s21);
     }
   }
-  // boundary readouts: sum_a Z_aj (C_a x_a), for x = x1 and x = q
-  float s10 = 0.f, s11 = 0.f, s20 = 0.f, s21 = 0.f, c1s = 0.f, c2s = 0.f;
-#pragma unroll
-  for (int m = 0; m < 32; ++m) {
-    const float f1 = sm.cx1[32 * rb + m], f2 = sm.cq[32 * rb + m];
-    s10 = fmaf(f1, x[2 * m], s10);
-    s11 = fmaf(f1, x[2 * m + 1], s11);
-    s20 = fmaf(f2, x[2 * m], s20);
-    s21 = fmaf(f2, x[2 * m + 1], s21);
-    c1s += f1;
-    c2s += f2;
-  }
-  s10 = fmaf(-128.f, c1s, s10);
-  s11 = fmaf(-128.f, c1s, s11);
-  s20 = fmaf(-128.f, c2s, s20);
-  s21 = fmaf(-128.f, c2s, s21);
-  // two column vectors combine through LDS: x1-part in colA, q-part in rowt scratch
-  sm.colA[rb][p] = make_float2(s10, s11);
-  reinterpret_cast<float2*>(&sm.rowt[0][0][0])[rb * NP + p] = make_float2(s20, s21);
+  const float o1 = -128.f * sm.csum[rb][0], o2 = -128.f * sm.csum[rb][1];
+  sm.colA[rb][p] = make_float2(s10 + o1, s11 + o1);
+  sm.colB[rb][p] = make_float2(s20 + o2, s21 + o2);
   __syncthreads();
   if (rb == 0) {
     float r10 = 0.f, r11 = 0.f, r20 = 0.f, r21 = 0.f;
@@ -296,29 +329,36 @@ __global__ __launch_bounds__((DK / 32) * (DV / 2)) void window_tile_kernel(TileA
     for (int r = 0; r < NRB; ++r) {
       r10 += sm.colA[r][p].x;
       r11 += sm.colA[r][p].y;
-      const float2 q2 = reinterpret_cast<const float2*>(&sm.rowt[0][0][0])[r * NP + p];
-      r20 += q2.x;
-      r21 += q2.y;
+      r20 += sm.colB[r][p].x;
+      r21 += sm.colB[r][p].y;
     }
     const float2 bb = *reinterpret_cast<const float2*>(wp.B + j0);
     const float f0 = bb.x * (1.0f / 127.0f), f1 = bb.y * (1.0f / 127.0f);
-    float pv0 = sm.g1[kMaxP] * f0 * r10, pv1 = sm.g1[kMaxP] * f1 * r11;
-    float o0 = sm.g2[kMaxP] * f0 * r20, o1 = sm.g2[kMaxP] * f1 * r21;
+    float pv0 = sm.g1[PM] * f0 * r10, pv1 = sm.g1[PM] * f1 * r11;
+    float w0 = sm.g2[PM] * f0 * r20, w1 = sm.g2[PM] * f1 * r21;
     for (int j = 0; j < ell; ++j) {
-      const float2 u = *reinterpret_cast<const float2*>(wp.U + j * DV + j0);
-      const float d1 = sm.g1[j] * sm.dots[2 * j], d2 = sm.g2[j] * sm.dots[2 * j + 1];
-      pv0 = fmaf(u.x, d1, pv0);
-      pv1 = fmaf(u.y, d1, pv1);
-      o0 = fmaf(u.x, d2, o0);
-      o1 = fmaf(u.y, d2, o1);
+      float d1 = 0.f, d2 = 0.f;
+#pragma unroll
+      for (int r = 0; r < NRB; ++r) {
+        d1 += sm.dots[r][j].x;
+        d2 += sm.dots[r][j].y;
+      }
+      const float2 u = *reinterpret_cast<const float2*>(&sm.u.rec.U[j][j0]);
+      const float e1 = sm.g1[j] * d1, e2 = sm.g2[j] * d2;
+      pv0 = fmaf(u.x, e1, pv0);
+      pv1 = fmaf(u.y, e1, pv1);
+      w0 = fmaf(u.x, e2, w0);
+      w1 = fmaf(u.y, e2, w1);
     }
+    float dn = 0.f;  // kt_i . q
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) dn += sm.dots[r][ell].y;
     const float2 vv = *reinterpret_cast<const float2*>(a.v + tv + j0);
     const float u0 = vv.x - pv0, u1 = vv.y - pv1;
-    const float dn = sm.dots[2 * ell + 1];  // kt_i . q
-    o0 = fmaf(u0, dn, o0);
-    o1 = fmaf(u1, dn, o1);
+    w0 = fmaf(u0, dn, w0);
+    w1 = fmaf(u1, dn, w1);
     *reinterpret_cast<float2*>(wp.U + ell * DV + j0) = make_float2(u0, u1);
-    *reinterpret_cast<float2*>(a.y + tv + j0) = make_float2(o0, o1);
+    *reinterpret_cast<float2*>(a.y + tv + j0) = make_float2(w0, w1);
     sm.unew[j0] = u0;
     sm.unew[j0 + 1] = u1;
   }
@@ -329,22 +369,34 @@ __global__ __launch_bounds__((DK / 32) * (DV / 2)) void window_tile_kernel(TileA
     }
     return;
   }
-  // the window is full: rebuild S_p and re-encode the boundary
+  // the window is full: rebuild S_p from the staged records and re-encode
   __syncthreads();
-  rebuild<DK, DV>(x, wp, P, true, sm);
-  encode_boundary<DK, DV>(x, wp, a.P.c_floor, sm, P, false);
+  rebuild<DK, DV, PM>(x, wp, P, true, sm);
+  encode_boundary<DK, DV, PM>(x, wp, a.P.c_floor, sm, P, false);
+}
+
+template <int DK, int DV, int PM>
+hipError_t launch_pm(const TileArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_tiles), block((DK / 32) * (DV / 2));
+  switch (a.op) {
+    case OP_DECODE: hipLaunchKernelGGL((window_tile_kernel<DK, DV, PM, OP_DECODE>), grid, block, 0, s, a); break;
+    case OP_PACK: hipLaunchKernelGGL((window_tile_kernel<DK, DV, PM, OP_PACK>), grid, block, 0, s, a); break;
+    case OP_UNPACK: hipLaunchKernelGGL((window_tile_kernel<DK, DV, PM, OP_UNPACK>), grid, block, 0, s, a); break;
+    case OP_FLUSH: hipLaunchKernelGGL((window_tile_kernel<DK, DV, PM, OP_FLUSH>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <int DK, int DV>
 hipError_t launch(const TileArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((window_tile_kernel<DK, DV>), dim3(a.n_tiles), dim3((DK / 32) * (DV / 2)), 0, s, a);
-  return hipGetLastError();
+  return a.P.p <= 16 ? launch_pm<DK, DV, 16>(a, s) : launch_pm<DK, DV, 32>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_tile_window(const TileArgs& a, hipStream_t s) {
-  if (a.P.p > kMaxP || a.P.p < 1) return hipErrorInvalidValue;
+  if (a.P.p > 32 || a.P.p < 1) return hipErrorInvalidValue;
   const int dk = a.P.dk, dv = a.P.dv;
   if (dk == 128 && dv == 128) return launch<128, 128>(a, s);
   if (dk == 64 && dv == 64) return launch<64, 64>(a, s);
