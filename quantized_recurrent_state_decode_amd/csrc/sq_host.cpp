@@ -90,6 +90,7 @@ void finish_plan(sq_plan* P) {
       }
       P->r_off[h] = (int)codes;
       P->c_off[h] = (int)codes + 2 * dk;
+      P->max_code_bytes = std::max<int>(P->max_code_bytes, (int)codes);
       used = codes + 2LL * dk + 2LL * dv;
       analytic += used;
     }
@@ -143,6 +144,7 @@ DevPlan dev_view(const sq_plan* P, const void* dev) {
   d.c_floor = P->c_floor;
   d.slot_bytes = P->slot_bytes;
   d.max_head_bytes = P->max_head_bytes;
+  d.max_code_bytes = P->max_code_bytes;
   d.head_off = reinterpret_cast<const long long*>(b + P->o_head_off);
   d.head_bits = reinterpret_cast<const int*>(b + P->o_head_bits);
   d.w = reinterpret_cast<const float*>(b + P->o_w);

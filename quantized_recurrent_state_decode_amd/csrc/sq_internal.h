@@ -15,6 +15,7 @@ struct DevPlan {
   float c_floor;
   long long slot_bytes;
   int max_head_bytes;
+  int max_code_bytes;         // KDA: largest code region of a head
   const long long* head_off;  // [H]
   const int* head_bits;       // [H] GDN/uniform width (16 = FP16 pivot head)
   const float* w;             // [H*dk] impact factors (STEP)
@@ -32,7 +33,7 @@ struct sq_plan {
   float c_floor = 1e-6f;
   int n_units = 0;
   long long slot_bytes = 0, payload_bytes = 0, analytic_bytes = 0;
-  int max_head_bytes = 0;
+  int max_head_bytes = 0, max_code_bytes = 0;
   std::vector<long long> head_off;
   std::vector<int> head_bits, unit_bits, row_key, row_bits, row_off, r_off, c_off;
   std::vector<float> w, winv;

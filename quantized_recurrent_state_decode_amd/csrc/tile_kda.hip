@@ -1,17 +1,24 @@
 // Fused quantized decode step for STEP KDA heads: channel-wise retention
 // D = diag(d), bit width chosen per key row (STEPQuant Sec. 4, unit = key
 // row for KDA), FP16 pivot rows, one column-scale vector c shared by all
-// integer rows of the head (App. D: "codebook normalization fixed by
-// precision", so rows of different widths share c).
+// integer rows of the head (App. D: the codebook normalisation is fixed by
+// precision, so rows of different widths share c).
 //
-// Storage rows are ordered by (width, key row) and kept row-major, so a
-// head is a run of variable-length rows.  The workgroup stages the packed
-// head in LDS with coalesced 16-byte copies, every lane extracts its two
-// columns of its 32 storage rows (the row width is uniform across the wave
-// at each row), and the new codes are assembled in LDS (bit-field OR) and
-// copied back with 16-byte stores.  The arithmetic is the GDN kernel's with
-// per-row q_b and per-row retention, in storage-row order; per-row inputs
-// (d, k, q, w) are gathered through the storage permutation.
+// Storage rows are ordered by (width, key row) and kept row-major, so a head
+// is a run of variable-length rows.  The workgroup stages the packed head in
+// LDS with coalesced 16-byte copies; lane (rb, p) extracts columns 2p, 2p+1
+// of its 32 storage rows (the width of a row is uniform across the wave),
+// writes the new codes back into the same LDS bytes and the head is copied
+// out with 16-byte stores.  Per-row inputs (d, k, q, w) are gathered through
+// the storage permutation.  Per element, with c' = c_j (integer rows) or 1
+// (FP16 rows) and rho_s the row's retained dequantisation factor:
+//   x = c' * value;   delta_j = sum_s kappa_s x_sj          (kappa = k rho)
+//   Xt = x + gamma_s e_j  (X = rho_s Xt, gamma = beta k / rho)
+//   y_j = sum_s theta_s Xt_sj                              (theta = q rho)
+// then the GDN kernel's row scales, column init, codes by magic rounding
+// (per-row q_b) and fixed-code column refit over the integer rows.
+#include <algorithm>
+
 #include "tile_common.h"
 
 using namespace sqk;
@@ -20,142 +27,173 @@ namespace {
 
 template <int DK, int DV>
 struct SmemKda {
-  float rowc[5][DK];
-  float rho[DK];
+  float rowc[7][DK];  // 0 kappa, 1 gamma, 2 theta, 3 rho, 4 pi or rho (FP16 rows),
+                      // 5 lambda_N = w^2 r^2 / q_b, 6 lambda_D = w^2 r^2 / q_b^2
+  float qb[DK];       // q_b of storage row s (0 for FP16 rows)
   int bits[DK];
   int off[DK];
   float2 colA[DK / 32][DV / 2];
   float2 colB[DK / 32][DV / 2];
+  float2 colM[DK / 32][DV / 2];
   float4 colC[DK / 32][DV / 2];
-  union {
-    uint32_t codes[DK * DV / 2];             // packed head (at most all-FP16 rows)
-    float rowt[DK / 32][32][DV / 2 + 1];     // row partials, transposed
-  } u;
 };
 
+// The packed head (at most max_code_bytes) and, while no codes are live,
+// the per-wave row transpose, share the dynamic LDS buffer.
+extern __shared__ uint4 kda_dyn[];
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Two b-bit fields (columns 2p, 2p+1) of a row stored at byte `off`.
-__device__ __forceinline__ void read_pair(const uint32_t* codes, int off, int b, int p,
+__device__ __forceinline__ void read_pair(const unsigned char* codes, int off, int b, int p,
                                           float& z0, float& z1) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(codes);
   if (b == 16) {
-    const uint32_t w = codes[(off >> 2) + p];
-    z0 = half_from_bits(w);
-    z1 = half_from_bits(w >> 16);
+    const uint32_t v = w[(off >> 2) + p];
+    z0 = half_from_bits(v);
+    z1 = half_from_bits(v >> 16);
     return;
   }
-  const int bit = 2 * p * b;                  // first bit of the pair in the row
+  const int bit = 2 * p * b;  // first bit of the pair in the row
   const int wi = (off >> 2) + (bit >> 5), sh = bit & 31;
-  uint64_t v = codes[wi];
-  if (sh + 2 * b > 32) v |= (uint64_t)codes[wi + 1] << 32;
+  uint64_t v = w[wi];
+  if (sh + 2 * b > 32) v |= (uint64_t)w[wi + 1] << 32;
   const uint32_t f = (uint32_t)(v >> sh);
   const int s = 32 - b;
   z0 = (float)((int32_t)(f << s) >> s);
   z1 = (float)((int32_t)((f >> b) << s) >> s);
 }
 
-__device__ __forceinline__ void write_pair(uint32_t* codes, int off, int b, int p, float u0,
-                                           float u1) {
-  if (b == 16) {
-    codes[(off >> 2) + p] = half_bits(u0) | (half_bits(u1) << 16);
-    return;
+// Write the lane's two codes (magic-rounded floats m0, m1) of a b-bit row.
+// Rows are byte-aligned; 2- and 6-bit pairs share bytes with the next lane's,
+// so even lanes write both lanes' bits.
+__device__ __forceinline__ void write_pair(unsigned char* codes, int off, int b, int p, float m0,
+                                           float m1) {
+  const uint32_t u0 = __float_as_uint(m0), u1 = __float_as_uint(m1);
+  if (b == 4) {
+    codes[off + p] = (unsigned char)((u0 & 15u) | ((u1 & 15u) << 4));
+  } else if (b == 8) {
+    *reinterpret_cast<unsigned short*>(codes + off + 2 * p) =
+        (unsigned short)((u0 & 0xffu) | ((u1 & 0xffu) << 8));
+  } else if (b == 2) {
+    const uint32_t nib = (u0 & 3u) | ((u1 & 3u) << 2);
+    const uint32_t nxt = __shfl_down(nib, 1);
+    if (!(p & 1)) codes[off + (p >> 1)] = (unsigned char)(nib | (nxt << 4));
+  } else {  // 6 bits: 12 bits per lane, 3 bytes per lane pair
+    const uint32_t f = (u0 & 63u) | ((u1 & 63u) << 6);
+    const uint32_t nxt = __shfl_down(f, 1);
+    if (!(p & 1)) {
+      const uint32_t v = f | (nxt << 12);
+      unsigned char* d = codes + off + 3 * (p >> 1);
+      d[0] = (unsigned char)v;
+      d[1] = (unsigned char)(v >> 8);
+      d[2] = (unsigned char)(v >> 16);
+    }
   }
-  const uint32_t m = (1u << b) - 1u;
-  const uint64_t f = (uint64_t)(((uint32_t)(int32_t)u0 & m) | (((uint32_t)(int32_t)u1 & m) << b));
-  const int bit = 2 * p * b;
-  const int wi = (off >> 2) + (bit >> 5), sh = bit & 31;
-  const uint64_t v = f << sh;
-  atomicOr(&codes[wi], (uint32_t)v);
-  if (sh + 2 * b > 32) atomicOr(&codes[wi + 1], (uint32_t)(v >> 32));
 }
 
-template <int DK, int DV>
-__global__ __launch_bounds__((DK / 32) * (DV / 2)) void kda_tile_kernel(TileArgs a) {
+template <int DK, int DV, int OP>
+__global__ __launch_bounds__((DK / 32) * (DV / 2))
+__attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   using G = Geo<DK, DV>;
   constexpr int NP = G::NP, NRB = G::NRB, NT = G::NT;
   __shared__ SmemKda<DK, DV> sm;
+  unsigned char* codes = reinterpret_cast<unsigned char*>(kda_dyn);
+  float(*rowt)[16][NP + 1] = reinterpret_cast<float(*)[16][NP + 1]>(kda_dyn);
   const int tile = blockIdx.x;
-  const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p;
+  const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p, r0 = 32 * rb;
   int h = 0;
   unsigned char* base = nullptr;
   if (!resolve_tile(a, tile, h, base)) {
-    if (a.op == OP_DECODE && t < DV) a.y[(long long)tile * DV + t] = __builtin_nanf("");
+    if (OP == OP_DECODE && t < DV) a.y[(long long)tile * DV + t] = __builtin_nanf("");
     return;
   }
-  const int op = a.op;
   const long long tk = (long long)tile * DK, tv = (long long)tile * DV;
   const int* rkey = a.P.row_key + h * DK;
   const int code_bytes = a.P.r_off[h];
   __half* r_ptr = reinterpret_cast<__half*>(base + a.P.r_off[h]);
   __half* c_ptr = reinterpret_cast<__half*>(base + a.P.c_off[h]);
-  if (t < DK) {
-    sm.bits[t] = a.P.row_bits[h * DK + t];
-    sm.off[t] = a.P.row_off[h * DK + t];
+  // per-storage-row metadata of this wave's rows
+  if (p < 32) {
+    const int s = r0 + p;
+    const int b = a.P.row_bits[h * DK + s];
+    sm.bits[s] = b;
+    sm.off[s] = a.P.row_off[h * DK + s];
+    sm.qb[s] = b == 16 ? 0.f : (float)((1 << (b - 1)) - 1);
   }
   float x[64];
-  float c0 = 1.f, c1 = 1.f;
-  if (op == OP_PACK) {
+  float y0 = 0.f, y1 = 0.f;
+  if constexpr (OP == OP_PACK) {
     const float* X = a.X + (long long)tile * DK * DV;
-    __syncthreads();
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
-      const int key = rkey[32 * rb + m];
+      const int key = rkey[r0 + m];
       const float2 v2 = *reinterpret_cast<const float2*>(X + key * DV + j0);
       x[2 * m] = v2.x;
       x[2 * m + 1] = v2.y;
     }
-    if (t < DK) sm.rho[t] = 1.0f;
+    if (p < 32) sm.rowc[3][r0 + p] = 1.0f;
+    __syncthreads();
   } else {
     for (int i = t * 16; i < code_bytes; i += NT * 16)
-      *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(sm.u.codes) + i) =
-          *reinterpret_cast<const uint4*>(base + i);
-    c0 = __half2float(c_ptr[j0]);
-    c1 = __half2float(c_ptr[j0 + 1]);
-    if (t < DK) {
-      const int b = a.P.row_bits[h * DK + t], key = rkey[t];
-      const bool piv = b == 16;
-      const float qb = piv ? 1.f : (float)((1 << (b - 1)) - 1);
-      const float sc = piv ? 1.f : __half2float(r_ptr[t]) / qb;
-      if (op == OP_UNPACK) {
-        sm.rho[t] = sc;
+      *reinterpret_cast<uint4*>(codes + i) = *reinterpret_cast<const uint4*>(base + i);
+    const float c0 = __half2float(c_ptr[j0]), c1 = __half2float(c_ptr[j0 + 1]);
+    if (p < 32) {
+      const int s = r0 + p, key = rkey[s];
+      const bool piv = sm.bits[s] == 16;
+      const float sc = piv ? 1.f : __half2float(r_ptr[s]) * frcp(sm.qb[s]);
+      if constexpr (OP == OP_UNPACK) {
+        sm.rowc[3][s] = sc;
       } else {
         const float d = a.gate[tk + key];
         const float kk = a.k[tk + key], qq = a.q[tk + key], bk = a.beta[tile] * kk;
         const float rho = d * sc;
+        // a vanishing retention keeps the division finite; the dropped part
+        // (rp - rho) c_j z_sj is below 2^-60 of the write term
         const float rp = fmaxf(rho, fmaxf(fabsf(bk) * 0x1p-60f, 0x1p-100f));
-        sm.rowc[0][t] = kk * rho;
-        sm.rowc[1][t] = bk / rp;
-        sm.rowc[2][t] = qq * rp;
-        sm.rho[t] = rp;
+        sm.rowc[0][s] = kk * rho;
+        sm.rowc[1][s] = bk * frcp(rp);
+        sm.rowc[2][s] = qq * rp;
+        sm.rowc[3][s] = rp;
       }
     }
-    __syncthreads();
+    __syncthreads();  // codes staged, per-row constants ready
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
-      const int s = 32 * rb + m;
-      read_pair(sm.u.codes, sm.off[s], sm.bits[s], p, x[2 * m], x[2 * m + 1]);
+      const int s = r0 + m;
+      const int b = sm.bits[s];
+      float z0, z1;
+      read_pair(codes, sm.off[s], b, p, z0, z1);
+      x[2 * m] = b == 16 ? z0 : c0 * z0;
+      x[2 * m + 1] = b == 16 ? z1 : c1 * z1;
     }
-    if (op == OP_UNPACK) {
+    if constexpr (OP == OP_UNPACK) {
       float* S = a.S_out + (long long)tile * DK * DV;
 #pragma unroll
       for (int m = 0; m < 32; ++m) {
-        const int s = 32 * rb + m;
-        const bool piv = sm.bits[s] == 16;
-        const float f0 = piv ? 1.f : sm.rho[s] * c0, f1 = piv ? 1.f : sm.rho[s] * c1;
-        *reinterpret_cast<float2*>(S + rkey[s] * DV + j0) = make_float2(f0 * x[2 * m], f1 * x[2 * m + 1]);
+        const float f = sm.bits[r0 + m] == 16 ? 1.f : sm.rowc[3][r0 + m];
+        *reinterpret_cast<float2*>(S + rkey[r0 + m] * DV + j0) = make_float2(f * x[2 * m], f * x[2 * m + 1]);
       }
       return;
     }
-    // pass 1: delta_j = sum_s kappa_s c'_sj z_sj  (c' = c_j, or 1 on pivot rows)
+    // pass 1: delta_j = sum_s kappa_s x_sj
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      const int s = 32 * rb + m;
-      const bool piv = sm.bits[s] == 16;
-      const float kap = sm.rowc[0][s];
-      a0 = fmaf(kap * (piv ? 1.f : c0), x[2 * m], a0);
-      a1 = fmaf(kap * (piv ? 1.f : c1), x[2 * m + 1], a1);
+    for (int m = 0; m < 32; m += 4) {
+      const float4 k4 = *reinterpret_cast<const float4*>(&sm.rowc[0][r0 + m]);
+      const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a0 = fmaf(kv[u], x[2 * (m + u)], a0);
+        a1 = fmaf(kv[u], x[2 * (m + u) + 1], a1);
+      }
     }
     sm.colA[rb][p] = make_float2(a0, a1);
-    __syncthreads();
+    __syncthreads();  // all rows unpacked: the code buffer may hold the transpose
     float d0 = 0.f, d1 = 0.f;
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
@@ -164,27 +202,75 @@ __global__ __launch_bounds__((DK / 32) * (DV / 2)) void kda_tile_kernel(TileArgs
     }
     const float2 vv = *reinterpret_cast<const float2*>(a.v + tv + j0);
     const float e0 = vv.x - d0, e1 = vv.y - d1;
-    float y0 = 0.f, y1 = 0.f;
+    // pass 2: Xt = x + gamma_s e_j, readout partials
 #pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      const int s = 32 * rb + m;
-      const bool piv = sm.bits[s] == 16;
-      const float gam = sm.rowc[1][s], th = sm.rowc[2][s];
-      const float v0 = fmaf(piv ? 1.f : c0, x[2 * m], gam * e0);
-      const float v1 = fmaf(piv ? 1.f : c1, x[2 * m + 1], gam * e1);
-      x[2 * m] = v0;
-      x[2 * m + 1] = v1;
-      y0 = fmaf(th, v0, y0);
-      y1 = fmaf(th, v1, y1);
+    for (int m = 0; m < 32; m += 4) {
+      const float4 g4 = *reinterpret_cast<const float4*>(&sm.rowc[1][r0 + m]);
+      const float4 t4 = *reinterpret_cast<const float4*>(&sm.rowc[2][r0 + m]);
+      const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, tv4[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float v0 = fmaf(gv[u], e0, x[2 * (m + u)]);
+        const float v1 = fmaf(gv[u], e1, x[2 * (m + u) + 1]);
+        x[2 * (m + u)] = v0;
+        x[2 * (m + u) + 1] = v1;
+        y0 = fmaf(tv4[u], v0, y0);
+        y1 = fmaf(tv4[u], v1, y1);
+      }
     }
     sm.colB[rb][p] = make_float2(y0, y1);
   }
-  __syncthreads();  // codes buffer no longer needed: rowt may overwrite it
+  // row statistics of Xt (integer rows), 16 rows at a time through a
+  // per-wave transpose in the dynamic buffer
 #pragma unroll
-  for (int m = 0; m < 32; ++m)
-    sm.u.rowt[rb][m][p] = fabsf(x[2 * m]) + fabsf(x[2 * m + 1]);
-  __syncthreads();
-  if (op == OP_DECODE && rb == 0) {
+  for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+      rowt[rb][m][p] = fabsf(x[2 * (16 * hf + m)]) + fabsf(x[2 * (16 * hf + m) + 1]);
+    wave_sync();
+    const int mm = p & 15, part = p >> 4;
+    float s = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < 16; ++pp) s += rowt[rb][mm][part * 16 + pp];
+#pragma unroll
+    for (int o = 16; o < NP; o <<= 1) s += __shfl_xor(s, o);
+    if (part == 0) {
+      const int si = r0 + 16 * hf + mm;
+      const float rp = sm.rowc[3][si];
+      if (sm.bits[si] == 16) {
+        r_ptr[si] = __float2half_rn(0.0f);
+        sm.rowc[4][si] = rp;  // FP16 rows: X = rho Xt
+        sm.rowc[5][si] = 0.f;
+        sm.rowc[6][si] = 0.f;
+      } else {
+        const int key = rkey[si];
+        const float wi = a.P.w[h * DK + key], iq = frcp(sm.qb[si]);
+        const float ri = fp16_scale(sqrtf(rp * s * (1.0f / (float)DV) * a.P.winv[h * DK + key]));
+        r_ptr[si] = __float2half_rn(ri);
+        const float ww = wi * wi * ri * ri * iq;
+        sm.rowc[4][si] = rp * frcp(ri);
+        sm.rowc[5][si] = ww;
+        sm.rowc[6][si] = ww * iq;
+      }
+    }
+    wave_sync();
+  }
+  // pass 3: P = X / r on integer rows (column absmax), X on FP16 rows
+  float mx0 = 0.f, mx1 = 0.f;
+#pragma unroll
+  for (int m = 0; m < 32; ++m) {
+    const int s = r0 + m;
+    const float f = sm.rowc[4][s];
+    x[2 * m] *= f;
+    x[2 * m + 1] *= f;
+    if (sm.bits[s] != 16) {
+      mx0 = fmaxf(mx0, fabsf(x[2 * m]));
+      mx1 = fmaxf(mx1, fabsf(x[2 * m + 1]));
+    }
+  }
+  sm.colM[rb][p] = make_float2(mx0, mx1);
+  const bool sat = __syncthreads_or(fmaxf(mx0, mx1) > kFp16Max) != 0;
+  if (OP == OP_DECODE && rb == 0) {
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
@@ -193,87 +279,44 @@ __global__ __launch_bounds__((DK / 32) * (DV / 2)) void kda_tile_kernel(TileArgs
     }
     *reinterpret_cast<float2*>(a.y + tv + j0) = make_float2(s0, s1);
   }
-  {
-    constexpr int LPR = NP / 32;
-    const int m = p & 31, part = p >> 5;
-    float s = 0.f;
-#pragma unroll 8
-    for (int pp = 0; pp < 32; ++pp) s += sm.u.rowt[rb][m][part * 32 + pp];
-    if constexpr (LPR == 2) s += __shfl_xor(s, 32);
-    if (part == 0) {
-      const int si = 32 * rb + m;
-      const int b = sm.bits[si];
-      const float rp = sm.rho[si];
-      if (b == 16) {
-        r_ptr[si] = __float2half_rn(0.0f);
-        sm.rowc[3][si] = 0.f;
-        sm.rowc[4][si] = 0.f;
-      } else {
-        const float qb = (float)((1 << (b - 1)) - 1);
-        const float wi = a.P.w[h * DK + rkey[si]];
-        const float ri = fp16_scale(sqrtf(rp * s / (float)DV / wi));
-        r_ptr[si] = __float2half_rn(ri);
-        sm.rowc[3][si] = rp / ri;
-        sm.rowc[4][si] = wi * wi * ri * ri / qb;
-      }
-    }
-  }
-  __syncthreads();
-  // pass 3: P = X / r on integer rows, column absmax; pivot rows -> X
-  float mx0 = 0.f, mx1 = 0.f;
-#pragma unroll
-  for (int m = 0; m < 32; ++m) {
-    const int s = 32 * rb + m;
-    if (sm.bits[s] == 16) {
-      x[2 * m] *= sm.rho[s];
-      x[2 * m + 1] *= sm.rho[s];
-    } else {
-      const float pi = sm.rowc[3][s];
-      x[2 * m] *= pi;
-      x[2 * m + 1] *= pi;
-      mx0 = fmaxf(mx0, fabsf(x[2 * m]));
-      mx1 = fmaxf(mx1, fabsf(x[2 * m + 1]));
-    }
-  }
-  sm.colA[rb][p] = make_float2(mx0, mx1);
-  __syncthreads();
   float m0 = 0.f, m1 = 0.f;
 #pragma unroll
   for (int r = 0; r < NRB; ++r) {
-    m0 = fmaxf(m0, sm.colA[r][p].x);
-    m1 = fmaxf(m1, sm.colA[r][p].y);
+    m0 = fmaxf(m0, sm.colM[r][p].x);
+    m1 = fmaxf(m1, sm.colM[r][p].y);
   }
   const float cz0 = fp16_scale(m0), cz1 = fp16_scale(m1);
-  const float ic0 = 1.0f / cz0, ic1 = 1.0f / cz1;
-  // the codes buffer is rebuilt from zero (bit fields are OR-ed in)
-  for (int i = t; i < DK * DV / 2; i += NT) sm.u.codes[i] = 0u;
-  __syncthreads();
+  const float ic0 = frcp(cz0), ic1 = frcp(cz1);
+  // pass 4: codes (magic rounding, per-row q_b) and the refit sums; the new
+  // codes go into the staged head in place
   float N0 = 0.f, N1 = 0.f, D0 = 0.f, D1 = 0.f;
 #pragma unroll
   for (int m = 0; m < 32; ++m) {
-    const int s = 32 * rb + m;
+    const int s = r0 + m;
     const int b = sm.bits[s];
     if (b == 16) {
-      write_pair(sm.u.codes, sm.off[s], 16, p, x[2 * m], x[2 * m + 1]);
+      *reinterpret_cast<uint32_t*>(codes + sm.off[s] + 4 * p) =
+          half_bits(x[2 * m]) | (half_bits(x[2 * m + 1]) << 16);
       continue;
     }
-    const float qb = (float)((1 << (b - 1)) - 1);
-    const float lam = sm.rowc[4][s];
+    const float qb = sm.qb[s], ln = sm.rowc[5][s], ld = sm.rowc[6][s];
     const float pv0 = x[2 * m], pv1 = x[2 * m + 1];
-    const float z0 = fminf(fmaxf(rintf(pv0 * (qb * ic0)), -qb), qb);
-    const float z1 = fminf(fmaxf(rintf(pv1 * (qb * ic1)), -qb), qb);
-    const float t0 = lam * z0, t1 = lam * z1;
-    N0 = fmaf(t0, pv0, N0);
-    N1 = fmaf(t1, pv1, N1);
-    D0 = fmaf(t0 / qb, z0, D0);
-    D1 = fmaf(t1 / qb, z1, D1);
-    write_pair(sm.u.codes, sm.off[s], b, p, z0, z1);
+    float mg0 = fmaf(pv0, qb * ic0, kMagic), mg1 = fmaf(pv1, qb * ic1, kMagic);
+    if (sat) {  // a column scale saturated at the FP16 maximum
+      mg0 = __builtin_amdgcn_fmed3f(mg0, kMagic - qb, kMagic + qb);
+      mg1 = __builtin_amdgcn_fmed3f(mg1, kMagic - qb, kMagic + qb);
+    }
+    const float z0 = mg0 - kMagic, z1 = mg1 - kMagic;
+    N0 = fmaf(ln * z0, pv0, N0);
+    N1 = fmaf(ln * z1, pv1, N1);
+    D0 = fmaf(ld * z0, z0, D0);
+    D1 = fmaf(ld * z1, z1, D1);
+    write_pair(codes, sm.off[s], b, p, mg0, mg1);
   }
   sm.colC[rb][p] = make_float4(N0, N1, D0, D1);
   __syncthreads();
   for (int i = t * 16; i < code_bytes; i += NT * 16)
-    *reinterpret_cast<uint4*>(base + i) =
-        *reinterpret_cast<const uint4*>(reinterpret_cast<unsigned char*>(sm.u.codes) + i);
+    *reinterpret_cast<uint4*>(base + i) = *reinterpret_cast<const uint4*>(codes + i);
   if (rb == 0) {
     float n0 = 0.f, n1 = 0.f, dd0 = 0.f, dd1 = 0.f;
 #pragma unroll
@@ -284,14 +327,23 @@ __global__ __launch_bounds__((DK / 32) * (DV / 2)) void kda_tile_kernel(TileArgs
       dd0 += c.z;
       dd1 += c.w;
     }
-    c_ptr[j0] = __float2half_rn(dd0 > 0.f ? fp16_scale(n0 / dd0) : cz0);
-    c_ptr[j0 + 1] = __float2half_rn(dd1 > 0.f ? fp16_scale(n1 / dd1) : cz1);
+    c_ptr[j0] = __float2half_rn(dd0 > 0.f ? fp16_scale(n0 * frcp(dd0)) : cz0);
+    c_ptr[j0 + 1] = __float2half_rn(dd1 > 0.f ? fp16_scale(n1 * frcp(dd1)) : cz1);
   }
 }
 
 template <int DK, int DV>
 hipError_t launch(const TileArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((kda_tile_kernel<DK, DV>), dim3(a.n_tiles), dim3((DK / 32) * (DV / 2)), 0, s, a);
+  constexpr int NP = DV / 2, NRB = DK / 32;
+  const size_t transpose = (size_t)NRB * 16 * (NP + 1) * sizeof(float);
+  const size_t dyn = ((std::max<size_t>((size_t)a.P.max_code_bytes, transpose) + 15) / 16) * 16;
+  const dim3 grid(a.n_tiles), block(NRB * NP);
+  switch (a.op) {
+    case OP_DECODE: hipLaunchKernelGGL((kda_tile_kernel<DK, DV, OP_DECODE>), grid, block, dyn, s, a); break;
+    case OP_PACK: hipLaunchKernelGGL((kda_tile_kernel<DK, DV, OP_PACK>), grid, block, dyn, s, a); break;
+    case OP_UNPACK: hipLaunchKernelGGL((kda_tile_kernel<DK, DV, OP_UNPACK>), grid, block, dyn, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
