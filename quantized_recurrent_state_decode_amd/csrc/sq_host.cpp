@@ -183,23 +183,53 @@ sq_status validate_slots(const int32_t* slots, int B, long long n_slots, hipStre
   return SQ_OK;
 }
 
+// Tiles of a class above which it gets a launch of its own (16 rounds of
+// 1024 resident 256-lane workgroups).
+constexpr long long kSoloTiles = 16384;
+
+// Decode arguments covering classes order[lo .. hi) of P.
+TileArgs class_args(const sq_plan* P, const TileArgs& a, const int* order, int lo, int hi) {
+  TileArgs b = a;
+  b.n_cls = hi - lo;
+  int end = 0;
+  for (int i = 0; i < 5; ++i) {
+    if (i < b.n_cls) {
+      const int c = order[lo + i];
+      b.cls_first[i] = P->cls_start[c];
+      b.cls_n[i] = P->cls_count[c];
+      b.cls_bits[i] = (const int[]){2, 4, 6, 8, 16}[c];
+      end += a.B * P->cls_count[c];
+    } else {
+      b.cls_first[i] = 0;
+      b.cls_n[i] = 1;
+      b.cls_bits[i] = 0;
+    }
+    b.cls_end[i] = end;
+  }
+  b.n_tiles = end;
+  return b;
+}
+
 hipError_t dispatch(const sq_plan* P, const TileArgs& a, hipStream_t st) {
   if (P->mode == SQ_MODE_WINDOW) return launch_tile_window(a, st);
   if (P->mode == SQ_MODE_STEP && P->kind == SQ_KIND_KDA) return launch_tile_kda(a, st);
   if (a.op != OP_DECODE || a.head_ids) return launch_tile_gdn(a, st);
-  // decode: one launch per code width, largest class first
+  // decode by width class, largest first.  A class that fills the chip many
+  // times over runs alone in its width-specialised kernel; the other classes
+  // share one merged launch (one grid, so small classes do not each pay a
+  // launch's latency).
   int order[5] = {0, 1, 2, 3, 4};
-  std::sort(order, order + 5, [&](int x, int y) { return P->cls_count[x] > P->cls_count[y]; });
-  for (int c : order) {
-    if (!P->cls_count[c]) continue;
-    TileArgs b = a;
-    b.cls_first = P->cls_start[c];
-    b.cls_n = P->cls_count[c];
-    b.n_tiles = a.B * b.cls_n;
-    hipError_t e = launch_decode_gdn(b, (const int[]){2, 4, 6, 8, 16}[c], st);
-    if (e != hipSuccess) return e;
+  std::stable_sort(order, order + 5, [&](int x, int y) { return P->cls_count[x] > P->cls_count[y]; });
+  int n = 0;
+  while (n < 5 && P->cls_count[order[n]]) ++n;
+  int first = 0;
+  if (n == 1 || (long long)a.B * P->cls_count[order[0]] >= kSoloTiles) {
+    TileArgs b = class_args(P, a, order, 0, 1);
+    hipError_t e = launch_decode_gdn(b, true, st);
+    if (e != hipSuccess || n == 1) return e;
+    first = 1;
   }
-  return hipSuccess;
+  return launch_decode_gdn(class_args(P, a, order, first, n), false, st);
 }
 
 TileArgs base_args(const sq_plan* P, const void* dev_plan, int op) {

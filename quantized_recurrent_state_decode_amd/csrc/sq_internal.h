@@ -65,12 +65,18 @@ struct TileArgs {
   unsigned char* out;        // quantize-only: packed head t at out + t*out_stride
   long long out_stride;
   int n_tiles;
-  int cls_first, cls_n;      // decode by width class: heads cls_heads[cls_first ..+cls_n)
+  // decode of STEP/uniform GDN: one launch over every width class.  Class i
+  // (i < n_cls) holds heads cls_heads[cls_first[i] ..+ cls_n[i]) of width
+  // cls_bits[i]; its tiles are blockIdx in [cls_end[i-1], cls_end[i]).
+  int n_cls;
+  int cls_first[5], cls_n[5], cls_bits[5], cls_end[5];
 };
 
 // Kernel launchers (defined in the .hip files).
 hipError_t launch_tile_gdn(const TileArgs& a, hipStream_t s);     // uniform + STEP GDN
-hipError_t launch_decode_gdn(const TileArgs& a, int bits, hipStream_t s);  // one width class
+// decode by width class: solo = class 0 alone in its width-specialised kernel,
+// else every class of a in one merged launch
+hipError_t launch_decode_gdn(const TileArgs& a, bool solo, hipStream_t s);
 hipError_t launch_tile_kda(const TileArgs& a, hipStream_t s);     // STEP KDA
 hipError_t launch_tile_window(const TileArgs& a, hipStream_t s);  // per-window variant
 hipError_t launch_dense_step(int kind, int H, int dk, int dv, float* S, long long n_slots,

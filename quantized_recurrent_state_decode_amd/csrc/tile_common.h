@@ -210,19 +210,32 @@ struct Geo {
 
 // Resolve the tile a workgroup owns.  Returns false if it must be skipped
 // (slot id or head id out of range); the decode op then writes NaN outputs.
+// A value equal on every active lane of the wave (a per-tile index, offset or
+// coefficient loaded from memory), moved to a scalar register so that it and
+// the pointers built from it take no vector registers.
+__device__ __forceinline__ int wuni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ long long wuni(long long v) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+__device__ __forceinline__ float wuni(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
 __device__ __forceinline__ bool resolve_tile(const TileArgs& a, int tile, int& h,
                                              unsigned char*& base) {
   if (a.head_ids) {
-    h = a.head_ids[tile];
+    h = wuni(a.head_ids[tile]);
     if (h < 0 || h >= a.P.H) return false;
     base = a.out + (long long)tile * a.out_stride;
     return true;
   }
   const int bi = tile / a.P.H;
   h = tile - bi * a.P.H;
-  const int slot = a.slots[bi];
+  const int slot = wuni(a.slots[bi]);
   if (slot < 0 || (long long)slot >= a.n_slots) return false;
-  base = a.pool + (long long)slot * a.P.slot_bytes + a.P.head_off[h];
+  base = a.pool + (long long)slot * a.P.slot_bytes + wuni(a.P.head_off[h]);
   return true;
 }
 

@@ -167,8 +167,8 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
   const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p;
   const int r0 = 32 * rb;                     // first row of this lane's block
   constexpr int op = OP;
-  __half* rs_ptr = reinterpret_cast<__half*>(base + a.P.r_off[h]);
-  __half* c_ptr = UNI ? nullptr : reinterpret_cast<__half*>(base + a.P.c_off[h]);
+  __half* rs_ptr = reinterpret_cast<__half*>(base + wuni(a.P.r_off[h]));
+  __half* c_ptr = UNI ? nullptr : reinterpret_cast<__half*>(base + wuni(a.P.c_off[h]));
   const long long tk = (long long)tile * DK, tv = (long long)tile * DV;
 
   float x[64];
@@ -198,8 +198,8 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
       if (op == OP_UNPACK) {
         sm.rowc[3][i] = sc;
       } else {
-        const float alpha = a.gate[tile];
-        const float kk = a.k[tk + i], qq = a.q[tk + i], bk = a.beta[tile] * kk;
+        const float alpha = wuni(a.gate[tile]);
+        const float kk = a.k[tk + i], qq = a.q[tk + i], bk = wuni(a.beta[tile]) * kk;
         const float rho = alpha * sc;
         // a vanishing retention keeps the division finite; the dropped part
         // (rp - rho) c_j z_ij is below 2^-60 of the write term
@@ -271,9 +271,11 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
     sm.colB[rb][p] = make_float2(y0, y1);
   }
   // row statistics of Xt (sum |.| for STEP, max |.| for uniform), 16 rows at a
-  // time through a per-wave transpose; the owner lane of each row then derives
-  // the row's stored scale and its constants for the next passes
+  // time through a per-wave transpose; after the shuffle stage every lane
+  // holds the statistic of row (p & 15) of the half, so one pass of the 32
+  // owner lanes then derives the stored scale of every row of the block
   uint32_t wd[2 * BITS];
+  float sh[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -283,9 +285,9 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
     }
     wave_sync();
     const int mm = p & 15, part = p >> 4;
-    float s = 0.f;
+    float s = sm.rowt[rb][mm][part * 16];
 #pragma unroll
-    for (int pp = 0; pp < 16; ++pp) {
+    for (int pp = 1; pp < 16; ++pp) {
       const float vv = sm.rowt[rb][mm][part * 16 + pp];
       s = UNI ? fmaxf(s, vv) : s + vv;
     }
@@ -294,23 +296,28 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
       const float ov = __shfl_xor(s, o);
       s = UNI ? fmaxf(s, ov) : s + ov;
     }
-    if (part == 0) {
-      const int i = r0 + 16 * hf + mm;
-      const float rp = sm.rowc[3][i];
-      if (UNI) {
-        const float si = fp16_scale(rp * s * (1.0f / QB));
-        rs_ptr[i] = __float2half_rn(si);
-        sm.rowc[4][i] = rp * frcp(si);  // code pre-value = Xt * sigma_i
-      } else {
-        const float wi = a.P.w[h * DK + i];
-        const float ri = fp16_scale(sqrtf(rp * s * (1.0f / (float)DV) * a.P.winv[h * DK + i]));
-        rs_ptr[i] = __float2half_rn(ri);
-        sm.rowc[4][i] = rp * frcp(ri);                  // pi: X / r_i = Xt * pi_i
-        sm.rowc[5][i] = wi * wi * ri * ri * (1.0f / QB);  // lambda: refit weight
-      }
-    }
+    sh[hf] = s;
     wave_sync();
   }
+  if (p < 32) {
+    const int i = r0 + p;
+    const float s = p < 16 ? sh[0] : sh[1];
+    const float rp = sm.rowc[3][i];
+    if (UNI) {
+      const float si = fp16_scale(rp * s * (1.0f / QB));
+      rs_ptr[i] = __float2half_rn(si);
+      sm.rowc[4][i] = rp * frcp(si);  // code pre-value = Xt * sigma_i
+    } else {
+      const float wi = a.P.w[h * DK + i];
+      // the hardware square root (1 ulp) only feeds an FP16 rounding
+      const float ri =
+          fp16_scale(__builtin_amdgcn_sqrtf(rp * s * (1.0f / (float)DV) * a.P.winv[h * DK + i]));
+      rs_ptr[i] = __float2half_rn(ri);
+      sm.rowc[4][i] = rp * frcp(ri);                  // pi: X / r_i = Xt * pi_i
+      sm.rowc[5][i] = wi * wi * ri * ri * (1.0f / QB);  // lambda: refit weight
+    }
+  }
+  wave_sync();
   if constexpr (UNI) {
     if (op == OP_DECODE) {
       __syncthreads();
@@ -343,9 +350,7 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
                              fmaxf(fabsf(x[2 * m + 5]), fabsf(x[2 * m + 7]))));
     }
     sm.colM[rb][p] = make_float2(mx0, mx1);
-    // below the FP16 maximum, c0 >= max |P| (1 - 2^-11) keeps every code within
-    // +-q_b without a clamp; a saturated column anywhere switches the tile to it
-    const bool sat = __syncthreads_or(fmaxf(mx0, mx1) > kFp16Max) != 0;
+    __syncthreads();
     if (op == OP_DECODE && rb == 0) {
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
@@ -364,6 +369,10 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
     }
     const float cz0 = fp16_scale(m0), cz1 = fp16_scale(m1);
     const float tau0 = QB * frcp(cz0), tau1 = QB * frcp(cz1);
+    // below the FP16 maximum, c0 >= max |P| (1 - 2^-11) keeps every code within
+    // +-q_b without a clamp; a wave holding a saturated column clamps all of
+    // its codes (a no-op on the others), the decision staying wave-uniform
+    const bool sat = __ballot(fmaxf(m0, m1) > kFp16Max) != 0ull;
     // pass 4: codes by magic rounding, fixed-code weighted least-squares sums
     float4 nd;
     if (sat) codes_refit<BITS, true>(x, &sm.rowc[5][r0], tau0, tau1, nd, wd);
@@ -422,11 +431,11 @@ __device__ __forceinline__ void pivot_tile(const TileArgs& a, const int tile, co
         *reinterpret_cast<float2*>(S + (32 * rb + m) * DV + j0) = make_float2(x[2 * m], x[2 * m + 1]);
       return;
     }
-    const float alpha = a.gate[tile];
+    const float alpha = wuni(a.gate[tile]);
     if (t < DK) {
       const float kk = a.k[tk + t];
       sm.rowc[0][t] = alpha * kk;
-      sm.rowc[1][t] = a.beta[tile] * kk;
+      sm.rowc[1][t] = wuni(a.beta[tile]) * kk;
       sm.rowc[2][t] = a.q[tk + t];
     }
     __syncthreads();
@@ -521,50 +530,105 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_tile_kernel(TileArgs a) {
 }
 
 
-// Decode of one code-width class: the heads of the class are
-// cls_heads[cls_first .. cls_first + cls_n); tile t = (batch row t / cls_n,
-// class head t % cls_n).  One kernel per width keeps each width's register
-// allocation separate.
-template <int DK, int DV, int BITS, bool UNI>
+// Pick entry i of a five-entry kernel-argument array with selects, so the
+// argument block is never indexed with a run-time subscript.
+__device__ __forceinline__ int pick5(const int (&v)[5], int i) {
+  int r = v[0];
+#pragma unroll
+  for (int j = 1; j < 5; ++j) r = i == j ? v[j] : r;
+  return r;
+}
+
+// Decode of every code-width class in one grid.  Class i covers blockIdx in
+// [cls_end[i-1], cls_end[i]); inside a class, tile t = (batch row t / cls_n,
+// class head t % cls_n).  The width is uniform over a workgroup, so each
+// workgroup runs exactly one of the width-specialised bodies; the kernel's
+// register budget is the largest of them.
+template <int DK, int DV, bool UNI>
 __global__ __launch_bounds__((DK / 32) * (DV / 2))
 __attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_decode_kernel(TileArgs a) {
   __shared__ SmemGdn<DK, DV> sm;
-  const int t = blockIdx.x;
-  const int bi = t / a.cls_n;
-  const int h = a.P.cls_heads[a.cls_first + (t - bi * a.cls_n)];
+  int t = blockIdx.x;
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c += t >= a.cls_end[j] ? 1 : 0;
+  if (c > 0) t -= pick5(a.cls_end, c - 1);
+  const int n = pick5(a.cls_n, c);
+  const int bits = pick5(a.cls_bits, c);
+  const int bi = t / n;
+  const int h = wuni(a.P.cls_heads[pick5(a.cls_first, c) + (t - bi * n)]);
   const int tile = bi * a.P.H + h;
-  const int slot = a.slots[bi];
+  const int slot = wuni(a.slots[bi]);
   if (slot < 0 || (long long)slot >= a.n_slots) {
     if (threadIdx.x < DV) a.y[(long long)tile * DV + threadIdx.x] = __builtin_nanf("");
     return;
   }
-  unsigned char* base = a.pool + (long long)slot * a.P.slot_bytes + a.P.head_off[h];
+  unsigned char* base = a.pool + (long long)slot * a.P.slot_bytes + wuni(a.P.head_off[h]);
+  switch (bits) {
+    case 2: quant_tile<DK, DV, 2, UNI, OP_DECODE>(a, tile, h, base, sm); break;
+    case 4: quant_tile<DK, DV, 4, UNI, OP_DECODE>(a, tile, h, base, sm); break;
+    case 6: quant_tile<DK, DV, 6, UNI, OP_DECODE>(a, tile, h, base, sm); break;
+    case 8: quant_tile<DK, DV, 8, UNI, OP_DECODE>(a, tile, h, base, sm); break;
+    case 16:
+      if constexpr (!UNI) pivot_tile<DK, DV, OP_DECODE>(a, tile, h, base, sm);
+      break;
+    default: break;
+  }
+}
+
+// Decode of class 0 alone with its width fixed at compile time: the register
+// allocation and schedule are those of that width only.
+template <int DK, int DV, int BITS, bool UNI>
+__global__ __launch_bounds__((DK / 32) * (DV / 2))
+__attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_class_kernel(TileArgs a) {
+  __shared__ SmemGdn<DK, DV> sm;
+  const int t = blockIdx.x;
+  const int n = a.cls_n[0];
+  const int bi = t / n;
+  const int h = wuni(a.P.cls_heads[a.cls_first[0] + (t - bi * n)]);
+  const int tile = bi * a.P.H + h;
+  const int slot = wuni(a.slots[bi]);
+  if (slot < 0 || (long long)slot >= a.n_slots) {
+    if (threadIdx.x < DV) a.y[(long long)tile * DV + threadIdx.x] = __builtin_nanf("");
+    return;
+  }
+  unsigned char* base = a.pool + (long long)slot * a.P.slot_bytes + wuni(a.P.head_off[h]);
   if constexpr (BITS == 16) pivot_tile<DK, DV, OP_DECODE>(a, tile, h, base, sm);
   else quant_tile<DK, DV, BITS, UNI, OP_DECODE>(a, tile, h, base, sm);
 }
 
 template <int DK, int DV, int BITS>
-hipError_t launch_class(const TileArgs& a, hipStream_t s) {
-  const dim3 grid(a.n_tiles), block((DK / 32) * (DV / 2));
+hipError_t launch_solo(const TileArgs& a, const dim3 grid, const dim3 block, hipStream_t s) {
   if (a.P.mode == SQ_MODE_UNIFORM) {
     if constexpr (BITS == 16) return hipErrorInvalidValue;
-    else hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, BITS, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gdn_class_kernel<DK, DV, BITS, true>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, BITS, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gdn_class_kernel<DK, DV, BITS, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
 
+// solo: class 0 alone through its width-specialised kernel; otherwise every
+// class of a through the merged kernel
 template <int DK, int DV>
-hipError_t launch_class_bits(const TileArgs& a, int bits, hipStream_t s) {
-  switch (bits) {
-    case 2: return launch_class<DK, DV, 2>(a, s);
-    case 4: return launch_class<DK, DV, 4>(a, s);
-    case 6: return launch_class<DK, DV, 6>(a, s);
-    case 8: return launch_class<DK, DV, 8>(a, s);
-    case 16: return launch_class<DK, DV, 16>(a, s);
-    default: return hipErrorInvalidValue;
+hipError_t launch_decode(const TileArgs& a, bool solo, hipStream_t s) {
+  if (a.n_tiles <= 0) return hipSuccess;
+  const dim3 grid(a.n_tiles), block((DK / 32) * (DV / 2));
+  if (solo) {
+    switch (a.cls_bits[0]) {
+      case 2: return launch_solo<DK, DV, 2>(a, grid, block, s);
+      case 4: return launch_solo<DK, DV, 4>(a, grid, block, s);
+      case 6: return launch_solo<DK, DV, 6>(a, grid, block, s);
+      case 8: return launch_solo<DK, DV, 8>(a, grid, block, s);
+      case 16: return launch_solo<DK, DV, 16>(a, grid, block, s);
+      default: return hipErrorInvalidValue;
+    }
   }
+  if (a.P.mode == SQ_MODE_UNIFORM)
+    hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, false>), grid, block, 0, s, a);
+  return hipGetLastError();
 }
 
 template <int DK, int DV>
@@ -579,12 +643,12 @@ hipError_t launch(const TileArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_decode_gdn(const TileArgs& a, int bits, hipStream_t s) {
+hipError_t launch_decode_gdn(const TileArgs& a, bool solo, hipStream_t s) {
   const int dk = a.P.dk, dv = a.P.dv;
-  if (dk == 128 && dv == 128) return launch_class_bits<128, 128>(a, bits, s);
-  if (dk == 64 && dv == 64) return launch_class_bits<64, 64>(a, bits, s);
-  if (dk == 128 && dv == 64) return launch_class_bits<128, 64>(a, bits, s);
-  if (dk == 64 && dv == 128) return launch_class_bits<64, 128>(a, bits, s);
+  if (dk == 128 && dv == 128) return launch_decode<128, 128>(a, solo, s);
+  if (dk == 64 && dv == 64) return launch_decode<64, 64>(a, solo, s);
+  if (dk == 128 && dv == 64) return launch_decode<128, 64>(a, solo, s);
+  if (dk == 64 && dv == 128) return launch_decode<64, 128>(a, solo, s);
   return hipErrorInvalidValue;
 }
 

@@ -114,9 +114,9 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   }
   const long long tk = (long long)tile * DK, tv = (long long)tile * DV;
   const int* rkey = a.P.row_key + h * DK;
-  const int code_bytes = a.P.r_off[h];
-  __half* r_ptr = reinterpret_cast<__half*>(base + a.P.r_off[h]);
-  __half* c_ptr = reinterpret_cast<__half*>(base + a.P.c_off[h]);
+  const int code_bytes = wuni(a.P.r_off[h]);
+  __half* r_ptr = reinterpret_cast<__half*>(base + code_bytes);
+  __half* c_ptr = reinterpret_cast<__half*>(base + wuni(a.P.c_off[h]));
   // per-storage-row metadata of this wave's rows
   if (p < 32) {
     const int s = r0 + p;
@@ -150,7 +150,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
         sm.rowc[3][s] = sc;
       } else {
         const float d = a.gate[tk + key];
-        const float kk = a.k[tk + key], qq = a.q[tk + key], bk = a.beta[tile] * kk;
+        const float kk = a.k[tk + key], qq = a.q[tk + key], bk = wuni(a.beta[tile]) * kk;
         const float rho = d * sc;
         // a vanishing retention keeps the division finite; the dropped part
         // (rp - rho) c_j z_sj is below 2^-60 of the write term

@@ -213,7 +213,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     return;
   }
   const int P = a.P.p;
-  const WinPtrs wp = win_ptrs(base, a.P.r_off[h], DK, DV, P);
+  const WinPtrs wp = win_ptrs(base, wuni(a.P.r_off[h]), DK, DV, P);
   constexpr int op = OP;
   float x[64];
   if constexpr (op == OP_PACK) {
@@ -253,7 +253,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
   }
   // ---- decode token i = ell + 1 (record index ell, 0-based)
   const long long tk = (long long)tile * DK, tv = (long long)tile * DV;
-  const float alpha = a.gate[tile], beta = a.beta[tile];
+  const float alpha = wuni(a.gate[tile]), beta = wuni(a.beta[tile]);
   if (t == 0) sm.al[ell] = alpha;
   if (p < 32) {  // per-row constants of this wave's rows
     const int r = r0 + p;
