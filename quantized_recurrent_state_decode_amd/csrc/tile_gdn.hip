@@ -88,10 +88,13 @@ __device__ __forceinline__ void codes_refit(float (&x)[64], const float* lam, fl
   float N0 = 0.f, N1 = 0.f, D0 = 0.f, D1 = 0.f;
 #pragma unroll
   for (int g = 0; g < 32; g += RG) {
-    // order the work group by group so that rounded values are packed while
-    // their rows are still the only ones in flight
+    // at 2 and 6 bits (8-row groups) order the work group by group so that rounded
+    // values are packed while their rows are still the only ones in flight;
+    // 4- and 8-bit codes schedule within the register budget unaided
+    if constexpr (BITS == 2 || BITS == 6) {
 #pragma unroll
-    for (int k = 0; k < 2 * RG; ++k) asm volatile("" : "+v"(x[2 * g + k]));
+      for (int k = 0; k < 2 * RG; ++k) asm volatile("" : "+v"(x[2 * g + k]));
+    }
 #pragma unroll
     for (int m = g; m < g + RG; m += 4) {
       const float4 l4 = ld4(lam + m);

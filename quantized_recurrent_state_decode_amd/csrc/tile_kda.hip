@@ -48,24 +48,47 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Two b-bit fields (columns 2p, 2p+1) of a row stored at byte `off`.
+// A per-row value: with 64 lanes per row block every lane of a wave works on
+// the same storage row, so the value is wave-uniform and goes to a scalar
+// register (row-wise branches become scalar); with 32 lanes a wave spans two
+// row blocks and the value stays per lane.
+template <bool WU>
+__device__ __forceinline__ int rowu(int v) {
+  if constexpr (WU) return wuni(v);
+  else return v;
+}
+template <bool WU>
+__device__ __forceinline__ float rowu(float v) {
+  if constexpr (WU) return wuni(v);
+  else return v;
+}
+
+// Two b-bit fields (columns 2p, 2p+1) of a row stored at byte `off` (rows
+// start on 16-byte boundaries; fields are two's complement, least significant
+// bit first).
 __device__ __forceinline__ void read_pair(const unsigned char* codes, int off, int b, int p,
                                           float& z0, float& z1) {
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(codes);
+  const unsigned char* row = codes + off;
   if (b == 16) {
-    const uint32_t v = w[(off >> 2) + p];
+    const uint32_t v = reinterpret_cast<const uint32_t*>(row)[p];
     z0 = half_from_bits(v);
     z1 = half_from_bits(v >> 16);
     return;
   }
-  const int bit = 2 * p * b;  // first bit of the pair in the row
-  const int wi = (off >> 2) + (bit >> 5), sh = bit & 31;
-  uint64_t v = w[wi];
-  if (sh + 2 * b > 32) v |= (uint64_t)w[wi + 1] << 32;
-  const uint32_t f = (uint32_t)(v >> sh);
-  const int s = 32 - b;
-  z0 = (float)((int32_t)(f << s) >> s);
-  z1 = (float)((int32_t)((f >> b) << s) >> s);
+  uint32_t f;
+  if (b == 8) {
+    f = reinterpret_cast<const unsigned short*>(row)[p];
+  } else if (b == 4) {
+    f = row[p];
+  } else if (b == 2) {
+    f = (uint32_t)row[p >> 1] >> (4 * (p & 1));
+  } else {  // 6 bits: the pair's 12 bits start at bit 12 p
+    const int i = (3 * p) >> 1;
+    f = ((uint32_t)row[i] | ((uint32_t)row[i + 1] << 8)) >> (4 * (p & 1));
+  }
+  // the builtin returns an unsigned type: reinterpret as signed before converting
+  z0 = (float)(int)__builtin_amdgcn_sbfe((int)f, 0, b);
+  z1 = (float)(int)__builtin_amdgcn_sbfe((int)f, b, b);
 }
 
 // Write the lane's two codes (magic-rounded floats m0, m1) of a b-bit row.
@@ -101,6 +124,7 @@ __global__ __launch_bounds__((DK / 32) * (DV / 2))
 __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   using G = Geo<DK, DV>;
   constexpr int NP = G::NP, NRB = G::NRB, NT = G::NT;
+  constexpr bool WU = NP % 64 == 0;  // a wave's lanes share their rows
   __shared__ SmemKda<DK, DV> sm;
   unsigned char* codes = reinterpret_cast<unsigned char*>(kda_dyn);
   float(*rowt)[16][NP + 1] = reinterpret_cast<float(*)[16][NP + 1]>(kda_dyn);
@@ -165,9 +189,9 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
       const int s = r0 + m;
-      const int b = sm.bits[s];
+      const int b = rowu<WU>(sm.bits[s]);
       float z0, z1;
-      read_pair(codes, sm.off[s], b, p, z0, z1);
+      read_pair(codes, rowu<WU>(sm.off[s]), b, p, z0, z1);
       x[2 * m] = b == 16 ? z0 : c0 * z0;
       x[2 * m + 1] = b == 16 ? z1 : c1 * z1;
     }
@@ -221,7 +245,10 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
     sm.colB[rb][p] = make_float2(y0, y1);
   }
   // row statistics of Xt (integer rows), 16 rows at a time through a
-  // per-wave transpose in the dynamic buffer
+  // per-wave transpose in the dynamic buffer; every lane ends up holding the
+  // sum of row (p & 15) of the half, and the 32 owner lanes then derive the
+  // stored scales of the block's rows in one pass
+  float sh[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -229,32 +256,37 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
       rowt[rb][m][p] = fabsf(x[2 * (16 * hf + m)]) + fabsf(x[2 * (16 * hf + m) + 1]);
     wave_sync();
     const int mm = p & 15, part = p >> 4;
-    float s = 0.f;
+    float s = rowt[rb][mm][part * 16];
 #pragma unroll
-    for (int pp = 0; pp < 16; ++pp) s += rowt[rb][mm][part * 16 + pp];
+    for (int pp = 1; pp < 16; ++pp) s += rowt[rb][mm][part * 16 + pp];
 #pragma unroll
     for (int o = 16; o < NP; o <<= 1) s += __shfl_xor(s, o);
-    if (part == 0) {
-      const int si = r0 + 16 * hf + mm;
-      const float rp = sm.rowc[3][si];
-      if (sm.bits[si] == 16) {
-        r_ptr[si] = __float2half_rn(0.0f);
-        sm.rowc[4][si] = rp;  // FP16 rows: X = rho Xt
-        sm.rowc[5][si] = 0.f;
-        sm.rowc[6][si] = 0.f;
-      } else {
-        const int key = rkey[si];
-        const float wi = a.P.w[h * DK + key], iq = frcp(sm.qb[si]);
-        const float ri = fp16_scale(sqrtf(rp * s * (1.0f / (float)DV) * a.P.winv[h * DK + key]));
-        r_ptr[si] = __float2half_rn(ri);
-        const float ww = wi * wi * ri * ri * iq;
-        sm.rowc[4][si] = rp * frcp(ri);
-        sm.rowc[5][si] = ww;
-        sm.rowc[6][si] = ww * iq;
-      }
-    }
+    sh[hf] = s;
     wave_sync();
   }
+  if (p < 32) {
+    const int si = r0 + p;
+    const float s = p < 16 ? sh[0] : sh[1];
+    const float rp = sm.rowc[3][si];
+    if (sm.bits[si] == 16) {
+      r_ptr[si] = __float2half_rn(0.0f);
+      sm.rowc[4][si] = rp;  // FP16 rows: X = rho Xt
+      sm.rowc[5][si] = 0.f;
+      sm.rowc[6][si] = 0.f;
+    } else {
+      const int key = rkey[si];
+      const float wi = a.P.w[h * DK + key], iq = frcp(sm.qb[si]);
+      // the hardware square root (1 ulp) only feeds an FP16 rounding
+      const float ri =
+          fp16_scale(__builtin_amdgcn_sqrtf(rp * s * (1.0f / (float)DV) * a.P.winv[h * DK + key]));
+      r_ptr[si] = __float2half_rn(ri);
+      const float ww = wi * wi * ri * ri * iq;
+      sm.rowc[4][si] = rp * frcp(ri);
+      sm.rowc[5][si] = ww;
+      sm.rowc[6][si] = ww * iq;
+    }
+  }
+  wave_sync();
   // pass 3: P = X / r on integer rows (column absmax), X on FP16 rows
   float mx0 = 0.f, mx1 = 0.f;
 #pragma unroll
@@ -263,13 +295,13 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
     const float f = sm.rowc[4][s];
     x[2 * m] *= f;
     x[2 * m + 1] *= f;
-    if (sm.bits[s] != 16) {
+    if (rowu<WU>(sm.bits[s]) != 16) {
       mx0 = fmaxf(mx0, fabsf(x[2 * m]));
       mx1 = fmaxf(mx1, fabsf(x[2 * m + 1]));
     }
   }
   sm.colM[rb][p] = make_float2(mx0, mx1);
-  const bool sat = __syncthreads_or(fmaxf(mx0, mx1) > kFp16Max) != 0;
+  __syncthreads();
   if (OP == OP_DECODE && rb == 0) {
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
@@ -287,19 +319,22 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   }
   const float cz0 = fp16_scale(m0), cz1 = fp16_scale(m1);
   const float ic0 = frcp(cz0), ic1 = frcp(cz1);
+  // below the FP16 maximum every code lies within +-q_b unclamped; a wave
+  // holding a saturated column clamps all its codes (a no-op on the others)
+  const bool sat = __ballot(fmaxf(m0, m1) > kFp16Max) != 0ull;
   // pass 4: codes (magic rounding, per-row q_b) and the refit sums; the new
   // codes go into the staged head in place
   float N0 = 0.f, N1 = 0.f, D0 = 0.f, D1 = 0.f;
 #pragma unroll
   for (int m = 0; m < 32; ++m) {
     const int s = r0 + m;
-    const int b = sm.bits[s];
+    const int b = rowu<WU>(sm.bits[s]), off = rowu<WU>(sm.off[s]);
     if (b == 16) {
-      *reinterpret_cast<uint32_t*>(codes + sm.off[s] + 4 * p) =
+      *reinterpret_cast<uint32_t*>(codes + off + 4 * p) =
           half_bits(x[2 * m]) | (half_bits(x[2 * m + 1]) << 16);
       continue;
     }
-    const float qb = sm.qb[s], ln = sm.rowc[5][s], ld = sm.rowc[6][s];
+    const float qb = rowu<WU>(sm.qb[s]), ln = sm.rowc[5][s], ld = sm.rowc[6][s];
     const float pv0 = x[2 * m], pv1 = x[2 * m + 1];
     float mg0 = fmaf(pv0, qb * ic0, kMagic), mg1 = fmaf(pv1, qb * ic1, kMagic);
     if (sat) {  // a column scale saturated at the FP16 maximum
@@ -311,7 +346,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
     N1 = fmaf(ln * z1, pv1, N1);
     D0 = fmaf(ld * z0, z0, D0);
     D1 = fmaf(ld * z1, z1, D1);
-    write_pair(codes, sm.off[s], b, p, mg0, mg1);
+    write_pair(codes, off, b, p, mg0, mg1);
   }
   sm.colC[rb][p] = make_float4(N0, N1, D0, D1);
   __syncthreads();
