@@ -30,10 +30,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "state-update steps/s and HBM GB/s (% of peak) at batch 512, 1 GPU"
-# kernels one decode step launches (GDN STEP / uniform: one per code-width class)
-KERNEL = {"step": "gdn_decode_kernel<128,128,b> (one launch per code width)",
-          "uniform": "gdn_decode_kernel<d,d,b,uniform>", "window": "window_tile_kernel<128,128>",
+# kernels one decode step launches (GDN STEP: the largest code-width class alone,
+# the other classes in one merged launch)
+KERNEL = {"step": "gdn_class_kernel<128,128,b> for the largest code-width class + "
+                  "gdn_decode_kernel<128,128> for the other classes",
+          "uniform": "gdn_class_kernel<d,d,b,uniform>", "window": "window_tile_kernel<128,128,16>",
           "kda": "kda_tile_kernel<128,128>"}
+# sources whose change invalidates a committed traffic measurement, per kernel family
+TRAFFIC_SOURCES = {"gdn": ("tile_gdn.hip",), "kda": ("tile_kda.hip",), "window": ("tile_window.hip",)}
 HBM_PEAK_GBS = 8000.0
 
 
@@ -52,11 +56,10 @@ def _plan(sq, w):
                                         "horizon": st["horizon"]})
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, family: str):
     """HBM bytes per step from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summary of this workload, if the decode kernel sources are still the ones
     the counters were taken on (else None)."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -65,13 +68,21 @@ def measured_traffic(workload: str):
         if ":" in line and line.split(":")[0] in ("traffic_bytes_per_step", "kernel_source_sha256_16"):
             k, v = line.split(":", 1)
             fields[k] = v.strip()
-    csrc = os.path.join(ROOT, "quantized_recurrent_state_decode_amd", "csrc")
-    h = hashlib.sha256()
-    for f in ("tile_gdn.hip", "tile_common.h", "sq_internal.h"):
-        h.update(open(os.path.join(csrc, f), "rb").read())
-    if fields.get("kernel_source_sha256_16") != h.hexdigest()[:16]:
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash(family):
         return None
     return int(fields["traffic_bytes_per_step"])
+
+
+def kernel_source_hash(family: str) -> str:
+    """First 16 hex digits of the sha256 of the decode sources of a kernel
+    family (its kernel file, the shared tile header, the internal header and
+    the host dispatcher)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "quantized_recurrent_state_decode_amd", "csrc")
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES[family] + ("tile_common.h", "sq_internal.h", "sq_host.cpp"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic_bytes(desc, w) -> int:
@@ -259,6 +270,7 @@ def main():
     launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     abytes = algorithmic_bytes(desc, w)
+    family = "window" if w.mode == "window" else w.kind
     gbs_step = abytes / (ms_per_step * 1e-3) / 1e9
     gbs_kernel = abytes / (launch_ms * 1e-3) / 1e9
     out = {
@@ -286,8 +298,9 @@ def main():
                    "state_gbs": gbs_step, "pct_of_hbm_peak": 100.0 * gbs_step / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": gbs_kernel, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": gbs_kernel / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w.name),
+                     "traffic": measured_traffic(w.name, family),
                      "kernel": KERNEL[w.mode if w.kind == "gdn" else "kda"],
+                     "kernel_source_sha256_16": kernel_source_hash(family),
                      "launch_ms": launch_ms, "bytes_per_launch": abytes,
                      "launch": "one sq_decode_step call (all its kernel launches), HIP events "
                                "on the launch stream"},
