@@ -35,9 +35,10 @@ METRIC = "state-update steps/s and HBM GB/s (% of peak) at batch 512, 1 GPU"
 KERNEL = {"step": "gdn_class_kernel<128,128,b> for the largest code-width class + "
                   "gdn_decode_kernel<128,128> for the other classes",
           "uniform": "gdn_class_kernel<d,d,b,uniform>", "window": "window_tile_kernel<128,128,16>",
-          "kda": "kda_tile_kernel<128,128>"}
+          "kda": "kda_tile_kernel<128,128>", "dense": "dense_kernel<128,128> (fp32 state)"}
 # sources whose change invalidates a committed traffic measurement, per kernel family
-TRAFFIC_SOURCES = {"gdn": ("tile_gdn.hip",), "kda": ("tile_kda.hip",), "window": ("tile_window.hip",)}
+TRAFFIC_SOURCES = {"gdn": ("tile_gdn.hip",), "kda": ("tile_kda.hip",), "window": ("tile_window.hip",),
+                   "dense": ("dense.hip",)}
 HBM_PEAK_GBS = 8000.0
 
 
@@ -94,6 +95,8 @@ def algorithmic_bytes(desc, w) -> int:
     B, H, dk, dv = w.batch, w.heads, w.d_k, w.d_v
     gate = B * H * (dk if w.kind == "kda" else 1) * 4
     io = B * H * (2 * dk + dv) * 4 + B * H * 4 + gate + B * H * dv * 4 + B * 4
+    if w.mode == "dense":
+        return 2 * B * H * dk * dv * 4 + io
     if w.mode != "window":
         return 2 * B * desc["payload_bytes"] + io
     p = w.window
@@ -117,7 +120,10 @@ def build_state(sq, w, pools, slots_dev, steps):
         sq.sq_dense_step(0 if w.kind == "gdn" else 1, w.heads, w.d_k, w.d_v, S, w.batch, ident,
                          w.batch, inp["q"], inp["k"], inp["v"], inp["beta"], inp["gate"], y)
     for pl in pools:
-        sq.sq_pool_pack(pl["plan"], pl["dev_plan"], pl["pool"], w.n_slots, slots_dev, w.batch, S)
+        if w.mode == "dense":
+            pl["pool"].index_copy_(0, slots_dev.long(), S)
+        else:
+            sq.sq_pool_pack(pl["plan"], pl["dev_plan"], pl["pool"], w.n_slots, slots_dev, w.batch, S)
     torch.cuda.synchronize()
     return S
 
@@ -193,6 +199,8 @@ def main():
     ap.add_argument("--input-sets", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the fp32-dense and uniform-INT4 runs at the pool workload's shape")
     ap.add_argument("--state-warmup", type=int, default=None,
                     help="fp32 steps that build the initial state (default: the workload's 128)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -211,12 +219,76 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = SI.workload(args.workload)
-    plan = _plan(sq, w)
-    desc = sq.sq_plan_query(plan)
+    m = measure(sq, w, args)
+    abytes, ms_per_step, launch_ms, desc = m["abytes"], m["ms_per_step"], m["launch_ms"], m["desc"]
+    family = "window" if w.mode == "window" else ("dense" if w.mode == "dense" else w.kind)
+    gbs_step = abytes / (ms_per_step * 1e-3) / 1e9
+    gbs_kernel = abytes / (launch_ms * 1e-3) / 1e9
+    hist = None
+    if desc is not None and desc["unit_bits"] is not None:
+        hist = {str(b): int(c) for b, c in zip(*np.unique(desc["unit_bits"], return_counts=True))}
+    out = {
+        "metric": METRIC,
+        "value": 1e3 / ms_per_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_slots": w.n_slots,
+                   "heads": w.heads, "d_k": w.d_k, "d_v": w.d_v, "mode": w.mode,
+                   "kind": w.kind, "nominal_bits": w.nominal_bits if w.mode == "step" else
+                   (w.bits if w.mode == "uniform" else (32 if w.mode == "dense" else 8)),
+                   "unit_bits_histogram": hist,
+                   "slot_bytes": (w.heads * w.d_k * w.d_v * 4 if desc is None else desc["slot_bytes"]),
+                   "layers_rotated": args.layers,
+                   "input_sets": args.input_sets, "algorithmic_bytes_per_step": abytes,
+                   "state_gbs": gbs_step, "pct_of_hbm_peak": 100.0 * gbs_step / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "achieved": gbs_kernel, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gbs_kernel / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name, family),
+                     "kernel": KERNEL[w.mode if w.kind == "gdn" else "kda"],
+                     "kernel_source_sha256_16": kernel_source_hash(family),
+                     "launch_ms": launch_ms, "bytes_per_launch": abytes,
+                     "launch": "one decode call (sq_decode_step with all its kernel launches, or "
+                               "sq_dense_step in dense mode), HIP events on the launch stream"},
+    }
+    if not args.no_cpu and desc is not None:
+        torch.cuda.synchronize()
+        sb = desc["slot_bytes"]
+        pb = m["pools"][0]["pool"]
+        s0 = int(m["slots"][0])
+        host = pb[s0 * sb:(s0 + 1) * sb].cpu().numpy().tobytes()
+        out["cpu_baseline"] = cpu_baseline(w, desc, host, m["slots"], args.cpu_seconds)
+    del m
+    if w.name == "gdn_pool_step4" and not args.no_compare:
+        out["same_hardware"] = same_hardware(sq, args, out["value"])
+    print(json.dumps(out))
+
+
+def measure(sq, w, args) -> dict:
+    """Time args.steps consecutive decode steps of workload w (after
+    args.warmup untimed ones), rotating args.layers independent pools so that
+    the live state exceeds the on-package cache, then time 64 single calls
+    with HIP events on the launch stream."""
+    import torch
+    from synth import inputs as SI
+    dense = w.mode == "dense"
+    plan = None if dense else _plan(sq, w)
+    desc = None if dense else sq.sq_plan_query(plan)
     slots = SI.slot_ids(w)
     slots_dev = torch.from_numpy(slots).cuda()
     pools = []
     for _ in range(args.layers):
+        if dense:
+            pools.append({"pool": torch.zeros((w.n_slots, w.heads, w.d_k, w.d_v),
+                                              dtype=torch.float32, device="cuda")})
+            continue
         dp = sq.device_plan(plan)
         pool = torch.empty(sq.sq_pool_bytes(plan, w.n_slots), dtype=torch.uint8, device="cuda")
         sq.sq_pool_init(plan, dp, pool, w.n_slots)
@@ -238,13 +310,19 @@ def main():
     y = torch.empty((args.input_sets, w.batch, w.heads, w.d_v), dtype=torch.float32,
                     device="cuda")
     stream = torch.cuda.current_stream()
+    kind = 0 if w.kind == "gdn" else 1
 
     def step(i):
         pl = pools[i % len(pools)]
         s = sets[i % len(sets)]
-        sq.sq_decode_step(plan, pl["dev_plan"], pl["pool"], w.n_slots, slots_dev, w.batch,
-                          s["q"], s["k"], s["v"], s["beta"], s["gate"], y[i % len(sets)],
-                          stream)
+        if dense:
+            sq.sq_dense_step(kind, w.heads, w.d_k, w.d_v, pl["pool"], w.n_slots, slots_dev,
+                             w.batch, s["q"], s["k"], s["v"], s["beta"], s["gate"],
+                             y[i % len(sets)], stream)
+        else:
+            sq.sq_decode_step(plan, pl["dev_plan"], pl["pool"], w.n_slots, slots_dev, w.batch,
+                              s["q"], s["k"], s["v"], s["beta"], s["gate"], y[i % len(sets)],
+                              stream)
 
     for i in range(args.warmup):
         step(i)
@@ -255,8 +333,7 @@ def main():
         step(args.warmup + i)
     end.record(stream)
     torch.cuda.synchronize()
-    elapsed_ms = start.elapsed_time(end)
-    ms_per_step = elapsed_ms / args.steps
+    ms_per_step = start.elapsed_time(end) / args.steps
 
     # per-launch durations with events on the launch stream (second pass)
     n_ev = min(args.steps, 64)
@@ -268,51 +345,30 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return {"desc": desc, "pools": pools, "slots": slots, "ms_per_step": ms_per_step,
+            "launch_ms": launch_ms, "abytes": algorithmic_bytes(desc, w)}
 
-    abytes = algorithmic_bytes(desc, w)
-    family = "window" if w.mode == "window" else w.kind
-    gbs_step = abytes / (ms_per_step * 1e-3) / 1e9
-    gbs_kernel = abytes / (launch_ms * 1e-3) / 1e9
-    out = {
-        "metric": METRIC,
-        "value": 1e3 / ms_per_step,
-        "unit": "steps/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "n_slots": w.n_slots,
-                   "heads": w.heads, "d_k": w.d_k, "d_v": w.d_v, "mode": w.mode,
-                   "kind": w.kind, "nominal_bits": w.nominal_bits if w.mode == "step" else
-                   (w.bits if w.mode == "uniform" else 8),
-                   "unit_bits_histogram": (None if desc["unit_bits"] is None else
-                                           {str(b): int(c) for b, c in zip(
-                                               *np.unique(desc["unit_bits"], return_counts=True))}),
-                   "slot_bytes": desc["slot_bytes"], "layers_rotated": args.layers,
-                   "input_sets": args.input_sets, "algorithmic_bytes_per_step": abytes,
-                   "state_gbs": gbs_step, "pct_of_hbm_peak": 100.0 * gbs_step / HBM_PEAK_GBS},
-        "roofline": {"bound": "hbm", "achieved": gbs_kernel, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": gbs_kernel / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w.name, family),
-                     "kernel": KERNEL[w.mode if w.kind == "gdn" else "kda"],
-                     "kernel_source_sha256_16": kernel_source_hash(family),
-                     "launch_ms": launch_ms, "bytes_per_launch": abytes,
-                     "launch": "one sq_decode_step call (all its kernel launches), HIP events "
-                               "on the launch stream"},
-    }
-    if not args.no_cpu:
-        torch.cuda.synchronize()
-        sb = desc["slot_bytes"]
-        pb = pools[0]["pool"]
-        s0 = int(slots[0])
-        host = pb[s0 * sb:(s0 + 1) * sb].cpu().numpy().tobytes()
-        out["cpu_baseline"] = cpu_baseline(w, desc, host, slots, args.cpu_seconds)
-    print(json.dumps(out))
+
+def same_hardware(sq, args, value: float) -> dict:
+    """The pool workload's shape (same batch, slots, heads, d, inputs and
+    timing protocol) with the fp32 state kept dense, and with uniform rowwise
+    INT4: the denominators of the packed path's speed-up on this GPU."""
+    import torch
+    from synth import inputs as SI
+    res = {}
+    for key, name in (("fp32_dense", "gdn_pool_fp32"), ("uniform_int4", "gdn_pool_int4")):
+        w = SI.workload(name)
+        m = measure(sq, w, args)
+        res[key] = {"workload": name, "steps_per_s": 1e3 / m["ms_per_step"],
+                    "ms_per_step": m["ms_per_step"], "launch_ms": m["launch_ms"],
+                    "algorithmic_bytes_per_step": m["abytes"],
+                    "achieved_gbs": m["abytes"] / (m["launch_ms"] * 1e-3) / 1e9,
+                    "kernel": KERNEL[w.mode]}
+        del m
+        torch.cuda.empty_cache()
+    res["speedup_vs_fp32_dense"] = value / res["fp32_dense"]["steps_per_s"]
+    res["speedup_vs_uniform_int4"] = value / res["uniform_int4"]["steps_per_s"]
+    return res
 
 
 if __name__ == "__main__":

@@ -40,7 +40,7 @@ _STREAM_STATIC = 3
 class Workload:
     name: str
     kind: str            # "gdn" (scalar gate per head) or "kda" (gate per key row)
-    mode: str            # "uniform" | "step" | "window"
+    mode: str            # "uniform" | "step" | "window" | "dense" (fp32 state, no codec)
     batch: int           # live requests per decode step
     n_slots: int         # slots in the state pool
     heads: int
@@ -91,6 +91,15 @@ WORKLOADS: Dict[str, Workload] = {
         name="gdn_pool_step4", kind="gdn", mode="step", batch=512, n_slots=1024, heads=48,
         d_k=128, d_v=128, steps=256, seed=3, nominal_bits=4.0, cand_bits=(2, 4, 6, 8),
         pivot_frac=0.0139, half_life=64.0),
+    # the pool workload's shape with the fp32 state kept dense (no codec): the
+    # same-hardware denominator of the packed path's speed-up
+    "gdn_pool_fp32": Workload(
+        name="gdn_pool_fp32", kind="gdn", mode="dense", batch=512, n_slots=1024, heads=48,
+        d_k=128, d_v=128, steps=256, seed=3, half_life=64.0),
+    # the pool workload's shape with uniform rowwise INT4 (absmax, one FP16 scale per key row)
+    "gdn_pool_int4": Workload(
+        name="gdn_pool_int4", kind="gdn", mode="uniform", batch=512, n_slots=1024, heads=48,
+        d_k=128, d_v=128, steps=256, seed=3, bits=4, half_life=64.0),
     # per-window variant: INT8 boundary + FP32 records, p = 16
     "gdn_window16": Workload(
         name="gdn_window16", kind="gdn", mode="window", batch=256, n_slots=256, heads=32,

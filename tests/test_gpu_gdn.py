@@ -247,17 +247,14 @@ def test_dense_fp32_step(kind):
     assert np.linalg.norm(Sh - ref) <= 1e-5 * np.linalg.norm(ref)
 
 
-def test_full_size_gdn_pool_sampled():
-    """The 512-of-1024-slot, 48-head, nominal 4-bit pool at full size, in the
-    launch configuration the bench times: 3 steps, 24 sampled tiles (including
-    every width and the pivot head) compared teacher-forced on the last."""
+def _full_size_pool_sampled(plan, extra_tiles):
+    """The 512-of-1024-slot, 48-head pool shape at full size, in the launch
+    configuration the bench times: 8 fp32 dense warm-up steps on the GPU, pack,
+    3 decode steps, 24 random tiles plus `extra_tiles` compared teacher-forced
+    on the last."""
     import torch
     rng = np.random.default_rng(33)
     w = SI.workload("gdn_pool_step4")
-    bits = np.full(48, 4)
-    bits[[5, 29]] = 2
-    bits[17] = 16
-    plan = sq.sq_plan_create_step(sq.SQ_KIND_GDN, 48, 128, 128, bits, _impact(rng, 48, 128))
     pool = Pool(plan, w.n_slots)
     slots = SI.slot_ids(w)
     # a state with the warm-up's scale: 8 fp32 dense steps on the GPU from S = 0
@@ -272,8 +269,9 @@ def test_full_size_gdn_pool_sampled():
     pool.pack(sdev, S[sdev.long()].contiguous(), w.batch)
     del S
     sample = [(int(b), int(h)) for b, h in zip(rng.choice(w.batch, 24), rng.choice(48, 24))]
-    sample += [(3, 17), (100, 5), (511, 29)]
+    sample += extra_tiles
     desc = oracle_desc(pool.desc)
+    wts = pool.desc["w"]
     for t in range(3):
         inp = SI.step_inputs(w, t, params)
         before = {b: pool.slot_bytes_of(int(slots[b])) for b, _ in sample} if t == 2 else None
@@ -285,6 +283,64 @@ def test_full_size_gdn_pool_sampled():
         after = pool.slot_bytes_of(int(slots[b]))
         check_decode_head(f"b {b} h {h}", desc, h, pool.head_bytes(before[b], h),
                           pool.head_bytes(after, h), head_inputs(inp, b, h),
-                          yh[b, h].astype(np.float64), pool.desc["w"][h].astype(np.float64), rep)
+                          yh[b, h].astype(np.float64),
+                          None if wts is None else wts[h].astype(np.float64), rep)
     print("adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
     rep.assert_ok()
+
+
+def test_full_size_gdn_pool_sampled():
+    """Nominal 4-bit STEP at the pool shape: 45 4-bit heads in their own
+    launch, two 2-bit heads and the FP16 pivot head in the merged launch."""
+    rng = np.random.default_rng(34)
+    bits = np.full(48, 4)
+    bits[[5, 29]] = 2
+    bits[17] = 16
+    plan = sq.sq_plan_create_step(sq.SQ_KIND_GDN, 48, 128, 128, bits, _impact(rng, 48, 128))
+    _full_size_pool_sampled(plan, [(3, 17), (100, 5), (511, 29)])
+
+
+def test_full_size_uniform_int4_pool_sampled():
+    """Uniform rowwise INT4 (the same-hardware baseline) at the pool shape."""
+    _full_size_pool_sampled(sq.sq_plan_create_uniform(48, 128, 128, 4),
+                            [(0, 0), (511, 47), (255, 20)])
+
+
+def test_full_size_fp32_dense_pool_sampled():
+    """The fp32 dense step (the other same-hardware baseline) at the pool
+    shape, in place over the 1024-slot pool: 8 warm-up steps, then one step
+    checked on sampled tiles against the float64 recurrence started from the
+    GPU's state, and untouched slots checked unchanged."""
+    import torch
+    rng = np.random.default_rng(35)
+    w = SI.workload("gdn_pool_fp32")
+    slots = SI.slot_ids(w)
+    S = torch.zeros((w.n_slots, 48, 128, 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((w.batch, 48, 128), dtype=torch.float32, device="cuda")
+    sdev = to_dev(slots)
+    params = SI.gate_params(w)
+    for t in range(8):
+        d = inputs_dev(SI.warmup_inputs(w, t, params))
+        sq.sq_dense_step(0, 48, 128, 128, S, w.n_slots, sdev, w.batch, d["q"], d["k"], d["v"],
+                         d["beta"], d["gate"], y)
+    sample = [(int(b), int(h)) for b, h in zip(rng.choice(w.batch, 24), rng.choice(48, 24))]
+    sample += [(0, 0), (511, 47)]
+    torch.cuda.synchronize()
+    before = {(b, h): S[int(slots[b]), h].cpu().numpy().astype(np.float64) for b, h in sample}
+    idle = int(np.setdiff1d(np.arange(w.n_slots), slots)[0])
+    idle_before = S[idle].cpu().numpy()
+    inp = SI.step_inputs(w, 0, params)
+    d = inputs_dev(inp)
+    sq.sq_dense_step(0, 48, 128, 128, S, w.n_slots, sdev, w.batch, d["q"], d["k"], d["v"],
+                     d["beta"], d["gate"], y)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    for b, h in sample:
+        x = {k: inp[k][b, h].astype(np.float64) for k in ("q", "k", "v")}
+        dvec = R.gate_vector(np.float64(inp["gate"][b, h]), "gdn", 128)
+        ref, yr = R.dense_step(before[(b, h)][None], x["q"][None], x["k"][None], x["v"][None],
+                               np.array([inp["beta"][b, h]], np.float64), dvec[None])
+        got = S[int(slots[b]), h].cpu().numpy()
+        assert np.linalg.norm(got - ref[0]) <= 1e-5 * np.linalg.norm(ref[0]), (b, h)
+        assert np.linalg.norm(yh[b, h] - yr[0]) <= 1e-5 * np.linalg.norm(yr[0]), (b, h)
+    assert np.array_equal(S[idle].cpu().numpy(), idle_before)
