@@ -30,7 +30,8 @@ Specification in brief:
 * window head: int32 l at byte 0 (bytes 4..15 zero), float32 alpha[p] at
   byte 16, INT8 Z [d_k, d_v] (blocked order) at round_up(16 + 4p, 128), then
   float32 C[d_k],
-  float32 B[d_v], float32 K~[p, d_k], float32 U[p, d_v].
+  float32 B[d_v], float32 K~[p, d_k], float32 U[p, d_v]; with r compensator
+  pairs, then FP16 K~c[r, d_k] and FP16 U~c[r, d_v].
 """
 from __future__ import annotations
 
@@ -88,7 +89,10 @@ def head_fields(desc: dict, h: int) -> Dict[str, int]:
         f["B"] = f["C"] + 4 * d_k
         f["K"] = f["B"] + 4 * d_v
         f["U"] = f["K"] + 4 * p * d_k
-        end = f["U"] + 4 * p * d_v
+        r = int(desc.get("rank", 0))
+        f["Kc"] = f["U"] + 4 * p * d_v
+        f["Uc"] = f["Kc"] + 2 * r * d_k
+        end = f["Uc"] + 2 * r * d_v
     else:
         raise ValueError(mode)
     f["used"] = end
@@ -223,6 +227,10 @@ def pack_head(desc: dict, h: int, st: dict) -> bytes:
         out[f["B"]:f["B"] + 4 * d_v] = np.asarray(st["B"], "<f4").tobytes()
         out[f["K"]:f["K"] + 4 * p * d_k] = np.asarray(st["kt"], "<f4").tobytes()
         out[f["U"]:f["U"] + 4 * p * d_v] = np.asarray(st["u"], "<f4").tobytes()
+        r = int(desc.get("rank", 0))
+        if r:
+            out[f["Kc"]:f["Kc"] + 2 * r * d_k] = _f16_bytes(np.asarray(st["Kc"]).reshape(-1))
+            out[f["Uc"]:f["Uc"] + 2 * r * d_v] = _f16_bytes(np.asarray(st["Uc"]).reshape(-1))
     return bytes(out)
 
 
@@ -277,6 +285,10 @@ def parse_head(desc: dict, h: int, buf: bytes) -> dict:
             np.float64).reshape(p, d_k)
         st["u"] = np.frombuffer(buf[f["U"]:f["U"] + 4 * p * d_v], "<f4").astype(
             np.float64).reshape(p, d_v)
+        r = int(desc.get("rank", 0))
+        if r:
+            st["Kc"] = _f16(buf[f["Kc"]:f["Kc"] + 2 * r * d_k]).reshape(r, d_k)
+            st["Uc"] = _f16(buf[f["Uc"]:f["Uc"] + 2 * r * d_v]).reshape(r, d_v)
     return st
 
 
@@ -303,5 +315,7 @@ def state_from_encoding(desc: dict, h: int, enc: dict, row_bits: Optional[np.nda
     if desc["mode"] == "uniform":
         return {"z": enc["z"], "s": enc["s"]}
     if desc["mode"] == "window":
-        return {k: enc[k] for k in ("Z", "C", "B", "ell", "alpha", "kt", "u")}
+        keys = ("Z", "C", "B", "ell", "alpha", "kt", "u") + (
+            ("Kc", "Uc") if int(desc.get("rank", 0)) else ())
+        return {k: enc[k] for k in keys}
     return {"z": enc["z"], "r": enc["r"], "c": enc["c"], "h": enc["h"]}

@@ -13,12 +13,31 @@ u_i = v_i - S_{i-1}^T (alpha_i k_i); the token's output is o_i = S_i^T q_i
 (Sec. 2.1 Eq. 1).  The per-token loop of Sec. 2.6 computes u_i, appends the
 record, emits o_i and rebuilds the dense state when the window holds p
 records; the rebuilt state is re-encoded with the smoothed INT8 quantizer
-(Sec. 2.5, appendix B.3) and the window restarts.  Compensator tokens
-(Sec. 2.4) are not part of this variant.
+(Sec. 2.5, appendix B.3) and the window restarts.
+
+Compensator tokens (Sec. 2.4, Eqs. 5-7 and 10), rank r > 0: the boundary is
+S_hat_0 = C dequant(R_hat) + K~c U~c^T with r FP16 factor pairs (k~c_h, u~c_h).
+They enter a window with identity decay and then decay with the boundary, so
+
+    S_l = Gamma_{1:l} (C dequant(R_hat) + K~c U~c^T) + sum_j Gamma_{j+1:l} k~_j u_j^T,
+    S_l^T x = dequant(R_hat)^T C Gamma_{1:l} x + U~c (K~c^T Gamma_{1:l} x)
+              + sum_j u_j (k~_j . Gamma_{j+1:l} x).
+
+At a rebuild the old factors are part of S_p; a new rank-r fit by power
+iteration replaces them and only the residual R = S_p - K~c U~c^T is smoothed
+and quantized.  The pages fix the objective (the Frobenius-optimal rank-r
+outer-product sum), that it is reached by power iteration rather than an
+exact decomposition, the rank and the FP16 storage; the rest is this
+oracle's reading (``lowrank_fit``): the r pairs are fitted one after another,
+each from the residual left by the ones before, with a fixed number of
+iterations started from that pair's previous value u~c_h (a freshly packed
+state starts from the all-ones vector), and each pair is rounded to FP16
+before it is taken out of the residual, so the stored factors are exactly
+what was removed.
 
 Storage precision follows the layout: records and the boundary scales are
 float32, so u_i and beta_i k_i are rounded to float32 when recorded and every
-later use reads the rounded value.
+later use reads the rounded value; compensator factors are binary16.
 """
 from __future__ import annotations
 
@@ -27,16 +46,94 @@ from typing import List
 import numpy as np
 
 from . import quantizers as Q
-from .numerics import fp32
+from .numerics import FP16_MAX, fp16, fp32
 
 
-def new_window_state(S_init: np.ndarray, p: int) -> dict:
-    """Boundary encoding of an initial state, empty window."""
+def fp16_value(x) -> np.ndarray:
+    """Binary16 round-to-nearest-even of a signed value, saturating at the
+    largest finite binary16 magnitude (compensator factors)."""
+    return fp16(np.clip(np.asarray(x, dtype=np.float64), -FP16_MAX, FP16_MAX))
+
+
+def lowrank_fit(M: np.ndarray, rank: int, iters: int, init=None, exact: bool = False,
+                adopt=None):
+    """Rank-`rank` outer-product fit of M by power iteration (Sec. 2.4, Eqs. 5-6).
+
+    Pair h is fitted to the residual left by pairs 0..h-1: starting from
+    b = init[h] (the all-ones vector when init is None or init[h] is zero),
+    `iters` times a = M b / |M b|, b = M^T a; then with sigma = |b| the pair is
+    k~ = sqrt(sigma) a, u~ = b / sqrt(sigma), so k~ u~^T = a (M^T a)^T is the
+    best rank-one fit along a.  A start with M b = 0 (M = 0 in particular)
+    gives a zero pair.  Unless `exact`, the pair is rounded to FP16 before it
+    is subtracted.  `adopt(h, k, u)` (teacher-forced parity) may replace the
+    pair that is subtracted and stored.  Returns (K [rank, d_k], U [rank, d_v],
+    residual)."""
+    Rm = np.array(M, dtype=np.float64, copy=True)
+    d_k, d_v = Rm.shape
+    K = np.zeros((rank, d_k))
+    U = np.zeros((rank, d_v))
+    for h in range(rank):
+        if init is not None and np.any(np.asarray(init[h]) != 0):
+            b = np.asarray(init[h], dtype=np.float64)
+        else:
+            b = np.ones(d_v)
+        a = None
+        for _ in range(iters):
+            a = Rm @ b
+            na = float(np.sqrt(a @ a))
+            if na == 0.0:
+                a = None
+                break
+            a = a / na
+            b = Rm.T @ a
+        k = np.zeros(d_k)
+        u = np.zeros(d_v)
+        if a is not None:
+            sigma = float(np.sqrt(b @ b))
+            if sigma > 0.0:
+                sq = np.sqrt(sigma)
+                k, u = sq * a, b / sq
+        if not exact:
+            k, u = fp16_value(k), fp16_value(u)
+        if adopt is not None:
+            k, u = adopt(h, k, u)
+        K[h], U[h] = k, u
+        Rm = Rm - np.outer(k, u)
+    return K, U, Rm
+
+
+def encode_boundary(S: np.ndarray, rank: int = 0, iters: int = 4, init=None,
+                    exact: bool = False, adopt=None) -> dict:
+    """Boundary of a dense state: compensator fit (rank > 0), then the
+    smoothed INT8 encoding of the residual (identity when `exact`)."""
+    d_k, d_v = S.shape
+    if rank > 0:
+        Kc, Uc, Rm = lowrank_fit(S, rank, iters, init, exact, adopt)
+    else:
+        Kc, Uc, Rm = np.zeros((0, d_k)), np.zeros((0, d_v)), np.asarray(S, dtype=np.float64)
+    if exact:
+        return {"S0": Rm.copy(), "Kc": Kc, "Uc": Uc}
+    enc = Q.quantize_window(Rm)
+    return {"Z": enc["Z"], "C": enc["C"], "B": enc["B"], "pre_z": enc["pre_z"],
+            "Kc": Kc, "Uc": Uc, "R": Rm}
+
+
+def boundary_residual(st: dict) -> np.ndarray:
+    """C dequant(R_hat) (or the exact residual of an `exact` state)."""
+    if "S0" in st:
+        return st["S0"]
+    return Q.dequant_window(st["Z"], st["C"], st["B"])
+
+
+def new_window_state(S_init: np.ndarray, p: int, rank: int = 0, iters: int = 4,
+                     exact: bool = False) -> dict:
+    """Boundary encoding of an initial state, empty window (a pack starts the
+    compensator fit from the all-ones vector)."""
     d_k, d_v = S_init.shape[-2:]
-    enc = Q.quantize_window(S_init)
-    return {"Z": enc["Z"], "C": enc["C"], "B": enc["B"], "ell": 0,
-            "alpha": np.zeros(p), "kt": np.zeros((p, d_k)), "u": np.zeros((p, d_v)),
-            "pre_z": enc["pre_z"]}
+    enc = encode_boundary(S_init, rank, iters, None, exact)
+    st = {k: v for k, v in enc.items() if k != "R"}
+    st.update(ell=0, alpha=np.zeros(p), kt=np.zeros((p, d_k)), u=np.zeros((p, d_v)))
+    return st
 
 
 def _gamma(alphas: np.ndarray, a: int, b: int) -> float:
@@ -46,67 +143,96 @@ def _gamma(alphas: np.ndarray, a: int, b: int) -> float:
     return float(np.prod(alphas[a - 1:b]))
 
 
-def window_readout(S0: np.ndarray, alphas, kt, u, n: int, x: np.ndarray) -> np.ndarray:
-    """S_n^T x from the boundary state and the first n records."""
-    out = S0.T @ (_gamma(alphas, 1, n) * x)
+def _comp(Kc, Uc):
+    if Kc is None or len(Kc) == 0:
+        return None
+    return np.asarray(Kc, dtype=np.float64), np.asarray(Uc, dtype=np.float64)
+
+
+def window_readout(S0: np.ndarray, alphas, kt, u, n: int, x: np.ndarray,
+                   Kc=None, Uc=None) -> np.ndarray:
+    """S_n^T x from the boundary residual S0, the compensators and the first
+    n records (Eq. 10)."""
+    gx = _gamma(alphas, 1, n) * x
+    out = S0.T @ gx
+    c = _comp(Kc, Uc)
+    if c is not None:
+        out = out + c[1].T @ (c[0] @ gx)
     for j in range(1, n + 1):
         out = out + u[j - 1] * float(kt[j - 1] @ (_gamma(alphas, j + 1, n) * x))
     return out
 
 
-def window_dense(S0: np.ndarray, alphas, kt, u, n: int) -> np.ndarray:
-    """S_n = Gamma_{1:n} S_hat_0 + sum_j Gamma_{j+1:n} k~_j u_j^T."""
-    S = _gamma(alphas, 1, n) * S0
+def window_dense(S0: np.ndarray, alphas, kt, u, n: int, Kc=None, Uc=None) -> np.ndarray:
+    """S_n = Gamma_{1:n} (S0 + K~c U~c^T) + sum_j Gamma_{j+1:n} k~_j u_j^T (Eq. 7)."""
+    base = np.asarray(S0, dtype=np.float64)
+    c = _comp(Kc, Uc)
+    if c is not None:
+        base = base + c[0].T @ c[1]
+    S = _gamma(alphas, 1, n) * base
     for j in range(1, n + 1):
         S = S + _gamma(alphas, j + 1, n) * np.outer(kt[j - 1], u[j - 1])
     return S
 
 
-def window_step(st: dict, q, k, v, beta: float, alpha: float, p: int) -> dict:
+def window_step(st: dict, q, k, v, beta: float, alpha: float, p: int, iters: int = 4,
+                exact: bool = False, adopt=None) -> dict:
     """One token on one (slot, head) window state.  Returns the output o_i,
-    the record written and the new state (a fresh dict)."""
+    the record written and the new state (a fresh dict).  The compensator
+    rank is that of st["Kc"] (absent or empty: none).  `exact` keeps records
+    and factors unrounded and the boundary unquantized."""
     ell = int(st["ell"])
     i = ell + 1
-    S0 = Q.dequant_window(st["Z"], st["C"], st["B"])
+    S0 = boundary_residual(st)
+    Kc, Uc = st.get("Kc"), st.get("Uc")
+    rank = 0 if Kc is None else len(Kc)
+    rnd = (lambda x: np.asarray(x, dtype=np.float64)) if exact else fp32
     alphas = st["alpha"].copy()
     kt = st["kt"].copy()
     u = st["u"].copy()
     alphas[i - 1] = alpha
-    prev = window_readout(S0, alphas, kt, u, i - 1, alpha * k)
-    u_i = fp32(v - prev)
-    kt[i - 1] = fp32(beta * k)
+    prev = window_readout(S0, alphas, kt, u, i - 1, alpha * k, Kc, Uc)
+    u_i = rnd(v - prev)
+    kt[i - 1] = rnd(beta * k)
     u[i - 1] = u_i
-    o = window_readout(S0, alphas, kt, u, i, q)
+    o = window_readout(S0, alphas, kt, u, i, q, Kc, Uc)
     new = dict(st, alpha=alphas, kt=kt, u=u, ell=i)
     flushed = None
     if i == p:
-        flushed = Q.quantize_window(window_dense(S0, alphas, kt, u, p))
-        new.update(Z=flushed["Z"], C=flushed["C"], B=flushed["B"], ell=0,
-                   pre_z=flushed["pre_z"])
+        flushed = encode_boundary(window_dense(S0, alphas, kt, u, p, Kc, Uc), rank, iters,
+                                  Uc, exact, adopt)
+        new.update({kk: vv for kk, vv in flushed.items() if kk not in ("R",)})
+        new["ell"] = 0
     return {"o": o, "u": u_i, "kt": kt[i - 1], "state": new, "flushed": flushed,
             "S0": S0}
 
 
-def window_flush(st: dict, p: int) -> dict:
+def window_flush(st: dict, p: int, iters: int = 4, exact: bool = False, adopt=None) -> dict:
     """Rebuild and re-encode a window holding 0 < l < p records (no-op at l = 0)."""
     ell = int(st["ell"])
     if ell == 0:
         return dict(st)
-    S0 = Q.dequant_window(st["Z"], st["C"], st["B"])
-    enc = Q.quantize_window(window_dense(S0, st["alpha"], st["kt"], st["u"], ell))
-    return dict(st, Z=enc["Z"], C=enc["C"], B=enc["B"], ell=0, pre_z=enc["pre_z"])
+    Kc, Uc = st.get("Kc"), st.get("Uc")
+    rank = 0 if Kc is None else len(Kc)
+    enc = encode_boundary(window_dense(boundary_residual(st), st["alpha"], st["kt"], st["u"],
+                                       ell, Kc, Uc), rank, iters, Uc, exact, adopt)
+    new = dict(st, ell=0)
+    new.update({kk: vv for kk, vv in enc.items() if kk != "R"})
+    return new
 
 
 def window_state_dense(st: dict) -> np.ndarray:
-    S0 = Q.dequant_window(st["Z"], st["C"], st["B"])
-    return window_dense(S0, st["alpha"], st["kt"], st["u"], int(st["ell"]))
+    return window_dense(boundary_residual(st), st["alpha"], st["kt"], st["u"], int(st["ell"]),
+                        st.get("Kc"), st.get("Uc"))
 
 
-def window_run(S_init: np.ndarray, inputs: List[dict], p: int) -> List[dict]:
-    st = new_window_state(S_init, p)
+def window_run(S_init: np.ndarray, inputs: List[dict], p: int, rank: int = 0, iters: int = 4,
+               exact: bool = False) -> List[dict]:
+    st = new_window_state(S_init, p, rank, iters, exact)
     outs = []
     for inp in inputs:
-        r = window_step(st, inp["q"], inp["k"], inp["v"], inp["beta"], inp["alpha"], p)
+        r = window_step(st, inp["q"], inp["k"], inp["v"], inp["beta"], inp["alpha"], p, iters,
+                        exact)
         outs.append(r)
         st = r["state"]
     return outs

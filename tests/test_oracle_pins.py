@@ -411,9 +411,123 @@ def test_window_boundary_bytes():
     f = L.head_fields({"mode": "window", "heads": 1, "d_k": d_k, "d_v": d_v, "p": p}, 0)
     base = (f["K"] - f["Z"]) / (d_k * d_v)
     assert base == g["boundary_bytes_per_element_r0"]
-    assert base + 2 * 4 * (d_k + d_v) / (d_k * d_v) == g["boundary_bytes_per_element_r4"]
     records = (f["used"] - f["K"]) + 4 * p            # K~ and U arrays plus alpha[p]
     assert records == 2 * g["record_buffer_bytes_fp16"]
+    # with r = 4 compensator pairs stored in the head (FP16 K~c, U~c)
+    f4 = L.head_fields({"mode": "window", "heads": 1, "d_k": d_k, "d_v": d_v, "p": p,
+                        "rank": 4}, 0)
+    boundary4 = (f4["K"] - f4["Z"]) + (f4["used"] - f4["Kc"])
+    assert boundary4 / (d_k * d_v) == g["boundary_bytes_per_element_r4"]
+    assert f4["Kc"] - f4["K"] == records - 4 * p
+
+
+# ------------------------------------------------- compensator tokens (N2)
+def _spectral(rng, d_k, d_v, s):
+    """A matrix with the given singular values (distinct) and its factors."""
+    Uo, _ = np.linalg.qr(rng.standard_normal((d_k, d_k)))
+    Vo, _ = np.linalg.qr(rng.standard_normal((d_v, d_v)))
+    n = len(s)
+    return (Uo[:, :n] * s) @ Vo[:, :n].T, Uo[:, :n], Vo[:, :n]
+
+
+def test_lowrank_rank1_limit_is_top_singular_pair(rng):
+    """Sec. 2.4, Eq. 5: with many iterations the rank-one power fit reaches the
+    Frobenius-optimal rank-one term sigma_1 u_1 v_1^T (Eckart-Young), split
+    evenly between the two factors."""
+    s = np.array([9.0, 4.0, 2.5, 1.0, 0.3])
+    M, Uo, Vo = _spectral(rng, 24, 17, s)
+    K, U, Rm = W.lowrank_fit(M, 1, 300, exact=True)
+    np.testing.assert_allclose(np.outer(K[0], U[0]), s[0] * np.outer(Uo[:, 0], Vo[:, 0]),
+                               rtol=0, atol=1e-12 * s[0])
+    assert abs(np.linalg.norm(K[0]) - np.sqrt(s[0])) < 1e-12
+    assert abs(np.linalg.norm(U[0]) - np.sqrt(s[0])) < 1e-12
+    assert abs(np.linalg.norm(Rm) ** 2 - np.sum(s[1:] ** 2)) < 1e-10
+
+
+def test_lowrank_rank_r_is_truncated_decomposition(rng):
+    """Sec. 2.4, Eq. 6: r pairs fitted one after another on the residual reach
+    the best rank-r approximation (the truncated singular decomposition) and
+    leave the energy of the remaining directions."""
+    s = np.array([12.0, 7.0, 4.0, 2.0, 0.9, 0.4, 0.1])
+    M, Uo, Vo = _spectral(rng, 20, 30, s)
+    K, U, Rm = W.lowrank_fit(M, 4, 400, exact=True)
+    best = (Uo[:, :4] * s[:4]) @ Vo[:, :4].T
+    np.testing.assert_allclose(K.T @ U, best, rtol=0, atol=1e-10 * s[0])
+    np.testing.assert_allclose(Rm, M - best, rtol=0, atol=1e-10 * s[0])
+
+
+def test_lowrank_exact_on_rank1_and_zero(rng):
+    """A rank-one matrix is fitted exactly after one iteration from any start
+    not orthogonal to its row vector; a zero matrix gives zero pairs."""
+    a, b = rng.standard_normal(9), rng.standard_normal(6)
+    K, U, Rm = W.lowrank_fit(np.outer(a, b), 2, 1, exact=True)
+    np.testing.assert_allclose(np.outer(K[0], U[0]), np.outer(a, b), rtol=0, atol=1e-13)
+    assert np.abs(Rm).max() < 1e-13
+    assert np.abs(np.outer(K[1], U[1])).max() < 1e-13  # only rounding noise left to fit
+    K, U, Rm = W.lowrank_fit(np.zeros((5, 7)), 3, 4)
+    assert not np.any(K) and not np.any(U) and not np.any(Rm)
+
+
+def test_lowrank_start_vector_is_used(rng):
+    """The fit starts from init[h]: started at the exact top right singular
+    vector, one iteration already gives the top pair (from the all-ones start
+    it does not)."""
+    s = np.array([5.0, 4.5, 1.0])
+    M, Uo, Vo = _spectral(rng, 10, 8, s)
+    K, U, _ = W.lowrank_fit(M, 1, 1, init=Vo[:, :1].T, exact=True)
+    np.testing.assert_allclose(np.outer(K[0], U[0]), s[0] * np.outer(Uo[:, 0], Vo[:, 0]),
+                               rtol=0, atol=1e-12)
+    K1, U1, _ = W.lowrank_fit(M, 1, 1, exact=True)
+    assert np.abs(np.outer(K1[0], U1[0]) - s[0] * np.outer(Uo[:, 0], Vo[:, 0])).max() > 1e-3
+
+
+def test_lowrank_stored_pairs_are_what_was_removed(rng):
+    """Rounded to FP16, the stored pairs are exactly the terms taken out of the
+    residual: residual + sum_h k~c_h u~c_h^T reproduces the input."""
+    M = rng.standard_normal((16, 12)) * 3.0
+    K, U, Rm = W.lowrank_fit(M, 3, 4)
+    np.testing.assert_array_equal(K, K.astype(np.float16).astype(np.float64))
+    np.testing.assert_array_equal(U, U.astype(np.float16).astype(np.float64))
+    np.testing.assert_allclose(Rm + K.T @ U, M, rtol=0, atol=1e-13)
+
+
+def test_compensated_window_exact_with_identity_quantizer(rng):
+    """Sec. 2.4-2.5, Eqs. 7 and 10: with an identity boundary quantizer and
+    unrounded records and factors, the compensated window path (readouts,
+    rebuilds, refits across three windows) reproduces the step recurrence."""
+    d_k, d_v, p, r = 10, 7, 4, 2
+    S = rng.standard_normal((d_k, d_v))
+    st = W.new_window_state(S, p, r, 3, exact=True)
+    np.testing.assert_allclose(W.window_state_dense(st), S, rtol=0, atol=1e-12)
+    assert np.abs(st["Kc"]).max() > 0
+    for t in range(3 * p):
+        inp, dvec = draw(rng, d_k, d_v, "gdn")
+        res = W.window_step(st, inp["q"], inp["k"], inp["v"], inp["beta"], dvec[0], p, 3,
+                            exact=True)
+        S, y = R.dense_step(S, inp["q"], inp["k"], inp["v"], inp["beta"], dvec)
+        np.testing.assert_allclose(res["o"], y, rtol=0, atol=1e-11)
+        st = res["state"]
+        np.testing.assert_allclose(W.window_state_dense(st), S, rtol=0, atol=1e-11)
+    assert st["ell"] == 0
+
+
+def test_compensated_readout_matches_dense(rng):
+    """Eq. 10 term by term: boundary residual, compensators decaying with the
+    boundary, records with their own decay, equals (S_l)^T x of Eq. 7."""
+    d_k, d_v, p, r = 9, 11, 6, 3
+    S0 = rng.standard_normal((d_k, d_v))
+    Kc, Uc = rng.standard_normal((r, d_k)), rng.standard_normal((r, d_v))
+    alphas = rng.uniform(0.5, 1.0, p)
+    kt, u = rng.standard_normal((p, d_k)), rng.standard_normal((p, d_v))
+    x = rng.standard_normal(d_k)
+    for n in range(p + 1):
+        np.testing.assert_allclose(W.window_readout(S0, alphas, kt, u, n, x, Kc, Uc),
+                                   W.window_dense(S0, alphas, kt, u, n, Kc, Uc).T @ x,
+                                   rtol=0, atol=1e-12)
+    g = np.prod(alphas[:2])
+    manual = g * (S0 + Kc.T @ Uc) + alphas[1] * np.outer(kt[0], u[0]) + np.outer(kt[1], u[1])
+    np.testing.assert_allclose(W.window_dense(S0, alphas, kt, u, 2, Kc, Uc), manual,
+                               rtol=0, atol=1e-12)
 
 
 # ----------------------------------------------------------------- P10-P13
