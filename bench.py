@@ -46,6 +46,9 @@ def _plan(sq, w):
     if w.mode == "uniform":
         return sq.sq_plan_create_uniform(w.heads, w.d_k, w.d_v, w.bits)
     if w.mode == "window":
+        if w.comp_rank:
+            return sq.sq_plan_create_window_lowrank(w.heads, w.d_k, w.d_v, w.window, w.comp_rank,
+                                                    w.power_iters)
         return sq.sq_plan_create_window(w.heads, w.d_k, w.d_v, w.window)
     with open(os.path.join(ROOT, "tests", "golden", f"calib_{w.name}.json")) as f:
         st = json.load(f)
@@ -89,9 +92,9 @@ def kernel_source_hash(family: str) -> str:
 def algorithmic_bytes(desc, w) -> int:
     """Bytes one decode step must move: the packed state of every live slot
     read and written once (payload, no padding), q, k, v, beta, gate in, y out,
-    slot ids.  Window mode: the boundary and C, B are read, the records held
-    (mean (p-1)/2 per token) are read, one record is written, the boundary is
-    rewritten once per p tokens."""
+    slot ids.  Window mode: the boundary and C, B (and the compensator pairs)
+    are read, the records held (mean (p-1)/2 per token) are read, one record
+    is written, the boundary is rewritten once per p tokens."""
     B, H, dk, dv = w.batch, w.heads, w.d_k, w.d_v
     gate = B * H * (dk if w.kind == "kda" else 1) * 4
     io = B * H * (2 * dk + dv) * 4 + B * H * 4 + gate + B * H * dv * 4 + B * 4
@@ -100,7 +103,7 @@ def algorithmic_bytes(desc, w) -> int:
     if w.mode != "window":
         return 2 * B * desc["payload_bytes"] + io
     p = w.window
-    base = dk * dv + 4 * (dk + dv)
+    base = dk * dv + 4 * (dk + dv) + 2 * w.comp_rank * (dk + dv)
     rec = 4 * (dk + dv) + 4
     per_tile = base + rec * (p - 1) / 2.0 + rec + base / p + 16
     return int(B * H * per_tile) + io
@@ -159,7 +162,8 @@ def cpu_baseline(w, desc, pool_bytes: bytes, slots, budget_s: float) -> dict:
                 q, k, v = (inp[x][b, h].astype(np.float64) for x in ("q", "k", "v"))
                 beta = float(inp["beta"][b, h])
                 if w.mode == "window":
-                    r = OW.window_step(st, q, k, v, beta, float(inp["gate"][b, h]), w.window)
+                    r = OW.window_step(st, q, k, v, beta, float(inp["gate"][b, h]), w.window,
+                                       w.power_iters)
                     states[b][h] = r["state"]
                     tiles += 1
                     continue

@@ -64,8 +64,10 @@
  *               layout (b = 8) at byte round_up(16 + 4p, 128); then float32
  *               C[d_k] (key-row smoothing), float32 B[d_v] (value-column
  *               scales), float32 Kt[p][d_k] (records beta_i k_i), float32
- *               U[p][d_v] (records u_i).  Boundary state
- *               S0_aj = C_a (Z_aj / 127) B_j ([LQ] Sec. 2.5, App. B.3).
+ *               U[p][d_v] (records u_i); with r compensator pairs, then
+ *               FP16 Kc[r][d_k] and FP16 Uc[r][d_v].  Boundary state
+ *               S0_aj = C_a (Z_aj / 127) B_j + sum_h Kc[h][a] Uc[h][j]
+ *               ([LQ] Sec. 2.4-2.5, Eq. 7, App. B.3).
  *
  * All FP16 scales are stored after clamping to [2^-14, 65504] and rounding
  * to nearest even ([SQ] App. B.5 states this clamp for its INT6 baseline;
@@ -99,6 +101,8 @@ enum {
 enum { SQ_MODE_UNIFORM = 0, SQ_MODE_STEP = 1, SQ_MODE_WINDOW = 2 };
 enum { SQ_KIND_GDN = 0, SQ_KIND_KDA = 1 };
 #define SQ_PIVOT_BITS 16
+#define SQ_MAX_COMP_RANK 8      /* compensator pairs per window head            */
+#define SQ_MAX_POWER_ITERS 32   /* power iterations per compensator pair        */
 
 typedef struct sq_plan sq_plan; /* opaque host object owned by the library */
 
@@ -115,6 +119,8 @@ typedef struct {
   const int32_t* unit_bits; /* STEP: [n_units] width per unit, 16 = FP16 pivot   */
   const float* w;           /* STEP: [H*d_k] row impact factors; else NULL       */
   float window_c_floor;     /* window: smoothing floor                           */
+  int32_t window_rank;      /* window: compensator pairs per head (0 = none)     */
+  int32_t window_iters;     /* window: power iterations per compensator pair     */
 } sq_plan_desc;
 
 /* Calibration statistics, one entry per unit u (a GDN head, or a KDA key row
@@ -170,6 +176,23 @@ sq_status sq_plan_create_uniform(int32_t heads, int32_t d_k, int32_t d_v, int32_
 sq_status sq_plan_create_window(int32_t heads, int32_t d_k, int32_t d_v, int32_t p,
                                 float c_floor, sq_plan** out);
 
+/* Per-window variant with compensator tokens ([LQ] Sec. 2.4-2.5, Eqs. 5-7
+ * and 10): each head also keeps `rank` FP16 factor pairs (Kc[h], Uc[h]) that
+ * join the boundary (S0 = C (Z/127) B + Kc^T Uc) with identity decay and then
+ * decay with it; their readout term Uc (Kc Gamma x) rides with the records.
+ * At every rebuild (a full window, sq_window_flush) and at pack the pairs
+ * are refitted by power iteration on the dense state, one after another on
+ * the residual left by the earlier ones: from b = the pair's stored Uc[h]
+ * (the all-ones vector at pack, or when Uc[h] is zero), `power_iters` times
+ * a = M b / |M b|, b = M^T a; then Kc[h] = FP16(sqrt|b| a),
+ * Uc[h] = FP16(b / sqrt|b|), and M -= Kc[h] Uc[h]^T.  Only the residual is
+ * smoothed and quantised.  1 <= p <= 32, 0 <= rank <= SQ_MAX_COMP_RANK
+ * (rank 0 is sq_plan_create_window), 1 <= power_iters <= SQ_MAX_POWER_ITERS,
+ * and p <= 16 unless d_v = 128; SQ_EUNSUPPORTED otherwise. */
+sq_status sq_plan_create_window_lowrank(int32_t heads, int32_t d_k, int32_t d_v, int32_t p,
+                                        float c_floor, int32_t rank, int32_t power_iters,
+                                        sq_plan** out);
+
 sq_status sq_plan_query(const sq_plan* plan, sq_plan_desc* desc);
 sq_status sq_plan_destroy(sq_plan* plan);
 
@@ -200,7 +223,8 @@ sq_status sq_pool_pack(const sq_plan* plan, const void* dev_plan, void* pool,
 
 /* Dequantise the given slots into S_out[B][H][d_k][d_v] (fp32).  Window mode
  * returns the dense state of the open window, S_l = Gamma_{1:l} S0 +
- * sum_j Gamma_{j+1:l} Kt_j U_j^T ([LQ] Sec. 2.3, Eq. 4). */
+ * sum_j Gamma_{j+1:l} Kt_j U_j^T ([LQ] Sec. 2.3, Eq. 4; S0 includes the
+ * compensator pairs, Eq. 7). */
 sq_status sq_pool_unpack(const sq_plan* plan, const void* dev_plan, const void* pool,
                          int64_t n_slots, const int32_t* slots, int32_t batch,
                          float* S_out, hipStream_t stream);

@@ -25,7 +25,7 @@ SQ_PIVOT_BITS = 16
 
 EXPORTED = (
     "sq_calibrate_bits", "sq_plan_create_step", "sq_plan_create_uniform",
-    "sq_plan_create_window", "sq_plan_query", "sq_plan_destroy", "sq_plan_device_bytes",
+    "sq_plan_create_window", "sq_plan_create_window_lowrank", "sq_plan_query", "sq_plan_destroy", "sq_plan_device_bytes",
     "sq_plan_upload", "sq_pool_bytes", "sq_pool_init", "sq_pool_pack", "sq_pool_unpack",
     "sq_decode_step", "sq_window_flush", "sq_quantize_tiles", "sq_max_head_bytes",
     "sq_dense_step", "sq_last_error",
@@ -46,7 +46,8 @@ class _Desc(ctypes.Structure):
                 ("payload_bytes", ctypes.c_int64), ("analytic_bytes", ctypes.c_int64),
                 ("head_off", ctypes.POINTER(ctypes.c_int64)),
                 ("unit_bits", ctypes.POINTER(ctypes.c_int32)),
-                ("w", ctypes.POINTER(ctypes.c_float)), ("window_c_floor", ctypes.c_float)]
+                ("w", ctypes.POINTER(ctypes.c_float)), ("window_c_floor", ctypes.c_float),
+                ("window_rank", ctypes.c_int32), ("window_iters", ctypes.c_int32)]
 
 
 class _Stats(ctypes.Structure):
@@ -88,6 +89,7 @@ def lib() -> ctypes.CDLL:
             "sq_plan_create_step": [_I32, _I32, _I32, _I32, _P, _P, _PP],
             "sq_plan_create_uniform": [_I32, _I32, _I32, _I32, _PP],
             "sq_plan_create_window": [_I32, _I32, _I32, _I32, _F32, _PP],
+            "sq_plan_create_window_lowrank": [_I32, _I32, _I32, _I32, _F32, _I32, _I32, _PP],
             "sq_plan_query": [_P, ctypes.POINTER(_Desc)],
             "sq_plan_destroy": [_P],
             "sq_plan_device_bytes": [_P, _SZ],
@@ -177,6 +179,12 @@ def sq_plan_create_window(heads: int, d_k: int, d_v: int, p: int, c_floor: float
     return _new_plan(lib().sq_plan_create_window, heads, d_k, d_v, p, c_floor)
 
 
+def sq_plan_create_window_lowrank(heads: int, d_k: int, d_v: int, p: int, rank: int,
+                                  power_iters: int = 4, c_floor: float = 1e-6) -> Plan:
+    return _new_plan(lib().sq_plan_create_window_lowrank, heads, d_k, d_v, p, c_floor, rank,
+                     power_iters)
+
+
 def sq_plan_create_step(kind: int, heads: int, d_k: int, d_v: int, unit_bits, w) -> Plan:
     ub = np.ascontiguousarray(unit_bits, dtype=np.int32)
     ww = np.ascontiguousarray(w, dtype=np.float32)
@@ -208,7 +216,8 @@ def sq_plan_query(plan: Plan) -> dict:
     _check(lib().sq_plan_query(plan, ctypes.byref(d)))
     out = {k: getattr(d, k) for k in ("mode", "kind", "heads", "d_k", "d_v", "uniform_bits",
                                       "window", "n_units", "slot_bytes", "payload_bytes",
-                                      "analytic_bytes", "window_c_floor")}
+                                      "analytic_bytes", "window_c_floor", "window_rank",
+                                      "window_iters")}
     out["head_off"] = np.ctypeslib.as_array(d.head_off, (d.heads,)).copy()
     out["unit_bits"] = (np.ctypeslib.as_array(d.unit_bits, (d.n_units,)).copy()
                         if d.n_units else None)

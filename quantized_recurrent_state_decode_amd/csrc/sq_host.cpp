@@ -68,7 +68,8 @@ void finish_plan(sq_plan* P) {
       analytic += used;
     } else if (P->mode == SQ_MODE_WINDOW) {
       const long long z = round_up(16 + 4LL * P->p, 128);
-      used = z + (long long)dk * dv + 4LL * dk + 4LL * dv + 4LL * P->p * (dk + dv);
+      used = z + (long long)dk * dv + 4LL * dk + 4LL * dv + 4LL * P->p * (dk + dv) +
+             2LL * P->rank * (dk + dv);
       P->r_off[h] = (int)z;  // start of Z
       analytic += used;
     } else if (P->kind == SQ_KIND_GDN) {
@@ -141,6 +142,8 @@ DevPlan dev_view(const sq_plan* P, const void* dev) {
   d.dv = P->dv;
   d.ubits = P->ubits;
   d.p = P->p;
+  d.rank = P->rank;
+  d.iters = P->iters;
   d.c_floor = P->c_floor;
   d.slot_bytes = P->slot_bytes;
   d.max_head_bytes = P->max_head_bytes;
@@ -264,8 +267,9 @@ extern "C" sq_status sq_plan_create_uniform(int32_t heads, int32_t d_k, int32_t 
   return ok();
 }
 
-extern "C" sq_status sq_plan_create_window(int32_t heads, int32_t d_k, int32_t d_v, int32_t p,
-                                           float c_floor, sq_plan** out) {
+extern "C" sq_status sq_plan_create_window_lowrank(int32_t heads, int32_t d_k, int32_t d_v,
+                                                   int32_t p, float c_floor, int32_t rank,
+                                                   int32_t power_iters, sq_plan** out) {
   if (!out) return fail(SQ_EINVAL, "out is null");
   *out = nullptr;
   sq_status s = check_dims(heads, d_k, d_v);
@@ -273,6 +277,16 @@ extern "C" sq_status sq_plan_create_window(int32_t heads, int32_t d_k, int32_t d
   if (p < 1 || p > 32) return fail(SQ_EUNSUPPORTED, "window length must be in [1, 32] (got %d)", p);
   if (!(c_floor > 0.0f) || !std::isfinite(c_floor))
     return fail(SQ_EINVAL, "smoothing floor must be positive and finite");
+  if (rank < 0 || rank > SQ_MAX_COMP_RANK)
+    return fail(SQ_EUNSUPPORTED, "compensator rank must be in [0, %d] (got %d)", SQ_MAX_COMP_RANK,
+                rank);
+  if (rank > 0 && (power_iters < 1 || power_iters > SQ_MAX_POWER_ITERS))
+    return fail(SQ_EUNSUPPORTED, "power iterations must be in [1, %d] (got %d)",
+                SQ_MAX_POWER_ITERS, power_iters);
+  // the kernel gives each compensator pair a lane after the record lanes of a
+  // row block (16 or 32 of them) among its d_v / 2 lanes
+  if (rank > 0 && (p <= 16 ? 16 : 32) + SQ_MAX_COMP_RANK > d_v / 2)
+    return fail(SQ_EUNSUPPORTED, "compensators with a window longer than 16 need d_v = 128");
   sq_plan* P = new (std::nothrow) sq_plan;
   if (!P) return fail(SQ_ENOMEM, "plan allocation");
   P->mode = SQ_MODE_WINDOW;
@@ -281,11 +295,18 @@ extern "C" sq_status sq_plan_create_window(int32_t heads, int32_t d_k, int32_t d
   P->dk = d_k;
   P->dv = d_v;
   P->p = p;
+  P->rank = rank;
+  P->iters = rank > 0 ? power_iters : 0;
   P->c_floor = c_floor;
   P->head_bits.assign(heads, 8);
   finish_plan(P);
   *out = P;
   return ok();
+}
+
+extern "C" sq_status sq_plan_create_window(int32_t heads, int32_t d_k, int32_t d_v, int32_t p,
+                                           float c_floor, sq_plan** out) {
+  return sq_plan_create_window_lowrank(heads, d_k, d_v, p, c_floor, 0, 0, out);
 }
 
 extern "C" sq_status sq_plan_create_step(int32_t kind, int32_t heads, int32_t d_k, int32_t d_v,
@@ -454,6 +475,8 @@ extern "C" sq_status sq_plan_query(const sq_plan* P, sq_plan_desc* d) {
   d->unit_bits = P->unit_bits.empty() ? nullptr : P->unit_bits.data();
   d->w = P->w.empty() ? nullptr : P->w.data();
   d->window_c_floor = P->c_floor;
+  d->window_rank = P->rank;
+  d->window_iters = P->iters;
   return ok();
 }
 

@@ -12,6 +12,7 @@
 // Device view of a plan: pointers into the caller-owned device table buffer.
 struct DevPlan {
   int mode, kind, H, dk, dv, ubits, p;
+  int rank, iters;            // window: compensator pairs, power iterations
   float c_floor;
   long long slot_bytes;
   int max_head_bytes;
@@ -30,6 +31,7 @@ struct DevPlan {
 
 struct sq_plan {
   int mode = 0, kind = 0, H = 0, dk = 0, dv = 0, ubits = 0, p = 0;
+  int rank = 0, iters = 0;
   float c_floor = 1e-6f;
   int n_units = 0;
   long long slot_bytes = 0, payload_bytes = 0, analytic_bytes = 0;

@@ -13,6 +13,16 @@
 // (Sec. 2.5, App. B.3): C_a = max(sqrt(mean_j |S_aj|), c_floor),
 // T = diag(C)^-1 S, B_j = max_a |T_aj|, Z = clamp(rne(127 T / B), +-127).
 //
+// Compensator tokens (Sec. 2.4-2.5, Eqs. 5-7, 10), rank r > 0: the boundary
+// also holds r FP16 pairs (kc_h, uc_h), S0 = C (Z/127) B + sum_h kc_h uc_h^T.
+// They decay with the boundary, so their readout term uc_h (kc_h . x) is
+// scaled like the boundary's and rides in spare lanes of the record dot
+// products.  A rebuild (and a pack) refits them by power iteration on the
+// register-resident dense state, pair after pair on the residual, from the
+// pair's previous uc_h (the all-ones vector at a pack or for a zero pair):
+// iters times a = M b / |M b|, b = M^T a; then kc = FP16(sqrt|b| a),
+// uc = FP16(b / sqrt|b|), M -= kc uc^T; the residual is what is quantized.
+//
 // Lanes own 2 columns x 32 rows of the INT8 boundary (blocked layout), so
 // S0^T x costs one fused multiply-add per element for each of the two read
 // vectors and the reduction over rows is lane-local plus one LDS combine.
@@ -25,7 +35,10 @@ using namespace sqk;
 
 namespace {
 
-template <int DK, int DV, int PM>
+constexpr int RM = SQ_MAX_COMP_RANK;  // compensator pairs per head, at most
+
+// RMX: compensator pairs the kernel variant can hold (0 or RM)
+template <int DK, int DV, int PM, int RMX>
 struct SmemWin {
   float x1[DK], qv[DK], ktn[DK];  // alpha_i k_i, q_i, beta_i k_i (float32)
   float cx1[DK], cq[DK];          // C_a x1_a, C_a q_a
@@ -33,7 +46,11 @@ struct SmemWin {
   float csum[DK / 32][2];         // per row block: sum_a C_a x1_a, sum_a C_a q_a
   float al[PM];                   // record decays
   float g1[PM + 1], g2[PM + 1];   // suffix products of the decays
-  float2 dots[DK / 32][PM];       // per row block: kt_j . x1, kt_j . q
+  float2 dots[DK / 32][PM + RMX];  // per row block: kt_j . x1, kt_j . q; then kc_h . x1, kc_h . q
+  float kc[RMX > 0 ? RMX : 1][DK];  // compensator pairs of the head (float)
+  float uc[RMX > 0 ? RMX : 1][DV];
+  float va[RMX > 0 ? DK : 1];       // compensator fit: a = M b, then the rounded kc
+  float red[2][DK / 32 + 1];        // compensator fit: block sums (two buffers)
   float unew[DV];
   float2 colA[DK / 32][DV / 2];
   float2 colB[DK / 32][DV / 2];
@@ -51,9 +68,11 @@ struct WinPtrs {
   float* alpha;
   unsigned char* Z;
   float *C, *B, *K, *U;
+  __half *Kc, *Uc;  // compensator pairs [r][d_k], [r][d_v]
 };
 
-__device__ __forceinline__ WinPtrs win_ptrs(unsigned char* base, int zoff, int DK, int DV, int P) {
+__device__ __forceinline__ WinPtrs win_ptrs(unsigned char* base, int zoff, int DK, int DV, int P,
+                                            int R) {
   WinPtrs w;
   w.ell = reinterpret_cast<int*>(base);
   w.alpha = reinterpret_cast<float*>(base + 16);
@@ -62,7 +81,14 @@ __device__ __forceinline__ WinPtrs win_ptrs(unsigned char* base, int zoff, int D
   w.B = w.C + DK;
   w.K = w.B + DV;
   w.U = w.K + P * DK;
+  w.Kc = reinterpret_cast<__half*>(w.U + P * DV);
+  w.Uc = w.Kc + R * DK;
   return w;
+}
+
+// FP16 of a signed value, saturating at the largest finite magnitude.
+__device__ __forceinline__ __half half_sat(float v) {
+  return __float2half_rn(fminf(fmaxf(v, -kFp16Max), kFp16Max));
 }
 
 __device__ __forceinline__ void wave_sync() {
@@ -72,8 +98,8 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // Copy the first n records (K rows, then U rows) of the head into LDS.
-template <int DK, int DV, int PM>
-__device__ __forceinline__ void stage_records(const WinPtrs& wp, int n, SmemWin<DK, DV, PM>& sm) {
+template <int DK, int DV, int PM, int RMX>
+__device__ __forceinline__ void stage_records(const WinPtrs& wp, int n, SmemWin<DK, DV, PM, RMX>& sm) {
   constexpr int NT = (DK / 32) * (DV / 2);
   const int t = threadIdx.x;
   const int nk = n * DK / 4, nu = n * DV / 4;
@@ -83,12 +109,145 @@ __device__ __forceinline__ void stage_records(const WinPtrs& wp, int n, SmemWin<
     reinterpret_cast<float4*>(&sm.u.rec.U[0][0])[i] = reinterpret_cast<const float4*>(wp.U)[i];
 }
 
+// Copy the head's R compensator pairs into LDS as float.
+template <int DK, int DV, int PM, int RMX>
+__device__ __forceinline__ void stage_comp(const WinPtrs& wp, int R, SmemWin<DK, DV, PM, RMX>& sm) {
+  constexpr int NT = (DK / 32) * (DV / 2);
+  const int t = threadIdx.x;
+  for (int i = t; i < R * DK; i += NT) (&sm.kc[0][0])[i] = __half2float(wp.Kc[i]);
+  for (int i = t; i < R * DV; i += NT) (&sm.uc[0][0])[i] = __half2float(wp.Uc[i]);
+}
+
+// Rank-R compensator fit of the dense state in x by power iteration, pair
+// after pair on the residual (warm: start from the staged uc_h unless it is
+// zero; else from the all-ones vector).  Stores the FP16 pairs in the head
+// and leaves the residual in x.  All threads call this; it begins with a
+// barrier, after which the record buffer may be reused.
+template <int DK, int DV, int PM, int RMX>
+__device__ __forceinline__ void fit_compensators(float (&x)[64], const WinPtrs& wp, int R,
+                                                 int iters, bool warm, SmemWin<DK, DV, PM, RMX>& sm) {
+  using G = Geo<DK, DV>;
+  constexpr int NP = G::NP, NRB = G::NRB;
+  const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p, r0 = 32 * rb;
+  __syncthreads();
+  for (int h = 0; h < R; ++h) {
+    float b0 = 1.f, b1 = 1.f;
+    if (warm) {
+      const float u0 = sm.uc[h][j0], u1 = sm.uc[h][j0 + 1];
+      if (__syncthreads_or(u0 != 0.f || u1 != 0.f)) {
+        b0 = u0;
+        b1 = u1;
+      }
+    }
+    float inv = 0.f;  // 1 / |M b| of the last iteration; 0 marks a zero pair
+    for (int it = 0; it < iters; ++it) {
+      // a = M b: row sums of the lane's two columns through the per-wave transpose
+      float sh[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          const int mr = 16 * hf + m;
+          sm.u.rowt[rb][m][p] = fmaf(x[2 * mr], b0, x[2 * mr + 1] * b1);
+        }
+        wave_sync();
+        const int mm = p & 15, part = p >> 4;
+        float sv = sm.u.rowt[rb][mm][part * 16];
+#pragma unroll
+        for (int pp = 1; pp < 16; ++pp) sv += sm.u.rowt[rb][mm][part * 16 + pp];
+#pragma unroll
+        for (int o = 16; o < NP; o <<= 1) sv += __shfl_xor(sv, o);
+        sh[hf] = sv;
+        wave_sync();
+      }
+      // |a|^2 partial and M^T a partial of the row block go out together;
+      // buffers alternate by iteration so one barrier per iteration suffices
+      float2(*part)[NP] = (it & 1) ? sm.colB : sm.colA;
+      float q2 = 0.f;
+      if (p < 32) {
+        const float ai = p < 16 ? sh[0] : sh[1];
+        sm.va[r0 + p] = ai;
+        q2 = ai * ai;
+      }
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) q2 += __shfl_xor(q2, o);
+      if (p == 0) sm.red[it & 1][rb] = q2;
+      wave_sync();
+      float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+      for (int m = 0; m < 32; m += 4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&sm.va[r0 + m]);
+        const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c0 = fmaf(av[q], x[2 * (m + q)], c0);
+          c1 = fmaf(av[q], x[2 * (m + q) + 1], c1);
+        }
+      }
+      part[rb][p] = make_float2(c0, c1);
+      __syncthreads();
+      float na2 = 0.f;
+#pragma unroll
+      for (int r = 0; r < NRB; ++r) na2 += sm.red[it & 1][r];
+      if (!(na2 > 0.f)) {  // M b = 0: a zero pair (block-uniform)
+        inv = 0.f;
+        break;
+      }
+      inv = 1.0f / sqrtf(na2);
+      // b = M^T a / |a|
+      b0 = 0.f;
+      b1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < NRB; ++r) {
+        b0 += part[r][p].x;
+        b1 += part[r][p].y;
+      }
+      b0 *= inv;
+      b1 *= inv;
+    }
+    // sigma = |b| over the columns (row block 0 holds each column once)
+    float s2 = rb == 0 ? fmaf(b0, b0, b1 * b1) : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) s2 += __shfl_xor(s2, o);
+    if (t == 0) sm.red[0][NRB] = s2;
+    __syncthreads();
+    const float sigma = sqrtf(sm.red[0][NRB]);
+    const bool zero = !(inv > 0.f) || !(sigma > 0.f);
+    const float sq = zero ? 0.f : sqrtf(sigma);
+    const float u0 = zero ? 0.f : __half2float(half_sat(b0 / sq));
+    const float u1 = zero ? 0.f : __half2float(half_sat(b1 / sq));
+    if (p < 32) {
+      const int i = r0 + p;
+      const __half kh = half_sat(zero ? 0.f : sq * (sm.va[i] * inv));
+      wp.Kc[h * DK + i] = kh;
+      sm.va[i] = __half2float(kh);
+    }
+    if (rb == 0) {
+      wp.Uc[h * DV + j0] = __float2half_rn(u0);
+      wp.Uc[h * DV + j0 + 1] = __float2half_rn(u1);
+    }
+    wave_sync();
+    // take the stored pair out of the state
+#pragma unroll
+    for (int m = 0; m < 32; m += 4) {
+      const float4 k4 = *reinterpret_cast<const float4*>(&sm.va[r0 + m]);
+      const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[2 * (m + q)] = fmaf(-kv[q], u0, x[2 * (m + q)]);
+        x[2 * (m + q) + 1] = fmaf(-kv[q], u1, x[2 * (m + q) + 1]);
+      }
+    }
+    __syncthreads();  // red, colA, colB and va are reused by the next pair
+  }
+}
+
 // x holds S (fp32, lane layout); re-encode it into the head and reset the
 // window.  All threads call this; it begins with a barrier, after which the
 // record buffer may be reused.
-template <int DK, int DV, int PM>
+template <int DK, int DV, int PM, int RMX>
 __device__ __forceinline__ void encode_boundary(float (&x)[64], const WinPtrs& wp, float c_floor,
-                                                SmemWin<DK, DV, PM>& sm, int P, bool clear_records) {
+                                                SmemWin<DK, DV, PM, RMX>& sm, int P, bool clear_records) {
   using G = Geo<DK, DV>;
   constexpr int NP = G::NP, NRB = G::NRB, NT = G::NT;
   const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p, r0 = 32 * rb;
@@ -150,10 +309,11 @@ __device__ __forceinline__ void encode_boundary(float (&x)[64], const WinPtrs& w
 }
 
 // Rebuild the dense state of L records (staged in LDS; record L-1 replaced by
-// the current token's when `last_new`) into x, which holds Z + 128 on entry.
-template <int DK, int DV, int PM>
-__device__ __forceinline__ void rebuild(float (&x)[64], const WinPtrs& wp, int L, bool last_new,
-                                        SmemWin<DK, DV, PM>& sm) {
+// the current token's when `last_new`) and R compensator pairs (staged) into
+// x, which holds Z + 128 on entry.
+template <int DK, int DV, int PM, int RMX>
+__device__ __forceinline__ void rebuild(float (&x)[64], const WinPtrs& wp, int L, int R,
+                                        bool last_new, SmemWin<DK, DV, PM, RMX>& sm) {
   using G = Geo<DK, DV>;
   constexpr int NP = G::NP, NT = G::NT;
   const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p, r0 = 32 * rb;
@@ -183,6 +343,21 @@ __device__ __forceinline__ void rebuild(float (&x)[64], const WinPtrs& wp, int L
     x[2 * m] = f * bb.x * (x[2 * m] - 128.f);
     x[2 * m + 1] = f * bb.y * (x[2 * m + 1] - 128.f);
   }
+  // compensator pairs decay with the boundary: Gamma_{1:L} kc_h uc_h^T
+  const float gb = sm.g1[PM];
+  for (int h = 0; h < R; ++h) {
+    const float u0 = sm.uc[h][j0], u1 = sm.uc[h][j0 + 1];
+#pragma unroll
+    for (int m = 0; m < 32; m += 4) {
+      const float4 k4 = *reinterpret_cast<const float4*>(&sm.kc[h][r0 + m]);
+      const float kv[4] = {gb * k4.x, gb * k4.y, gb * k4.z, gb * k4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[2 * (m + q)] = fmaf(kv[q], u0, x[2 * (m + q)]);
+        x[2 * (m + q) + 1] = fmaf(kv[q], u1, x[2 * (m + q) + 1]);
+      }
+    }
+  }
   for (int j = 0; j < L; ++j) {
     const float2 u = *reinterpret_cast<const float2*>(&sm.u.rec.U[j][j0]);
 #pragma unroll
@@ -198,12 +373,12 @@ __device__ __forceinline__ void rebuild(float (&x)[64], const WinPtrs& wp, int L
   }
 }
 
-template <int DK, int DV, int PM, int OP>
+template <int DK, int DV, int PM, int OP, int RMX>
 __global__ __launch_bounds__((DK / 32) * (DV / 2))
 __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
   using G = Geo<DK, DV>;
   constexpr int NP = G::NP, NRB = G::NRB;
-  __shared__ SmemWin<DK, DV, PM> sm;
+  __shared__ SmemWin<DK, DV, PM, RMX> sm;
   const int tile = blockIdx.x;
   const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p, r0 = 32 * rb;
   int h = 0;
@@ -212,8 +387,8 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     if (OP == OP_DECODE && t < DV) a.y[(long long)tile * DV + t] = __builtin_nanf("");
     return;
   }
-  const int P = a.P.p;
-  const WinPtrs wp = win_ptrs(base, wuni(a.P.r_off[h]), DK, DV, P);
+  const int P = a.P.p, R = RMX > 0 ? a.P.rank : 0;
+  const WinPtrs wp = win_ptrs(base, wuni(a.P.r_off[h]), DK, DV, P, R);
   constexpr int op = OP;
   float x[64];
   if constexpr (op == OP_PACK) {
@@ -224,7 +399,8 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
       x[2 * m] = v2.x;
       x[2 * m + 1] = v2.y;
     }
-    encode_boundary<DK, DV, PM>(x, wp, a.P.c_floor, sm, P, true);
+    if (R > 0) fit_compensators<DK, DV, PM, RMX>(x, wp, R, a.P.iters, false, sm);
+    encode_boundary<DK, DV, PM, RMX>(x, wp, a.P.c_floor, sm, P, true);
     return;
   }
   // records held; a value outside [0, p) is not a state this library writes,
@@ -233,16 +409,18 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
   {
     uint32_t wd[16];
     load_chunk<8, NP>(wp.Z, rb, p, wd);
-    stage_records<DK, DV, PM>(wp, ell, sm);
+    stage_records<DK, DV, PM, RMX>(wp, ell, sm);
+    stage_comp<DK, DV, PM, RMX>(wp, R, sm);
     unpack_offset<8>(wd, x);  // Z + 128
   }
   if (t < ell) sm.al[t] = wp.alpha[t];
   if constexpr (op == OP_UNPACK || op == OP_FLUSH) {
     if (op == OP_FLUSH && ell == 0) return;
     __syncthreads();
-    rebuild<DK, DV, PM>(x, wp, ell, false, sm);
+    rebuild<DK, DV, PM, RMX>(x, wp, ell, R, false, sm);
     if constexpr (op == OP_FLUSH) {
-      encode_boundary<DK, DV, PM>(x, wp, a.P.c_floor, sm, P, false);
+      if (R > 0) fit_compensators<DK, DV, PM, RMX>(x, wp, R, a.P.iters, true, sm);
+      encode_boundary<DK, DV, PM, RMX>(x, wp, a.P.c_floor, sm, P, false);
       return;
     }
     float* S = a.S_out + (long long)tile * DK * DV;
@@ -293,12 +471,15 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     }
     sm.g2[PM] = g;
   }
-  // record dot products over this wave's rows: lane j handles record j
-  if (p <= ell && p < PM) {
+  // dot products over this wave's rows: lane j < PM handles record j, lane
+  // PM + h compensator pair h
+  const bool comp_lane = p >= PM && p < PM + R;
+  if ((p <= ell && p < PM) || comp_lane) {
+    const float* src = comp_lane ? sm.kc[p - PM] : (p == ell ? sm.ktn : sm.u.rec.K[p]);
     float d1 = 0.f, d2 = 0.f;
 #pragma unroll 8
     for (int m = 0; m < 32; ++m) {
-      const float kt = p == ell ? sm.ktn[r0 + m] : sm.u.rec.K[p][r0 + m];
+      const float kt = src[r0 + m];
       d1 = fmaf(kt, sm.x1[r0 + m], d1);
       d2 = fmaf(kt, sm.qv[r0 + m], d2);
     }
@@ -336,6 +517,20 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     const float f0 = bb.x * (1.0f / 127.0f), f1 = bb.y * (1.0f / 127.0f);
     float pv0 = sm.g1[PM] * f0 * r10, pv1 = sm.g1[PM] * f1 * r11;
     float w0 = sm.g2[PM] * f0 * r20, w1 = sm.g2[PM] * f1 * r21;
+    for (int hh = 0; hh < R; ++hh) {  // compensators decay with the boundary
+      float d1 = 0.f, d2 = 0.f;
+#pragma unroll
+      for (int r = 0; r < NRB; ++r) {
+        d1 += sm.dots[r][PM + hh].x;
+        d2 += sm.dots[r][PM + hh].y;
+      }
+      const float e1 = sm.g1[PM] * d1, e2 = sm.g2[PM] * d2;
+      const float uc0 = sm.uc[hh][j0], uc1 = sm.uc[hh][j0 + 1];
+      pv0 = fmaf(uc0, e1, pv0);
+      pv1 = fmaf(uc1, e1, pv1);
+      w0 = fmaf(uc0, e2, w0);
+      w1 = fmaf(uc1, e2, w1);
+    }
     for (int j = 0; j < ell; ++j) {
       float d1 = 0.f, d2 = 0.f;
 #pragma unroll
@@ -369,23 +564,30 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     }
     return;
   }
-  // the window is full: rebuild S_p from the staged records and re-encode
+  // the window is full: rebuild S_p from the staged records, refit the
+  // compensators and re-encode the residual
   __syncthreads();
-  rebuild<DK, DV, PM>(x, wp, P, true, sm);
-  encode_boundary<DK, DV, PM>(x, wp, a.P.c_floor, sm, P, false);
+  rebuild<DK, DV, PM, RMX>(x, wp, P, R, true, sm);
+  if (R > 0) fit_compensators<DK, DV, PM, RMX>(x, wp, R, a.P.iters, true, sm);
+  encode_boundary<DK, DV, PM, RMX>(x, wp, a.P.c_floor, sm, P, false);
+}
+
+template <int DK, int DV, int PM, int RMX>
+hipError_t launch_op(const TileArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_tiles), block((DK / 32) * (DV / 2));
+  switch (a.op) {
+    case OP_DECODE: hipLaunchKernelGGL((window_tile_kernel<DK, DV, PM, OP_DECODE, RMX>), grid, block, 0, s, a); break;
+    case OP_PACK: hipLaunchKernelGGL((window_tile_kernel<DK, DV, PM, OP_PACK, RMX>), grid, block, 0, s, a); break;
+    case OP_UNPACK: hipLaunchKernelGGL((window_tile_kernel<DK, DV, PM, OP_UNPACK, RMX>), grid, block, 0, s, a); break;
+    case OP_FLUSH: hipLaunchKernelGGL((window_tile_kernel<DK, DV, PM, OP_FLUSH, RMX>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <int DK, int DV, int PM>
 hipError_t launch_pm(const TileArgs& a, hipStream_t s) {
-  const dim3 grid(a.n_tiles), block((DK / 32) * (DV / 2));
-  switch (a.op) {
-    case OP_DECODE: hipLaunchKernelGGL((window_tile_kernel<DK, DV, PM, OP_DECODE>), grid, block, 0, s, a); break;
-    case OP_PACK: hipLaunchKernelGGL((window_tile_kernel<DK, DV, PM, OP_PACK>), grid, block, 0, s, a); break;
-    case OP_UNPACK: hipLaunchKernelGGL((window_tile_kernel<DK, DV, PM, OP_UNPACK>), grid, block, 0, s, a); break;
-    case OP_FLUSH: hipLaunchKernelGGL((window_tile_kernel<DK, DV, PM, OP_FLUSH>), grid, block, 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return a.P.rank > 0 ? launch_op<DK, DV, PM, RM>(a, s) : launch_op<DK, DV, PM, 0>(a, s);
 }
 
 template <int DK, int DV>
@@ -396,7 +598,9 @@ hipError_t launch(const TileArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_tile_window(const TileArgs& a, hipStream_t s) {
-  if (a.P.p > 32 || a.P.p < 1) return hipErrorInvalidValue;
+  if (a.P.p > 32 || a.P.p < 1 || a.P.rank < 0 || a.P.rank > RM) return hipErrorInvalidValue;
+  // compensator lanes follow the record lanes inside one row block
+  if (a.P.rank > 0 && (a.P.p <= 16 ? 16 : 32) + RM > a.P.dv / 2) return hipErrorInvalidValue;
   const int dk = a.P.dk, dv = a.P.dv;
   if (dk == 128 && dv == 128) return launch<128, 128>(a, s);
   if (dk == 64 && dv == 64) return launch<64, 64>(a, s);

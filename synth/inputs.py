@@ -53,6 +53,8 @@ class Workload:
     cand_bits: Tuple[int, ...] = (4, 6, 8)
     pivot_frac: float = 0.0
     window: int = 16                    # window length p (window mode)
+    comp_rank: int = 0                  # window mode: compensator pairs per head
+    power_iters: int = 4                # window mode: power iterations per pair
     half_life: float = 64.0             # constant GDN half-life (tokens)
     half_life_range: Optional[Tuple[float, float]] = None  # log-uniform range
     warmup_steps: int = 128
@@ -104,6 +106,11 @@ WORKLOADS: Dict[str, Workload] = {
     "gdn_window16": Workload(
         name="gdn_window16", kind="gdn", mode="window", batch=256, n_slots=256, heads=32,
         d_k=128, d_v=128, steps=1024, seed=4, window=16, half_life=64.0),
+    # the same with r = 4 FP16 compensator pairs per head, 4 power iterations
+    "gdn_window16_r4": Workload(
+        name="gdn_window16_r4", kind="gdn", mode="window", batch=256, n_slots=256, heads=32,
+        d_k=128, d_v=128, steps=1024, seed=4, window=16, half_life=64.0, comp_rank=4,
+        power_iters=4),
 }
 
 

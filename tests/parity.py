@@ -48,7 +48,8 @@ def oracle_desc(d: dict) -> dict:
                 "bits": d["uniform_bits"]}
     if d["mode"] == 2:
         return {"mode": "window", "heads": d["heads"], "d_k": d["d_k"], "d_v": d["d_v"],
-                "p": d["window"]}
+                "p": d["window"], "rank": d.get("window_rank", 0),
+                "iters": d.get("window_iters", 0)}
     ub = d["unit_bits"]
     if d["kind"] == 0:
         return {"mode": "step", "kind": "gdn", "heads": d["heads"], "d_k": d["d_k"],
@@ -203,6 +204,30 @@ def check_window_quant(where, S, gpu, rep: Report, c_floor=Q.WINDOW_C_FLOOR):
     rep.bad(where, "window codes", bad)
 
 
+def comp_adopter(where, gpu: dict, iters: int, dim: int, rep: Report):
+    """Teacher-forced check of the compensator pairs (LeapQuant notes Sec. 2.4):
+    the GPU's stored FP16 pair h must be the oracle's binary16 rounding of its
+    float64 fit, or a correct rounding of a value within the float32 error of
+    the fit, taken as (2 iters + 1) dim 2^-24 of the pair vector's norm (each
+    iteration is two dim-term sums, plus the final scaling).  The GPU's pair
+    is adopted either way, so the residual and the next pairs follow the
+    stored values."""
+    tau = (2 * iters + 1) * dim * 2.0 ** -24
+
+    def adopt(h, k, u):
+        out = []
+        for raw, g, name in ((k, gpu["Kc"][h], "Kc"), (u, gpu["Uc"][h], "Uc")):
+            own = W.fp16_value(raw)
+            half_ulp = 0.5 * np.spacing(np.abs(raw).astype(np.float16)).astype(np.float64)
+            near = np.abs(g - raw) <= half_ulp + tau * np.linalg.norm(raw)
+            ok = (g == own) | near
+            rep.add("comp_adopted", int(np.sum((g != own) & ok)))
+            rep.bad(where, f"compensator {name}[{h}]", ~ok)
+            out.append(np.asarray(g, dtype=np.float64).copy())
+        return out[0], out[1]
+    return adopt
+
+
 # --------------------------------------------------------------- step checks
 def check_decode_head(where, desc, h, before: bytes, after: bytes, inp: dict, y_gpu, w,
                       rep: Report):
@@ -212,13 +237,13 @@ def check_decode_head(where, desc, h, before: bytes, after: bytes, inp: dict, y_
     d_k = desc["d_k"]
     mode = desc["mode"]
     if mode == "window":
+        rank, iters = int(desc.get("rank", 0)), int(desc.get("iters", 0))
+        adopt = comp_adopter(where, st1, iters, max(d_k, desc["d_v"]), rep) if rank else None
         r = W.window_step(st0, inp["q"], inp["k"], inp["v"], float(inp["beta"]),
-                          float(inp["gate"]), int(desc["p"]))
+                          float(inp["gate"]), int(desc["p"]), iters, adopt=adopt)
         rep.y(where, y_gpu, r["o"])
         if r["flushed"] is not None:
-            S = W.window_dense(r["S0"], r["state"]["alpha"], r["state"]["kt"], r["state"]["u"],
-                               int(desc["p"]))
-            check_window_quant(where, S, st1, rep)
+            check_window_quant(where, r["flushed"]["R"], st1, rep)
             rep.bad(where, "l after flush", np.array([st1["ell"] != 0]))
         else:
             i = int(st0["ell"])
@@ -230,6 +255,10 @@ def check_decode_head(where, desc, h, before: bytes, after: bytes, inp: dict, y_
             rel = np.linalg.norm(st1["u"][i] - r["u"]) / max(np.linalg.norm(r["u"]), 1e-300)
             rep.bad(where, f"record u rel err {rel:.2e}", np.array([not rel <= Y_REL]))
             rep.bad(where, "boundary codes changed", st1["Z"] != st0["Z"])
+            if rank:
+                rep.bad(where, "compensators changed",
+                        (st1["Kc"] != st0["Kc"]).ravel())
+                rep.bad(where, "compensators changed", (st1["Uc"] != st0["Uc"]).ravel())
         return
     kind = desc.get("kind", "gdn")
     dvec = R.gate_vector(inp["gate"], "gdn" if mode == "uniform" else kind, d_k)
@@ -248,12 +277,23 @@ def check_decode_head(where, desc, h, before: bytes, after: bytes, inp: dict, y_
         check_step(where, X, w, row_bits_of(desc, h), st1, rep, mag=mag)
 
 
+def check_window_encode(where, desc, S, gpu: dict, rep: Report, init=None):
+    """A boundary re-encode of dense S: with compensators, the teacher-forced
+    pair fit (started from `init`, the head's previous pairs, or the all-ones
+    vector) comes first and the residual is what is quantized."""
+    rank, iters = int(desc.get("rank", 0)), int(desc.get("iters", 0))
+    if rank:
+        adopt = comp_adopter(where, gpu, iters, max(desc["d_k"], desc["d_v"]), rep)
+        S = W.encode_boundary(S, rank, iters, init, adopt=adopt)["R"]
+    check_window_quant(where, S, gpu, rep)
+
+
 def check_quantized_head(where, desc, h, X, packed: bytes, w, rep: Report):
     st = parse_head(desc, h, packed)
     if desc["mode"] == "uniform":
         check_uniform(where, X, int(desc["bits"]), st, rep)
     elif desc["mode"] == "window":
-        check_window_quant(where, X, st, rep)
+        check_window_encode(where, desc, X, st, rep)  # a pack starts from all-ones
         rep.bad(where, "l", np.array([st["ell"] != 0]))
     else:
         check_step(where, X, w, row_bits_of(desc, h), st, rep)

@@ -40,7 +40,7 @@ def _desc_for_oracle(d, unit_bits=None):
                 "bits": d["uniform_bits"]}
     if d["mode"] == sq.SQ_MODE_WINDOW:
         return {"mode": "window", "heads": d["heads"], "d_k": d["d_k"], "d_v": d["d_v"],
-                "p": d["window"]}
+                "p": d["window"], "rank": d["window_rank"]}
     ub = d["unit_bits"]
     if d["kind"] == sq.SQ_KIND_GDN:
         return {"mode": "step", "kind": "gdn", "heads": d["heads"], "d_k": d["d_k"],
@@ -49,7 +49,7 @@ def _desc_for_oracle(d, unit_bits=None):
             "d_v": d["d_v"], "row_bits": ub.reshape(d["heads"], d["d_k"])}
 
 
-@pytest.mark.parametrize("case", ["uni64", "uni128_4", "gdn", "kda", "win"])
+@pytest.mark.parametrize("case", ["uni64", "uni128_4", "gdn", "kda", "win", "win_r4", "win_r8_64"])
 def test_layout_sizes_match_independent_parser(case):
     rng = np.random.default_rng(7)
     if case == "uni64":
@@ -62,8 +62,12 @@ def test_layout_sizes_match_independent_parser(case):
     elif case == "kda":
         bits = rng.choice([4, 6, 8, 16], size=4 * 128)
         p = sq.sq_plan_create_step(sq.SQ_KIND_KDA, 4, 128, 128, bits, np.ones((4, 128)))
-    else:
+    elif case == "win":
         p = sq.sq_plan_create_window(5, 128, 128, 16)
+    elif case == "win_r4":
+        p = sq.sq_plan_create_window_lowrank(5, 128, 128, 16, 4, 4)
+    else:
+        p = sq.sq_plan_create_window_lowrank(3, 64, 64, 7, 8, 2)
     d = sq.sq_plan_query(p)
     lay = L.slot_layout(_desc_for_oracle(d))
     assert d["slot_bytes"] == lay["slot_bytes"]
@@ -176,6 +180,15 @@ def test_error_codes():
     with pytest.raises(sq.StepqError) as e:
         sq.sq_plan_create_window(1, 128, 128, 0)
     assert e.value.status == sq.SQ_EUNSUPPORTED
+    with pytest.raises(sq.StepqError) as e:
+        sq.sq_plan_create_window_lowrank(1, 128, 128, 16, 9, 4)
+    assert e.value.status == sq.SQ_EUNSUPPORTED and "rank" in sq.sq_last_error()
+    with pytest.raises(sq.StepqError) as e:
+        sq.sq_plan_create_window_lowrank(1, 128, 128, 16, 4, 0)
+    assert e.value.status == sq.SQ_EUNSUPPORTED and "iterations" in sq.sq_last_error()
+    d = sq.sq_plan_query(sq.sq_plan_create_window_lowrank(1, 128, 128, 16, 0, 0))
+    assert d["window_rank"] == 0 and d["window_iters"] == 0
+    assert d["slot_bytes"] == sq.sq_plan_query(sq.sq_plan_create_window(1, 128, 128, 16))["slot_bytes"]
     with pytest.raises(sq.StepqError) as e:
         sq.sq_plan_create_step(sq.SQ_KIND_GDN, 2, 128, 128, [4, 3], np.ones((2, 128)))
     assert e.value.status == sq.SQ_EUNSUPPORTED

@@ -1,6 +1,7 @@
 """GPU parity of the per-window variant (INT8 boundary with key-row smoothing,
-float32 records, dense rebuild every p tokens) against the oracle,
-teacher-forced, across window flushes."""
+float32 records, dense rebuild every p tokens, optional FP16 compensator
+pairs refitted at every rebuild) against the oracle, teacher-forced, across
+window flushes."""
 import numpy as np
 import pytest
 
@@ -9,7 +10,7 @@ from oracle import window as W
 from synth import inputs as SI
 
 from gpu_util import Pool, head_inputs, inputs_dev, oracle_warmup, to_dev
-from parity import (Report, check_decode_head, check_quantized_head, check_window_quant,
+from parity import (Report, check_decode_head, check_quantized_head, check_window_encode,
                     dequant_head, oracle_desc)
 
 pytestmark = pytest.mark.gpu
@@ -40,10 +41,18 @@ def _run(pool, w, slots, steps, tiles=None, compare=None):
     return rep
 
 
-@pytest.mark.parametrize("p,steps", [(4, 10), (16, 34), (1, 3)])
-def test_window_decode_across_flushes(p, steps):
+def _plan(heads, dk, dv, p, rank, iters=4):
+    if rank == 0:
+        return sq.sq_plan_create_window(heads, dk, dv, p)
+    return sq.sq_plan_create_window_lowrank(heads, dk, dv, p, rank, iters)
+
+
+@pytest.mark.parametrize("p,steps,rank,iters", [(4, 10, 0, 0), (16, 34, 0, 0), (1, 3, 0, 0),
+                                                (4, 10, 4, 4), (16, 34, 4, 4), (8, 17, 8, 2),
+                                                (32, 33, 1, 6)])
+def test_window_decode_across_flushes(p, steps, rank, iters):
     w = SI.workload("gdn_window16", batch=3, n_slots=5, heads=2, window=p, steps=steps)
-    pool = Pool(sq.sq_plan_create_window(2, 128, 128, p), 5)
+    pool = Pool(_plan(2, 128, 128, p, rank, iters), 5)
     slots = SI.slot_ids(w)
     pool.pack(to_dev(slots), to_dev(oracle_warmup(w, 32).astype(np.float32)), w.batch)
     rep = _run(pool, w, slots, w.steps)
@@ -51,25 +60,28 @@ def test_window_decode_across_flushes(p, steps):
     rep.assert_ok()
 
 
-def test_window_64_and_rectangular():
+@pytest.mark.parametrize("rank", [0, 2])
+def test_window_64_and_rectangular(rank):
     for dk, dv in ((64, 64), (128, 64), (64, 128)):
         w = SI.workload("gdn_window16", batch=2, n_slots=2, heads=2, d_k=dk, d_v=dv, window=3,
                         steps=7)
-        pool = Pool(sq.sq_plan_create_window(2, dk, dv, 3), 2)
+        pool = Pool(_plan(2, dk, dv, 3, rank, 3), 2)
         slots = SI.slot_ids(w)
         pool.pack(to_dev(slots), to_dev(oracle_warmup(w, 16).astype(np.float32)), w.batch)
         rep = _run(pool, w, slots, w.steps)
         rep.assert_ok()
 
 
-def test_window_flush_unpack_pack():
+@pytest.mark.parametrize("rank", [0, 4])
+def test_window_flush_unpack_pack(rank):
     """sq_window_flush rebuilds partial windows (l = 0 heads untouched),
     sq_pool_unpack returns S_l, sq_pool_pack / quantize-only encode the
-    boundary."""
+    boundary (with compensators: refitted from the head's previous pairs at
+    a flush, from the all-ones vector at a pack)."""
     import torch
     rng = np.random.default_rng(12)
     w = SI.workload("gdn_window16", batch=4, n_slots=4, heads=2, window=8, steps=5)
-    pool = Pool(sq.sq_plan_create_window(2, 128, 128, 8), 4)
+    pool = Pool(_plan(2, 128, 128, 8, rank), 4)
     desc = oracle_desc(pool.desc)
     slots = SI.slot_ids(w)
     sdev = to_dev(slots)
@@ -101,7 +113,8 @@ def test_window_flush_unpack_pack():
             assert st0["ell"] == (5 if b < 2 else 3)
             st1 = parse_head(desc, h, pool.head_bytes(after, h))
             assert st1["ell"] == 0
-            check_window_quant(f"flush b {b} h {h}", W.window_state_dense(st0), st1, rep)
+            check_window_encode(f"flush b {b} h {h}", desc, W.window_state_dense(st0), st1, rep,
+                                init=st0.get("Uc"))
     rep.assert_ok()
     # a second flush is a no-op (l = 0)
     snap = pool.pool.cpu().numpy().copy()
@@ -124,12 +137,13 @@ def test_window_flush_unpack_pack():
     rep.assert_ok()
 
 
-def test_full_size_window_sampled():
+@pytest.mark.parametrize("rank", [0, 4])
+def test_full_size_window_sampled(rank):
     """Batch 256, 32 heads, p = 16 at full size: 20 tokens (one flush at token
     16), 16 sampled tiles compared at the flush and at the last token."""
     import torch
     w = SI.workload("gdn_window16")
-    pool = Pool(sq.sq_plan_create_window(32, 128, 128, 16), w.n_slots)
+    pool = Pool(_plan(32, 128, 128, 16, rank), w.n_slots)
     slots = SI.slot_ids(w)
     sdev = to_dev(slots)
     S = torch.zeros((w.batch, 32, 128, 128), dtype=torch.float32, device="cuda")
