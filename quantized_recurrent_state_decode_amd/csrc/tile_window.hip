@@ -26,9 +26,12 @@
 // Lanes own 2 columns x 32 rows of the INT8 boundary (blocked layout), so
 // S0^T x costs one fused multiply-add per element for each of the two read
 // vectors and the reduction over rows is lane-local plus one LDS combine.
-// The records held are staged in LDS with 16-byte loads issued together
-// with the boundary load; record dot products run one lane per record over
-// the wave's own rows; the rebuild at a flush reads the records from LDS.
+// The window position is read first; the boundary, the token's inputs and
+// then the records and pairs held (16-byte loads into registers, a fixed
+// count per thread) all go out before any of them is waited on, and the
+// records are committed to LDS together.  Record dot products run one lane
+// per record over the wave's own rows; the rebuild at a flush reads the
+// records from LDS.
 #include "tile_common.h"
 
 using namespace sqk;
@@ -44,7 +47,7 @@ struct SmemWin {
   float cx1[DK], cq[DK];          // C_a x1_a, C_a q_a
   float rowf[DK];                 // rebuild row factor, then 1 / C_a
   float csum[DK / 32][2];         // per row block: sum_a C_a x1_a, sum_a C_a q_a
-  float al[PM];                   // record decays
+  float al[PM + 1];               // record decays (+ a spare word)
   float g1[PM + 1], g2[PM + 1];   // suffix products of the decays
   float2 dots[DK / 32][PM + RMX];  // per row block: kt_j . x1, kt_j . q; then kc_h . x1, kc_h . q
   float kc[RMX > 0 ? RMX : 1][DK];  // compensator pairs of the head (float)
@@ -97,26 +100,71 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Copy the first n records (K rows, then U rows) of the head into LDS.
+// The records and compensator pairs held by a head, staged through
+// registers: `issue` starts every load (a fixed number per thread,
+// predicated on what the head holds), `commit` stores them to LDS, so the
+// loads share one memory round trip.
 template <int DK, int DV, int PM, int RMX>
-__device__ __forceinline__ void stage_records(const WinPtrs& wp, int n, SmemWin<DK, DV, PM, RMX>& sm) {
-  constexpr int NT = (DK / 32) * (DV / 2);
-  const int t = threadIdx.x;
-  const int nk = n * DK / 4, nu = n * DV / 4;
-  for (int i = t; i < nk; i += NT)
-    reinterpret_cast<float4*>(&sm.u.rec.K[0][0])[i] = reinterpret_cast<const float4*>(wp.K)[i];
-  for (int i = t; i < nu; i += NT)
-    reinterpret_cast<float4*>(&sm.u.rec.U[0][0])[i] = reinterpret_cast<const float4*>(wp.U)[i];
-}
+struct Staged {
+  static constexpr int NT = (DK / 32) * (DV / 2);
+  static constexpr int NK = (PM * DK / 4 + NT - 1) / NT;  // float4 of K rows per thread
+  static constexpr int NU = (PM * DV / 4 + NT - 1) / NT;  // float4 of U rows per thread
+  static constexpr int NC = RMX > 0 ? (RMX * (DK + DV) / 2 + NT - 1) / NT : 1;  // half2 of pairs
+  float4 k[NK], u[NU];
+  uint32_t c[NC];
+  float al;
 
-// Copy the head's R compensator pairs into LDS as float.
-template <int DK, int DV, int PM, int RMX>
-__device__ __forceinline__ void stage_comp(const WinPtrs& wp, int R, SmemWin<DK, DV, PM, RMX>& sm) {
-  constexpr int NT = (DK / 32) * (DV / 2);
-  const int t = threadIdx.x;
-  for (int i = t; i < R * DK; i += NT) (&sm.kc[0][0])[i] = __half2float(wp.Kc[i]);
-  for (int i = t; i < R * DV; i += NT) (&sm.uc[0][0])[i] = __half2float(wp.Uc[i]);
-}
+  // Loads are unconditional so that none waits for another: a slot the head
+  // does not hold reads element 0 instead (a line other threads read anyway)
+  // and is never committed.
+  __device__ __forceinline__ void issue(const WinPtrs& wp, int n, int R) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = t + i * NT;
+      k[i] = reinterpret_cast<const float4*>(wp.K)[e < n * DK / 4 ? e : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int e = t + i * NT;
+      u[i] = reinterpret_cast<const float4*>(wp.U)[e < n * DV / 4 ? e : 0];
+    }
+    if (RMX > 0) {
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int e = t + i * NT;
+        c[i] = reinterpret_cast<const uint32_t*>(wp.Kc)[e < R * (DK + DV) / 2 ? e : 0];
+      }
+    }
+    al = wp.alpha[t < n ? t : 0];
+  }
+
+  // Stores are unconditional too (a conditional store would pull its load
+  // next to it): slots past the records held land in record rows that are
+  // never read, those past the pairs held and the decays of threads past the
+  // records held in spare LDS words.
+  __device__ __forceinline__ void commit(int n, int R, SmemWin<DK, DV, PM, RMX>& sm) const {
+    static_assert(NK * NT == PM * DK / 4 && NU * NT == PM * DV / 4, "staging slots");
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) reinterpret_cast<float4*>(&sm.u.rec.K[0][0])[t + i * NT] = k[i];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) reinterpret_cast<float4*>(&sm.u.rec.U[0][0])[t + i * NT] = u[i];
+    if (RMX > 0) {
+      // pair values 2e, 2e+1 of the head's [Kc (R d_k) | Uc (R d_v)] run
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int e = t + i * NT, f = 2 * e;
+        float* dst = e >= R * (DK + DV) / 2 ? &sm.va[f & (DK - 2)]
+                     : f < R * DK           ? &sm.kc[0][0] + f
+                                            : &sm.uc[0][0] + (f - R * DK);
+        dst[0] = half_from_bits(c[i]);
+        dst[1] = half_from_bits(c[i] >> 16);
+      }
+    }
+    sm.al[t < n ? t : PM] = al;
+  }
+};
 
 // Rank-R compensator fit of the dense state in x by power iteration, pair
 // after pair on the residual (warm: start from the staged uc_h unless it is
@@ -403,17 +451,33 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     encode_boundary<DK, DV, PM, RMX>(x, wp, a.P.c_floor, sm, P, true);
     return;
   }
-  // records held; a value outside [0, p) is not a state this library writes,
-  // it is clamped so that every access stays inside the head
-  const int ell = min(max(wp.ell[0], 0), P - 1);
-  {
-    uint32_t wd[16];
-    load_chunk<8, NP>(wp.Z, rb, p, wd);
-    stage_records<DK, DV, PM, RMX>(wp, ell, sm);
-    stage_comp<DK, DV, PM, RMX>(wp, R, sm);
-    unpack_offset<8>(wd, x);  // Z + 128
+  // The window position is read first; the loads that do not depend on it
+  // (boundary codes, the token's inputs) go out behind it, so that they share
+  // one memory round trip with the staging of the records and pairs held.
+  // A position outside [0, p) is not a state this library writes; it is
+  // clamped so that every access stays inside the head.
+  const int ell0 = wp.ell[0];
+  uint32_t wd[16];
+  load_chunk<8, NP>(wp.Z, rb, p, wd);
+  const long long tk = (long long)tile * DK, tv = (long long)tile * DV;
+  float kk = 0.f, qq = 0.f, ca = 0.f, alpha = 0.f, beta = 0.f;
+  if constexpr (op == OP_DECODE) {
+    alpha = a.gate[tile];
+    beta = a.beta[tile];
+    if (p < 32) {
+      const int r = r0 + p;
+      kk = a.k[tk + r];
+      qq = a.q[tk + r];
+      ca = wp.C[r];
+    }
   }
-  if (t < ell) sm.al[t] = wp.alpha[t];
+  const int ell = min(max(ell0, 0), P - 1);
+  {
+    Staged<DK, DV, PM, RMX> stg;
+    stg.issue(wp, ell, R);
+    stg.commit(ell, R, sm);
+  }
+  unpack_offset<8>(wd, x);  // Z + 128
   if constexpr (op == OP_UNPACK || op == OP_FLUSH) {
     if (op == OP_FLUSH && ell == 0) return;
     __syncthreads();
@@ -430,12 +494,9 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     return;
   }
   // ---- decode token i = ell + 1 (record index ell, 0-based)
-  const long long tk = (long long)tile * DK, tv = (long long)tile * DV;
-  const float alpha = wuni(a.gate[tile]), beta = wuni(a.beta[tile]);
   if (t == 0) sm.al[ell] = alpha;
   if (p < 32) {  // per-row constants of this wave's rows
     const int r = r0 + p;
-    const float kk = a.k[tk + r], qq = a.q[tk + r], ca = wp.C[r];
     const float x1 = alpha * kk, kn = beta * kk;
     sm.x1[r] = x1;
     sm.qv[r] = qq;
