@@ -39,8 +39,15 @@ struct SmemKda {
 };
 
 // The packed head (at most max_code_bytes) and, while no codes are live,
-// the per-wave row transpose, share the dynamic LDS buffer.
+// the per-wave row transpose, share the dynamic LDS buffer; its last 16
+// bytes are a spare slot for staging stores past the head's region.
 extern __shared__ uint4 kda_dyn[];
+
+template <int DK, int DV>
+__host__ __device__ constexpr int dyn_bytes(int max_code_bytes) {
+  constexpr int transpose = (DK / 32) * 16 * (DV / 2 + 1) * 4;
+  return ((max_code_bytes > transpose ? max_code_bytes : transpose) + 15) / 16 * 16 + 16;
+}
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -141,13 +148,14 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   const int code_bytes = wuni(a.P.r_off[h]);
   __half* r_ptr = reinterpret_cast<__half*>(base + code_bytes);
   __half* c_ptr = reinterpret_cast<__half*>(base + wuni(a.P.c_off[h]));
-  // per-storage-row metadata of this wave's rows
+  // per-storage-row metadata of this wave's rows (loaded first: the key row
+  // indexes the token's inputs)
+  int rk = 0, rbits = 16, roff = 0;
   if (p < 32) {
     const int s = r0 + p;
-    const int b = a.P.row_bits[h * DK + s];
-    sm.bits[s] = b;
-    sm.off[s] = a.P.row_off[h * DK + s];
-    sm.qb[s] = b == 16 ? 0.f : (float)((1 << (b - 1)) - 1);
+    rk = rkey[s];
+    rbits = a.P.row_bits[h * DK + s];
+    roff = a.P.row_off[h * DK + s];
   }
   float x[64];
   float y0 = 0.f, y1 = 0.f;
@@ -160,21 +168,72 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
       x[2 * m] = v2.x;
       x[2 * m + 1] = v2.y;
     }
-    if (p < 32) sm.rowc[3][r0 + p] = 1.0f;
+    if (p < 32) {
+      const int s = r0 + p;
+      sm.bits[s] = rbits;
+      sm.off[s] = roff;
+      sm.qb[s] = rbits == 16 ? 0.f : (float)((1 << (rbits - 1)) - 1);
+      sm.rowc[3][s] = 1.0f;
+    }
     __syncthreads();
   } else {
-    for (int i = t * 16; i < code_bytes; i += NT * 16)
-      *reinterpret_cast<uint4*>(codes + i) = *reinterpret_cast<const uint4*>(base + i);
+    // The head's code rows are staged through registers, CH 16-byte chunks
+    // per thread and round (one round covers 16 KB at 128 x 128): the loads
+    // are unconditional (chunks past the region reread chunk 0) and so are
+    // the stores (those chunks land in a spare slot past the largest region),
+    // so nothing waits between them; the per-row inputs go out alongside.
+    constexpr int CH = 4;
+    const int nch = code_bytes >> 4;
+    const int spare = dyn_bytes<DK, DV>(a.P.max_code_bytes) / 16 - 1;
+    const uint4* src = reinterpret_cast<const uint4*>(base);
+    uint4* dst = reinterpret_cast<uint4*>(codes);
+    uint4 v[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {  // first round, issued before the per-row inputs
+      const int e = t + i * NT;
+      v[i] = src[e < nch ? e : 0];
+    }
+    // keep the key-indexed loads (which wait for the key rows) behind these
     const float c0 = __half2float(c_ptr[j0]), c1 = __half2float(c_ptr[j0 + 1]);
+    float rs = 0.f, d = 0.f, kk = 0.f, qq = 0.f;
     if (p < 32) {
-      const int s = r0 + p, key = rkey[s];
-      const bool piv = sm.bits[s] == 16;
-      const float sc = piv ? 1.f : __half2float(r_ptr[s]) * frcp(sm.qb[s]);
+      rs = __half2float(r_ptr[r0 + p]);
+      if constexpr (OP == OP_DECODE) {
+        d = a.gate[tk + rk];
+        kk = a.k[tk + rk];
+        qq = a.q[tk + rk];
+      }
+    }
+    const float beta = OP == OP_DECODE ? a.beta[tile] : 0.f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int e = t + i * NT;
+      dst[e < nch ? e : spare] = v[i];
+    }
+    for (int c = CH * NT; c < nch; c += CH * NT) {  // heads larger than one round
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int e = c + t + i * NT;
+        v[i] = src[e < nch ? e : 0];
+      }
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int e = c + t + i * NT;
+        dst[e < nch ? e : spare] = v[i];
+      }
+    }
+    if (p < 32) {
+      const int s = r0 + p, b = rbits;
+      const float qb = b == 16 ? 0.f : (float)((1 << (b - 1)) - 1);
+      sm.bits[s] = b;
+      sm.off[s] = roff;
+      sm.qb[s] = qb;
+      const bool piv = b == 16;
+      const float sc = piv ? 1.f : rs * frcp(qb);
       if constexpr (OP == OP_UNPACK) {
         sm.rowc[3][s] = sc;
       } else {
-        const float d = a.gate[tk + key];
-        const float kk = a.k[tk + key], qq = a.q[tk + key], bk = wuni(a.beta[tile]) * kk;
+        const float bk = beta * kk;
         const float rho = d * sc;
         // a vanishing retention keeps the division finite; the dropped part
         // (rp - rho) c_j z_sj is below 2^-60 of the write term
@@ -370,8 +429,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
 template <int DK, int DV>
 hipError_t launch(const TileArgs& a, hipStream_t s) {
   constexpr int NP = DV / 2, NRB = DK / 32;
-  const size_t transpose = (size_t)NRB * 16 * (NP + 1) * sizeof(float);
-  const size_t dyn = ((std::max<size_t>((size_t)a.P.max_code_bytes, transpose) + 15) / 16) * 16;
+  const size_t dyn = (size_t)dyn_bytes<DK, DV>(a.P.max_code_bytes);
   const dim3 grid(a.n_tiles), block(NRB * NP);
   switch (a.op) {
     case OP_DECODE: hipLaunchKernelGGL((kda_tile_kernel<DK, DV, OP_DECODE>), grid, block, dyn, s, a); break;
