@@ -144,6 +144,47 @@ typedef struct {
   double omega_floor_rel;   /* relative floor of omega (1e-12)                    */
 } sq_calib_opts;
 
+/* ------------------------------------------------- calibration statistics */
+
+/* The statistics sq_calibrate_bits takes, accumulated on the GPU over a
+ * calibration stream ([SQ] Sec. 4, Eqs. 6-8; Sec. 4.1, App. B-C).  The caller
+ * owns every buffer and zeroes the float64 accumulators before the first call;
+ * each call adds to them, and the caller divides by the number of samples.
+ *
+ * sq_calib_gate_stats adds one step of n sequences: log_sum[u] += sum_s
+ * log r_{s,u} (r = alpha[s][h] for a GDN unit u = h; d[s][h][i] for a KDA unit
+ * u = h d_k + i) and omega_sum[h][i] += sum_s g_{s,h,i}^2 with the transported
+ * query g = D (q - beta k (k . q)) (A_t^T q_t, [SQ] Sec. 4.1).  q, k, gate as in
+ * sq_decode_step with batch n; device pointers; float64 arithmetic.  Divided
+ * by the sample count: ell_u and omega_i of sq_calib_stats.
+ * Errors: SQ_EINVAL, SQ_EUNSUPPORTED (d_k not 64 or 128), SQ_EHIP. */
+sq_status sq_calib_gate_stats(int32_t kind, int32_t heads, int32_t d_k, int32_t n,
+                              const float* q, const float* k, const float* beta,
+                              const float* gate, double* log_sum, double* omega_sum,
+                              hipStream_t stream);
+
+/* Row impact factors from omega [heads][d_k] (host memory): w = (omega' /
+ * geomean_head(omega'))^(gamma / 2) with omega' = max(omega, floor_rel *
+ * max_head(omega)); a head whose omega are all zero gets w = 1 ([SQ] App. B,
+ * C; the same function sq_calibrate_bits applies).  w: host [heads][d_k].
+ * Errors: SQ_EINVAL, SQ_ENONFINITE. */
+sq_status sq_impact_factors(int32_t heads, int32_t d_k, const double* omega, double gamma,
+                            double floor_rel, float* w);
+
+/* Distortion d_u(b) of one snapshot ([SQ] Sec. 4, Eq. 8: the error of unit u
+ * quantised at width b): the plan's quantizer (a STEP plan of GDN heads, all
+ * at width b, no FP16 heads, with the impact factors w) packs the dense tiles
+ * S[n][H][d_k][d_v] (tile t = sequence t / H, head t % H) into `packed`
+ * (n H sq_max_head_bytes bytes of caller-owned device scratch), then
+ * dist_sum[u] += sum over the n sequences of the squared error
+ * sum (r_i c_j z_ij / q_b - S_ij)^2 of unit u: a whole head (per_row = 0,
+ * u = h) or one key row (per_row = 1, u = h d_k + i).  float64 accumulation
+ * with atomic adds (the order of the additions is not fixed).
+ * Errors: SQ_EINVAL, SQ_EPLAN_MISMATCH, SQ_EHIP. */
+sq_status sq_calib_distortion(const sq_plan* plan, const void* dev_plan, int32_t n,
+                              const float* S, void* packed, int32_t per_row, double* dist_sum,
+                              hipStream_t stream);
+
 /* ---------------------------------------------------------------- plans */
 
 /* Lifetime-aware bit allocation with sparse FP16 pivots ([SQ] Sec. 4, Eq. 8;

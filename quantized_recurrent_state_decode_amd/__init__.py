@@ -28,7 +28,8 @@ EXPORTED = (
     "sq_plan_create_window", "sq_plan_create_window_lowrank", "sq_plan_query", "sq_plan_destroy", "sq_plan_device_bytes",
     "sq_plan_upload", "sq_pool_bytes", "sq_pool_init", "sq_pool_pack", "sq_pool_unpack",
     "sq_decode_step", "sq_window_flush", "sq_quantize_tiles", "sq_max_head_bytes",
-    "sq_dense_step", "sq_last_error",
+    "sq_dense_step", "sq_calib_gate_stats", "sq_impact_factors", "sq_calib_distortion",
+    "sq_last_error",
 )
 
 
@@ -104,6 +105,9 @@ def lib() -> ctypes.CDLL:
             "sq_max_head_bytes": [_P, _SZ],
             "sq_dense_step": [_I32, _I32, _I32, _I32, _P, _I64, _P, _I32, _P, _P, _P, _P,
                               _P, _P, _P],
+            "sq_calib_gate_stats": [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P],
+            "sq_impact_factors": [_I32, _I32, _P, ctypes.c_double, ctypes.c_double, _P],
+            "sq_calib_distortion": [_P, _P, _I32, _P, _P, _I32, _P, _P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -296,6 +300,31 @@ def sq_dense_step(kind, heads, d_k, d_v, S, n_slots, slots, batch, q, k, v, beta
     _check(lib().sq_dense_step(kind, heads, d_k, d_v, _ptr(S, f), n_slots, _ptr(slots, _i32()),
                                batch, _ptr(q, f), _ptr(k, f), _ptr(v, f), _ptr(beta, f),
                                _ptr(gate, f), _ptr(y, f), _stream(stream)))
+
+
+def sq_calib_gate_stats(kind, heads, d_k, n, q, k, beta, gate, log_sum, omega_sum,
+                        stream=None) -> None:
+    import torch
+    f, d = _f32(), torch.float64
+    _check(lib().sq_calib_gate_stats(kind, heads, d_k, n, _ptr(q, f), _ptr(k, f), _ptr(beta, f),
+                                     _ptr(gate, f), _ptr(log_sum, d), _ptr(omega_sum, d),
+                                     _stream(stream)))
+
+
+def sq_impact_factors(omega, gamma: float = 0.25, floor_rel: float = 1e-12) -> np.ndarray:
+    """omega: host float64 [heads, d_k] -> w float32 [heads, d_k]."""
+    om = np.ascontiguousarray(omega, dtype=np.float64)
+    heads, d_k = om.shape
+    w = np.zeros((heads, d_k), dtype=np.float32)
+    _check(lib().sq_impact_factors(heads, d_k, om.ctypes.data, gamma, floor_rel, w.ctypes.data))
+    return w
+
+
+def sq_calib_distortion(plan, dev_plan, n, S, packed, per_row, dist_sum, stream=None) -> None:
+    import torch
+    _check(lib().sq_calib_distortion(plan, _ptr(dev_plan), n, _ptr(S, _f32()), _ptr(packed),
+                                     1 if per_row else 0, _ptr(dist_sum, torch.float64),
+                                     _stream(stream)))
 
 
 def device_plan(plan: Plan, device="cuda", stream=None):

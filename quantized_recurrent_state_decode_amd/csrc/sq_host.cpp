@@ -213,6 +213,28 @@ TileArgs class_args(const sq_plan* P, const TileArgs& a, const int* order, int l
   return b;
 }
 
+// row impact factors w = (omega / geomean_head(omega))^(gamma/2) with a relative
+// floor ([SQ] App. B, C); a head whose omega are all zero gets w = 1
+void impact_factors(int H, int dk, const double* omega, double gamma, double floor_rel, float* w) {
+  for (int h = 0; h < H; ++h) {
+    const double* om = omega + (size_t)h * dk;
+    double mx = 0.0;
+    for (int i = 0; i < dk; ++i) mx = std::max(mx, om[i]);
+    if (mx <= 0.0) {
+      for (int i = 0; i < dk; ++i) w[h * dk + i] = 1.0f;
+      continue;
+    }
+    std::vector<double> f(dk);
+    double lsum = 0.0;
+    for (int i = 0; i < dk; ++i) {
+      f[i] = std::max(om[i], floor_rel * mx);
+      lsum += std::log(f[i]);
+    }
+    const double gm = std::exp(lsum / dk);
+    for (int i = 0; i < dk; ++i) w[h * dk + i] = (float)std::pow(f[i] / gm, gamma / 2.0);
+  }
+}
+
 hipError_t dispatch(const sq_plan* P, const TileArgs& a, hipStream_t st) {
   if (P->mode == SQ_MODE_WINDOW) return launch_tile_window(a, st);
   if (P->mode == SQ_MODE_STEP && P->kind == SQ_KIND_KDA) return launch_tile_kda(a, st);
@@ -435,25 +457,8 @@ extern "C" sq_status sq_calibrate_bits(const sq_calib_stats* st, const sq_calib_
   std::vector<int32_t> bits(U);
   for (int u = 0; u < U; ++u) bits[u] = piv[u] ? SQ_PIVOT_BITS : st->cand_bits[level[u]];
 
-  // row impact factors w = (omega / geomean_head(omega))^(gamma/2)   ([SQ] App. B, C)
   std::vector<float> w(H * dk);
-  for (int h = 0; h < H; ++h) {
-    const double* om = st->omega + (size_t)h * dk;
-    double mx = 0.0;
-    for (int i = 0; i < dk; ++i) mx = std::max(mx, om[i]);
-    if (mx <= 0.0) {
-      for (int i = 0; i < dk; ++i) w[h * dk + i] = 1.0f;
-      continue;
-    }
-    std::vector<double> f(dk);
-    double lsum = 0.0;
-    for (int i = 0; i < dk; ++i) {
-      f[i] = std::max(om[i], op->omega_floor_rel * mx);
-      lsum += std::log(f[i]);
-    }
-    const double gm = std::exp(lsum / dk);
-    for (int i = 0; i < dk; ++i) w[h * dk + i] = (float)std::pow(f[i] / gm, op->gamma / 2.0);
-  }
+  impact_factors(H, dk, st->omega, op->gamma, op->omega_floor_rel, w.data());
   return sq_plan_create_step(st->kind, H, dk, dv, bits.data(), w.data(), out);
 }
 
@@ -622,6 +627,55 @@ extern "C" sq_status sq_quantize_tiles(const sq_plan* P, const void* dev_plan, c
   a.n_tiles = n_tiles;
   hipError_t e = dispatch(P, a, st);
   if (e != hipSuccess) return hip_fail(e, "launching quantize-only");
+  return ok();
+}
+
+extern "C" sq_status sq_impact_factors(int32_t heads, int32_t d_k, const double* omega,
+                                       double gamma, double floor_rel, float* w) {
+  if (!omega || !w || heads <= 0 || d_k <= 0 || !std::isfinite(gamma) || !(floor_rel >= 0))
+    return fail(SQ_EINVAL, "bad arguments to sq_impact_factors");
+  for (long long i = 0; i < (long long)heads * d_k; ++i)
+    if (!std::isfinite(omega[i]) || omega[i] < 0)
+      return fail(SQ_ENONFINITE, "omega[%lld] must be finite and non-negative", i);
+  impact_factors(heads, d_k, omega, gamma, floor_rel, w);
+  return ok();
+}
+
+extern "C" sq_status sq_calib_gate_stats(int32_t kind, int32_t heads, int32_t d_k, int32_t n,
+                                         const float* q, const float* k, const float* beta,
+                                         const float* gate, double* log_sum, double* omega_sum,
+                                         hipStream_t st) {
+  if (kind != SQ_KIND_GDN && kind != SQ_KIND_KDA) return fail(SQ_EINVAL, "bad kind %d", kind);
+  if (heads <= 0 || n < 0 || !q || !k || !beta || !gate || !log_sum || !omega_sum)
+    return fail(SQ_EINVAL, "bad arguments to sq_calib_gate_stats");
+  if (!supported_dim(d_k)) return fail(SQ_EUNSUPPORTED, "d_k must be 64 or 128 (got %d)", d_k);
+  if (n == 0) return ok();
+  hipError_t e = launch_calib_gate(kind, heads, d_k, n, q, k, beta, gate, log_sum, omega_sum, st);
+  if (e != hipSuccess) return hip_fail(e, "launching calibration gate statistics");
+  return ok();
+}
+
+extern "C" sq_status sq_calib_distortion(const sq_plan* P, const void* dev_plan, int32_t n,
+                                         const float* S, void* packed, int32_t per_row,
+                                         double* dist_sum, hipStream_t st) {
+  if (!P || !dev_plan || !S || !packed || !dist_sum || n < 0)
+    return fail(SQ_EINVAL, "bad arguments to sq_calib_distortion");
+  if (P->mode != SQ_MODE_STEP || P->kind != SQ_KIND_GDN)
+    return fail(SQ_EPLAN_MISMATCH, "sq_calib_distortion needs a STEP plan of GDN heads");
+  for (int h = 0; h < P->H; ++h)
+    if (P->head_bits[h] == SQ_PIVOT_BITS)
+      return fail(SQ_EPLAN_MISMATCH, "sq_calib_distortion needs integer heads (head %d is FP16)", h);
+  if (n == 0) return ok();
+  // the plan's own quantizer, quantize-only, tile t = (sequence t / H, head t % H)
+  TileArgs a = base_args(P, dev_plan, OP_PACK);
+  a.X = S;
+  a.out = static_cast<unsigned char*>(packed);
+  a.out_stride = P->max_head_bytes;
+  a.n_tiles = n * P->H;
+  hipError_t e = dispatch(P, a, st);
+  if (e == hipSuccess)
+    e = launch_calib_dist(a.P, a.n_tiles, a.out, a.out_stride, S, per_row ? 1 : 0, dist_sum, st);
+  if (e != hipSuccess) return hip_fail(e, "launching calibration distortion");
   return ok();
 }
 

@@ -81,6 +81,12 @@ hipError_t launch_tile_gdn(const TileArgs& a, hipStream_t s);     // uniform + S
 hipError_t launch_decode_gdn(const TileArgs& a, bool solo, hipStream_t s);
 hipError_t launch_tile_kda(const TileArgs& a, hipStream_t s);     // STEP KDA
 hipError_t launch_tile_window(const TileArgs& a, hipStream_t s);  // per-window variant
+hipError_t launch_calib_gate(int kind, int H, int dk, int n, const float* q, const float* k,
+                             const float* beta, const float* gate, double* log_sum,
+                             double* om_sum, hipStream_t s);
+hipError_t launch_calib_dist(const DevPlan& P, int n_tiles, const unsigned char* packed,
+                             long long stride, const float* S, int per_row, double* dist,
+                             hipStream_t s);
 hipError_t launch_dense_step(int kind, int H, int dk, int dv, float* S, long long n_slots,
                              const int* slots, int B, const float* q, const float* k,
                              const float* v, const float* beta, const float* gate, float* y,

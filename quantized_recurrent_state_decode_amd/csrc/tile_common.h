@@ -225,8 +225,8 @@ __device__ __forceinline__ float wuni(float v) {
 
 __device__ __forceinline__ bool resolve_tile(const TileArgs& a, int tile, int& h,
                                              unsigned char*& base) {
-  if (a.head_ids) {
-    h = wuni(a.head_ids[tile]);
+  if (a.out) {  // quantize-only: head head_ids[tile], or tile % H without ids
+    h = a.head_ids ? wuni(a.head_ids[tile]) : tile % a.P.H;
     if (h < 0 || h >= a.P.H) return false;
     base = a.out + (long long)tile * a.out_stride;
     return true;

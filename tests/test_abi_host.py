@@ -167,6 +167,27 @@ def test_calibrate_bits_uniform_heads_fill_budget():
     assert (b == 16).sum() == 1 and (b == 4).sum() == 45 and (b == 2).sum() == 2
 
 
+def test_impact_factors_match_oracle():
+    """sq_impact_factors (the function sq_calibrate_bits applies) equals the
+    oracle's w = (omega' / geomean omega')^(gamma/2), relative floor included,
+    to float32 rounding; an all-zero head gets w = 1."""
+    rng = np.random.default_rng(21)
+    om = rng.lognormal(0.0, 2.0, (5, 64))
+    om[1, :7] = 0.0                               # below the relative floor
+    om[2, 3] = 1e-30
+    w = sq.sq_impact_factors(om, 0.25, 1e-12)
+    np.testing.assert_allclose(w, C.impact_factors(om, 0.25, 1e-12), rtol=2e-7)
+    om[4] = 0.0
+    w = sq.sq_impact_factors(om)
+    assert np.all(w[4] == 1.0)
+    np.testing.assert_allclose(w[:4], C.impact_factors(om[:4]), rtol=2e-7)
+    bad = om.copy()
+    bad[0, 0] = np.nan
+    with pytest.raises(sq.StepqError) as e:
+        sq.sq_impact_factors(bad)
+    assert e.value.status == sq.SQ_ENONFINITE
+
+
 def test_error_codes():
     with pytest.raises(sq.StepqError) as e:
         sq.sq_plan_create_uniform(1, 96, 128, 8)
