@@ -207,6 +207,9 @@ def main():
                     help="skip the fp32-dense and uniform-INT4 runs at the pool workload's shape")
     ap.add_argument("--state-warmup", type=int, default=None,
                     help="fp32 steps that build the initial state (default: the workload's 128)")
+    ap.add_argument("--prefill", type=int, default=0, metavar="T",
+                    help="measure sq_prefill_chunk instead: one chunk of T tokens per sequence "
+                         "over the workload's batch and heads (tokens/s)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before timing, copy MIB MiB device-to-device once (a plain copy of "
                          "known size for scaling HBM traffic counters)")
@@ -223,6 +226,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = SI.workload(args.workload)
+    if args.prefill:
+        print(json.dumps(measure_prefill(sq, w, args)))
+        return
     m = measure(sq, w, args)
     abytes, ms_per_step, launch_ms, desc = m["abytes"], m["ms_per_step"], m["launch_ms"], m["desc"]
     family = "window" if w.mode == "window" else ("dense" if w.mode == "dense" else w.kind)
@@ -351,6 +357,56 @@ def measure(sq, w, args) -> dict:
     launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     return {"desc": desc, "pools": pools, "slots": slots, "ms_per_step": ms_per_step,
             "launch_ms": launch_ms, "abytes": algorithmic_bytes(desc, w)}
+
+
+VALU_PEAK = 256 * 4 * 16 * 2.4e9   # non-packed fp32 lane-ops/s: CUs x SIMDs x lanes x clock
+
+
+def measure_prefill(sq, w, args) -> dict:
+    """One chunk of T tokens for every sequence of the workload's batch, on
+    dense fp32 states (sq_prefill_chunk, the middle step between
+    sq_pool_unpack and sq_pool_pack).  The chunk is arithmetic-bound: four
+    fp32 lane-ops per state element and token (decayed update, write term,
+    readout, next key retrieval)."""
+    import torch
+    from synth import inputs as SI
+    T, B, H, dk, dv = args.prefill, w.batch, w.heads, w.d_k, w.d_v
+    params = SI.gate_params(w)
+    steps = [SI.step_inputs(w, t, params) for t in range(T)]
+    x = {k: torch.from_numpy(np.ascontiguousarray(np.stack([st[k] for st in steps], axis=1))).cuda()
+         for k in steps[0]}
+    del steps
+    S = torch.zeros((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    y = torch.empty((B, T, H, dv), dtype=torch.float32, device="cuda")
+    kind = 0 if w.kind == "gdn" else 1
+
+    def chunk():
+        sq.sq_prefill_chunk(kind, H, dk, dv, B, T, S, x["q"], x["k"], x["v"], x["beta"],
+                            x["gate"], y)
+
+    for _ in range(max(args.warmup // 10, 1)):
+        chunk()
+    torch.cuda.synchronize()
+    n = max(args.steps // 32, 2)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(n):
+        chunk()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / n
+    ops = 4.0 * dk * dv * B * H * T
+    return {"metric": "prefill tokens/s (one chunk per sequence, state in registers)",
+            "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": n,
+            "warmup": max(args.warmup // 10, 1), "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": w.name, "batch": B, "heads": H, "d_k": dk, "d_v": dv,
+                       "kind": w.kind, "chunk_tokens": T},
+            "roofline": {"bound": "alu", "achieved": ops / (ms * 1e-3) / 1e12,
+                         "peak": VALU_PEAK / 1e12, "unit": "T lane-ops/s",
+                         "frac": ops / (ms * 1e-3) / VALU_PEAK, "traffic": None,
+                         "kernel": "prefill_kernel<d_k,d_v>", "launch_ms": ms,
+                         "ops_per_launch": ops}}
 
 
 def same_hardware(sq, args, value: float) -> dict:

@@ -316,6 +316,21 @@ sq_status sq_quantize_tiles(const sq_plan* plan, const void* dev_plan, const flo
                             hipStream_t stream);
 sq_status sq_max_head_bytes(const sq_plan* plan, size_t* bytes);
 
+/* Prefill of one chunk ([SQ] App. F.1: a prefill unpacks the active states,
+ * runs the chunk and packs the boundary states; with sq_pool_unpack before
+ * and sq_pool_pack after, this is the middle step): T tokens of the
+ * unquantised gated delta rule, X = D S + beta k (v - (D S)^T k)^T,
+ * y = X^T q, S <- X ([SQ] Sec. 3, Eq. 1), for B sequences, in place on dense
+ * fp32 states S[B][H][d_k][d_v] (device, caller-owned; the state stays in
+ * registers for the whole chunk).  Inputs are sequence-major:
+ * q, k [B][T][H][d_k], v [B][T][H][d_v], beta [B][T][H], gate GDN alpha
+ * [B][T][H] or KDA d [B][T][H][d_k]; y [B][T][H][d_v] receives every token's
+ * output.  Errors: SQ_EINVAL, SQ_EUNSUPPORTED, SQ_EHIP. */
+sq_status sq_prefill_chunk(int32_t kind, int32_t heads, int32_t d_k, int32_t d_v,
+                           int32_t batch, int32_t T, float* S, const float* q, const float* k,
+                           const float* v, const float* beta, const float* gate, float* y,
+                           hipStream_t stream);
+
 /* Full-precision reference step on fp32 states S[n_slots][H][d_k][d_v]
  * (the FP32-state baseline of [SQ] Sec. 5.1 and [LQ] Sec. 3.3):
  * X = D S + beta k (v - (D S)^T k)^T stored in place, y = X^T q.

@@ -679,6 +679,21 @@ extern "C" sq_status sq_calib_distortion(const sq_plan* P, const void* dev_plan,
   return ok();
 }
 
+extern "C" sq_status sq_prefill_chunk(int32_t kind, int32_t H, int32_t dk, int32_t dv,
+                                      int32_t B, int32_t T, float* S, const float* q,
+                                      const float* k, const float* v, const float* beta,
+                                      const float* gate, float* y, hipStream_t st) {
+  if (kind != SQ_KIND_GDN && kind != SQ_KIND_KDA) return fail(SQ_EINVAL, "bad kind %d", kind);
+  sq_status s = check_dims(H, dk, dv);
+  if (s) return s;
+  if (B < 0 || T < 0 || !S || !q || !k || !v || !beta || !gate || !y)
+    return fail(SQ_EINVAL, "bad arguments to sq_prefill_chunk");
+  if (B == 0 || T == 0) return ok();
+  hipError_t e = launch_prefill_chunk(kind, H, dk, dv, B, T, S, q, k, v, beta, gate, y, st);
+  if (e != hipSuccess) return hip_fail(e, "launching prefill chunk");
+  return ok();
+}
+
 extern "C" sq_status sq_dense_step(int32_t kind, int32_t H, int32_t dk, int32_t dv, float* S,
                                    int64_t n_slots, const int32_t* slots, int32_t B,
                                    const float* q, const float* k, const float* v,
