@@ -65,9 +65,9 @@ def lowrank_fit(M: np.ndarray, rank: int, iters: int, init=None, exact: bool = F
     k~ = sqrt(sigma) a, u~ = b / sqrt(sigma), so k~ u~^T = a (M^T a)^T is the
     best rank-one fit along a.  A start with M b = 0 (M = 0 in particular)
     gives a zero pair.  Unless `exact`, the pair is rounded to FP16 before it
-    is subtracted.  `adopt(h, k, u)` (teacher-forced parity) may replace the
-    pair that is subtracted and stored.  Returns (K [rank, d_k], U [rank, d_v],
-    residual)."""
+    is subtracted.  `adopt(h, k, u)` (teacher-forced parity) receives the
+    unrounded pair and returns the FP16 pair that is subtracted and stored.
+    Returns (K [rank, d_k], U [rank, d_v], residual)."""
     Rm = np.array(M, dtype=np.float64, copy=True)
     d_k, d_v = Rm.shape
     K = np.zeros((rank, d_k))
@@ -93,10 +93,10 @@ def lowrank_fit(M: np.ndarray, rank: int, iters: int, init=None, exact: bool = F
             if sigma > 0.0:
                 sq = np.sqrt(sigma)
                 k, u = sq * a, b / sq
-        if not exact:
-            k, u = fp16_value(k), fp16_value(u)
-        if adopt is not None:
+        if adopt is not None and not exact:
             k, u = adopt(h, k, u)
+        elif not exact:
+            k, u = fp16_value(k), fp16_value(u)
         K[h], U[h] = k, u
         Rm = Rm - np.outer(k, u)
     return K, U, Rm
