@@ -7,16 +7,22 @@
 // Storage rows are ordered by (width, key row) and kept row-major, so a head
 // is a run of variable-length rows.  The workgroup stages the packed head in
 // LDS with coalesced 16-byte copies; lane (rb, p) extracts columns 2p, 2p+1
-// of its 32 storage rows (the width of a row is uniform across the wave),
-// writes the new codes back into the same LDS bytes and the head is copied
-// out with 16-byte stores.  Per-row inputs (d, k, q, w) are gathered through
-// the storage permutation.  Per element, with c' = c_j (integer rows) or 1
-// (FP16 rows) and rho_s the row's retained dequantisation factor:
-//   x = c' * value;   delta_j = sum_s kappa_s x_sj          (kappa = k rho)
-//   Xt = x + gamma_s e_j  (X = rho_s Xt, gamma = beta k / rho)
-//   y_j = sum_s theta_s Xt_sj                              (theta = q rho)
+// of its 32 storage rows, writes the new codes back into the same LDS bytes
+// and the head is copied out with 16-byte stores.  Because the rows are
+// sorted, the rows of one block that share a width are consecutive: the block
+// keeps one bit mask per width class and the byte offset of the class's first
+// row, so a row's width and offset are scalar values and every per-row branch
+// is a scalar branch to code specialised for that width.  Per-row inputs
+// (d, k, q, w) are gathered through the storage permutation.  Per element,
+// with rho_s the row's retained dequantisation factor (d_s r_s / q_b on
+// integer rows, d_s on FP16 rows):
+//   integer rows: x = c_j z;  kappa = k rho, gamma = beta k / rho,
+//                 theta = q rho, Xt = X / rho
+//   FP16 rows:    x = rho h;  kappa = k, gamma = beta k, theta = q, Xt = X
+//   delta_j = sum_s kappa_s x_sj,  Xt = x + gamma_s e_j,
+//   y_j = sum_s theta_s Xt_sj
 // then the GDN kernel's row scales, column init, codes by magic rounding
-// (per-row q_b) and fixed-code column refit over the integer rows.
+// (per-width q_b) and fixed-code column refit over the integer rows.
 #include <algorithm>
 
 #include "tile_common.h"
@@ -26,21 +32,33 @@ using namespace sqk;
 namespace {
 
 template <int DK, int DV>
-struct SmemKda {
-  float rowc[7][DK];  // 0 kappa, 1 gamma, 2 theta, 3 rho, 4 pi or rho (FP16 rows),
-                      // 5 lambda_N = w^2 r^2 / q_b, 6 lambda_D = w^2 r^2 / q_b^2
-  float qb[DK];       // q_b of storage row s (0 for FP16 rows)
-  int bits[DK];
-  int off[DK];
+struct SmemKdaCore {
+  float rowc[6][DK];  // 0 kappa, 1 gamma, 2 theta, 3 rho, 4 pi or rho (FP16 rows),
+                      // 5 lambda = w^2 r^2 / q_b (0 on FP16 rows)
   float2 colA[DK / 32][DV / 2];
   float2 colB[DK / 32][DV / 2];
   float2 colM[DK / 32][DV / 2];
   float4 colC[DK / 32][DV / 2];
 };
+// Row m of a width class is addressed as (class base - lo * row bytes) + m *
+// row bytes, the last term an instruction offset.  The first term may fall
+// below the dynamic buffer by up to 31 rows of the widest class; the static
+// block (placed before the dynamic one) is padded to at least that size, so
+// the address register never goes negative.
+template <int DK, int DV>
+constexpr int kda_pad() {
+  constexpr int need = 31 * 2 * DV, have = (int)sizeof(SmemKdaCore<DK, DV>);
+  return need > have ? need - have : 16;
+}
+template <int DK, int DV>
+struct SmemKda : SmemKdaCore<DK, DV> {
+  unsigned char pad[kda_pad<DK, DV>()];
+};
 
 // The packed head (at most max_code_bytes) and, while no codes are live,
 // the per-wave row transpose, share the dynamic LDS buffer; its last 16
-// bytes are a spare slot for staging stores past the head's region.
+// bytes are a spare slot for staging stores past the head's region (and
+// hold the second dword read for the last lanes of the last row).
 extern __shared__ uint4 kda_dyn[];
 
 template <int DK, int DV>
@@ -55,73 +73,142 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// A per-row value: with 64 lanes per row block every lane of a wave works on
-// the same storage row, so the value is wave-uniform and goes to a scalar
-// register (row-wise branches become scalar); with 32 lanes a wave spans two
-// row blocks and the value stays per lane.
-template <bool WU>
-__device__ __forceinline__ int rowu(int v) {
-  if constexpr (WU) return wuni(v);
-  else return v;
-}
-template <bool WU>
-__device__ __forceinline__ float rowu(float v) {
-  if constexpr (WU) return wuni(v);
-  else return v;
+// Width classes 2, 4, 6, 8 bits and FP16 (16).
+template <int B>
+struct Wc {
+  static constexpr int bits = B;
+  static constexpr int idx = B == 2 ? 0 : B == 4 ? 1 : B == 6 ? 2 : B == 8 ? 3 : 4;
+};
+
+// The width classes of one row block: bit m of msk[c] marks row m of the
+// block as class c (2, 4, 6, 8 bits, FP16).  rd[c] and wr[c] are byte
+// addresses, relative to the staged head, for row 0 of class c numbered from
+// the class's first row: row m of the class is read at rd[c] + m * (DV *
+// width / 8) (the dword holding the lane's first field bit) and written at
+// wr[c] + m * (DV * width / 8) (the lane's bytes).  With 64 lanes per block
+// the masks are wave-uniform (scalar registers); with 32 a wave holds two
+// blocks and they are per lane.
+struct RowCls {
+  uint32_t msk[5];
+  int rd[5], wr[5];
+};
+
+template <int DV, int C>
+constexpr int row_bytes() {
+  constexpr int W[5] = {2, 4, 6, 8, 16};
+  return DV * W[C] / 8;
 }
 
-// Two b-bit fields (columns 2p, 2p+1) of a row stored at byte `off` (rows
-// start on 16-byte boundaries; fields are two's complement, least significant
-// bit first).
-__device__ __forceinline__ void read_pair(const unsigned char* codes, int off, int b, int p,
-                                          float& z0, float& z1) {
-  const unsigned char* row = codes + off;
-  if (b == 16) {
-    const uint32_t v = reinterpret_cast<const uint32_t*>(row)[p];
-    z0 = half_from_bits(v);
-    z1 = half_from_bits(v >> 16);
-    return;
-  }
-  uint32_t f;
-  if (b == 8) {
-    f = reinterpret_cast<const unsigned short*>(row)[p];
-  } else if (b == 4) {
-    f = row[p];
-  } else if (b == 2) {
-    f = (uint32_t)row[p >> 1] >> (4 * (p & 1));
-  } else {  // 6 bits: the pair's 12 bits start at bit 12 p
-    const int i = (3 * p) >> 1;
-    f = ((uint32_t)row[i] | ((uint32_t)row[i + 1] << 8)) >> (4 * (p & 1));
-  }
-  // the builtin returns an unsigned type: reinterpret as signed before converting
-  z0 = (float)(int)__builtin_amdgcn_sbfe((int)f, 0, b);
-  z1 = (float)(int)__builtin_amdgcn_sbfe((int)f, b, b);
+// Call f(Wc<width>) for the class of row m (classes tested in order of their
+// share at a nominal 6 bits).
+template <class F>
+__device__ __forceinline__ void by_class(const RowCls& R, int m, F&& f) {
+  const uint32_t bit = 1u << m;
+  if (R.msk[2] & bit) f(Wc<6>{});
+  else if (R.msk[1] & bit) f(Wc<4>{});
+  else if (R.msk[3] & bit) f(Wc<8>{});
+  else if (R.msk[4] & bit) f(Wc<16>{});
+  else if (R.msk[0] & bit) f(Wc<2>{});
 }
 
-// Write the lane's two codes (magic-rounded floats m0, m1) of a b-bit row.
-// Rows are byte-aligned; 2- and 6-bit pairs share bytes with the next lane's,
-// so even lanes write both lanes' bits.
-__device__ __forceinline__ void write_pair(unsigned char* codes, int off, int b, int p, float m0,
-                                           float m1) {
+// lane i takes the value of lane i + n of its 16-lane row (n = 1, 2)
+template <int N>
+__device__ __forceinline__ uint32_t from_next(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x100 + N, 0xf, 0xf, false);
+}
+
+// The lane's two values (columns 2p, 2p+1) of a row of width B from the two
+// dwords lo, hi read at the dword holding the first field bit: two's-
+// complement integers starting at bit 2 B p of the row (the shift count of
+// the funnel shift is taken mod 32), or FP16 values (B = 16, dword p).
+template <int B>
+__device__ __forceinline__ void decode_pair(uint32_t lo, uint32_t hi, int p, float& z0, float& z1) {
+  if constexpr (B == 16) {
+    z0 = half_from_bits(lo);
+    z1 = half_from_bits(lo >> 16);
+  } else {
+    const uint32_t f = __builtin_amdgcn_alignbit(hi, lo, 2 * B * p);
+    // the builtin returns an unsigned type: reinterpret as signed before converting
+    z0 = (float)(int)__builtin_amdgcn_sbfe((int)f, 0, B);
+    z1 = (float)(int)__builtin_amdgcn_sbfe((int)f, B, B);
+  }
+}
+
+// Write the lane's two codes (magic-rounded floats m0, m1) of a row of width
+// B < 16; a is the lane's write address in the row.  2- and 6-bit fields of a
+// group of four lanes fill two or six bytes, which lanes of the group write as
+// 16-bit words (lane q of a 6-bit group writes bytes 2q, 2q+1).
+template <int B>
+__device__ __forceinline__ void write_pair(unsigned char* codes, int a, int p, float m0, float m1) {
   const uint32_t u0 = __float_as_uint(m0), u1 = __float_as_uint(m1);
-  if (b == 4) {
-    codes[off + p] = (unsigned char)((u0 & 15u) | ((u1 & 15u) << 4));
-  } else if (b == 8) {
-    *reinterpret_cast<unsigned short*>(codes + off + 2 * p) =
-        (unsigned short)((u0 & 0xffu) | ((u1 & 0xffu) << 8));
-  } else if (b == 2) {
+  if constexpr (B == 4) {
+    codes[a] = (unsigned char)((u0 & 15u) | ((u1 & 15u) << 4));
+  } else if constexpr (B == 8) {
+    *reinterpret_cast<unsigned short*>(codes + a) = (unsigned short)((u0 & 0xffu) | ((u1 & 0xffu) << 8));
+  } else if constexpr (B == 2) {
     const uint32_t nib = (u0 & 3u) | ((u1 & 3u) << 2);
-    const uint32_t nxt = __shfl_down(nib, 1);
-    if (!(p & 1)) codes[off + (p >> 1)] = (unsigned char)(nib | (nxt << 4));
-  } else {  // 6 bits: 12 bits per lane, 3 bytes per lane pair
+    const uint32_t n1 = nib | (from_next<1>(nib) << 4);
+    const uint32_t n2 = n1 | (from_next<2>(n1) << 8);
+    if ((p & 3) == 0) *reinterpret_cast<unsigned short*>(codes + a) = (unsigned short)n2;
+  } else {
     const uint32_t f = (u0 & 63u) | ((u1 & 63u) << 6);
-    const uint32_t nxt = __shfl_down(f, 1);
-    if (!(p & 1)) {
-      const uint32_t v = f | (nxt << 12);
-      unsigned char* d = codes + off + 3 * (p >> 1);
-      d[0] = (unsigned char)v;
-      d[1] = (unsigned char)(v >> 8);
-      d[2] = (unsigned char)(v >> 16);
+    const uint32_t nx = from_next<1>(f);
+    const int q = p & 3;
+    if (q < 3)
+      *reinterpret_cast<unsigned short*>(codes + a) =
+          (unsigned short)((f >> (4 * q)) | (nx << (12 - 4 * q)));
+  }
+}
+
+// Refit sums of one width class: D_c = sum_s lambda_s z^2 (divided by q_b at
+// the end), kept as named scalars so that a row's branch updates two of them.
+struct DSums {
+  float d2a = 0.f, d2b = 0.f, d4a = 0.f, d4b = 0.f, d6a = 0.f, d6b = 0.f, d8a = 0.f, d8b = 0.f;
+};
+template <int C>
+__device__ __forceinline__ void fma_d(DSums& D, float t0, float z0, float t1, float z1) {
+  if constexpr (C == 0) { D.d2a = fmaf(t0, z0, D.d2a); D.d2b = fmaf(t1, z1, D.d2b); }
+  else if constexpr (C == 1) { D.d4a = fmaf(t0, z0, D.d4a); D.d4b = fmaf(t1, z1, D.d4b); }
+  else if constexpr (C == 2) { D.d6a = fmaf(t0, z0, D.d6a); D.d6b = fmaf(t1, z1, D.d6b); }
+  else { D.d8a = fmaf(t0, z0, D.d8a); D.d8b = fmaf(t1, z1, D.d8b); }
+}
+
+// pass 4 over the lane's rows: codes by magic rounding with the per-width
+// scale tau[c] = q_b / c0_j, the fixed-code refit sums (N over all integer
+// rows, D per width) and the new codes (or FP16 values) written into the
+// staged head
+template <int DK, int DV, bool SAT>
+__device__ __forceinline__ void codes_refit(float (&x)[64], const RowCls& R, const float* lam,
+                                            const float (&tau)[4][2], unsigned char* codes, int p,
+                                            float& N0, float& N1, DSums& D) {
+#pragma unroll
+  for (int m4 = 0; m4 < 32; m4 += 4) {
+    const float4 l4 = *reinterpret_cast<const float4*>(lam + m4);
+    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int m = m4 + u;
+      by_class(R, m, [&](auto w) {
+        constexpr int B = decltype(w)::bits, C = decltype(w)::idx;
+        const int a = R.wr[C] + m * row_bytes<DV, C>();
+        if constexpr (B == 16) {
+          *reinterpret_cast<uint32_t*>(codes + a) = half_bits(x[2 * m]) | (half_bits(x[2 * m + 1]) << 16);
+        } else {
+          constexpr float QB = (float)((1 << (B - 1)) - 1);
+          const float pv0 = x[2 * m], pv1 = x[2 * m + 1];
+          float mg0 = fmaf(pv0, tau[C][0], kMagic), mg1 = fmaf(pv1, tau[C][1], kMagic);
+          if constexpr (SAT) {  // a column scale saturated at the FP16 maximum
+            mg0 = __builtin_amdgcn_fmed3f(mg0, kMagic - QB, kMagic + QB);
+            mg1 = __builtin_amdgcn_fmed3f(mg1, kMagic - QB, kMagic + QB);
+          }
+          const float z0 = mg0 - kMagic, z1 = mg1 - kMagic;
+          const float t0 = lv[u] * z0, t1 = lv[u] * z1;
+          N0 = fmaf(t0, pv0, N0);
+          N1 = fmaf(t1, pv1, N1);
+          fma_d<C>(D, t0, z0, t1, z1);
+          write_pair<B>(codes, a, p, mg0, mg1);
+        }
+      });
     }
   }
 }
@@ -148,14 +235,36 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   const int code_bytes = wuni(a.P.r_off[h]);
   __half* r_ptr = reinterpret_cast<__half*>(base + code_bytes);
   __half* c_ptr = reinterpret_cast<__half*>(base + wuni(a.P.c_off[h]));
-  // per-storage-row metadata of this wave's rows (loaded first: the key row
-  // indexes the token's inputs)
+  // per-storage-row metadata of the block's rows, held by the owner lanes
+  // p < 32 (loaded first: the key row indexes the token's inputs)
   int rk = 0, rbits = 16, roff = 0;
   if (p < 32) {
     const int s = r0 + p;
     rk = rkey[s];
     rbits = a.P.row_bits[h * DK + s];
     roff = a.P.row_off[h * DK + s];
+  }
+  // width classes of the block's rows and the lane's field addresses
+  static_assert((int)sizeof(SmemKda<DK, DV>) >= 31 * 2 * DV, "LDS address bases may go negative");
+  RowCls R;
+  {
+    constexpr int W[5] = {2, 4, 6, 8, 16};
+    const int lane = t & 63, half = WU ? 0 : (lane & 32);
+    // byte of the lane's fields in a row: read, and written (2 and 6 bits
+    // write per group of four lanes)
+    const int rdb[5] = {4 * (p >> 3), 4 * (p >> 2), 4 * ((12 * p) >> 5), 4 * (p >> 1), 4 * p};
+    const int wrb[5] = {2 * (p >> 2), p, 6 * (p >> 2) + 2 * (p & 3), 2 * p, 4 * p};
+#pragma unroll
+    for (int c = 0; c < 5; ++c) {
+      const unsigned long long bal = __ballot(p < 32 && rbits == W[c]);
+      const uint32_t mk = (uint32_t)(bal >> half);
+      const int lo = mk ? __builtin_ctz(mk) : 0;
+      const int first = WU ? __builtin_amdgcn_readlane(roff, lo) : __shfl(roff, half + lo);
+      const int b0 = first - lo * (DV * W[c] / 8);
+      R.msk[c] = mk;
+      R.rd[c] = b0 + rdb[c];
+      R.wr[c] = b0 + wrb[c];
+    }
   }
   float x[64];
   float y0 = 0.f, y1 = 0.f;
@@ -168,13 +277,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
       x[2 * m] = v2.x;
       x[2 * m + 1] = v2.y;
     }
-    if (p < 32) {
-      const int s = r0 + p;
-      sm.bits[s] = rbits;
-      sm.off[s] = roff;
-      sm.qb[s] = rbits == 16 ? 0.f : (float)((1 << (rbits - 1)) - 1);
-      sm.rowc[3][s] = 1.0f;
-    }
+    if (p < 32) sm.rowc[3][r0 + p] = 1.0f;
     __syncthreads();
   } else {
     // The head's code rows are staged through registers, CH 16-byte chunks
@@ -193,7 +296,6 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
       const int e = t + i * NT;
       v[i] = src[e < nch ? e : 0];
     }
-    // keep the key-indexed loads (which wait for the key rows) behind these
     const float c0 = __half2float(c_ptr[j0]), c1 = __half2float(c_ptr[j0 + 1]);
     float rs = 0.f, d = 0.f, kk = 0.f, qq = 0.f;
     if (p < 32) {
@@ -223,42 +325,73 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
       }
     }
     if (p < 32) {
-      const int s = r0 + p, b = rbits;
-      const float qb = b == 16 ? 0.f : (float)((1 << (b - 1)) - 1);
-      sm.bits[s] = b;
-      sm.off[s] = roff;
-      sm.qb[s] = qb;
-      const bool piv = b == 16;
+      const int s = r0 + p;
+      const bool piv = rbits == 16;
+      const float qb = piv ? 1.f : (float)((1 << (rbits - 1)) - 1);
       const float sc = piv ? 1.f : rs * frcp(qb);
       if constexpr (OP == OP_UNPACK) {
         sm.rowc[3][s] = sc;
+        sm.rowc[4][s] = 1.0f;
       } else {
         const float bk = beta * kk;
         const float rho = d * sc;
-        // a vanishing retention keeps the division finite; the dropped part
-        // (rp - rho) c_j z_sj is below 2^-60 of the write term
-        const float rp = fmaxf(rho, fmaxf(fabsf(bk) * 0x1p-60f, 0x1p-100f));
-        sm.rowc[0][s] = kk * rho;
-        sm.rowc[1][s] = bk * frcp(rp);
-        sm.rowc[2][s] = qq * rp;
-        sm.rowc[3][s] = rp;
+        if (piv) {
+          // FP16 rows keep X itself: the unpacked value is scaled by rho, so
+          // X = rho h + beta k e_j takes two roundings, as the stored FP16
+          // value needs
+          sm.rowc[0][s] = kk;
+          sm.rowc[1][s] = bk;
+          sm.rowc[2][s] = qq;
+          sm.rowc[3][s] = 1.0f;
+          sm.rowc[4][s] = rho;
+        } else {
+          // a vanishing retention keeps the division finite; the dropped part
+          // (rp - rho) c_j z_sj is below 2^-60 of the write term
+          const float rp = fmaxf(rho, fmaxf(fabsf(bk) * 0x1p-60f, 0x1p-100f));
+          sm.rowc[0][s] = kk * rho;
+          sm.rowc[1][s] = bk * frcp(rp);
+          sm.rowc[2][s] = qq * rp;
+          sm.rowc[3][s] = rp;
+        }
       }
     }
     __syncthreads();  // codes staged, per-row constants ready
+    // all rows' fields are read before any is decoded, so the LDS reads of
+    // the 32 rows overlap: the width only selects the address, and one
+    // two-dword read (outside the branches) serves every width; x holds the
+    // raw dwords in between
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
-      const int s = r0 + m;
-      const int b = rowu<WU>(sm.bits[s]);
-      float z0, z1;
-      read_pair(codes, rowu<WU>(sm.off[s]), b, p, z0, z1);
-      x[2 * m] = b == 16 ? z0 : c0 * z0;
-      x[2 * m + 1] = b == 16 ? z1 : c1 * z1;
+      int ad = 0;
+      by_class(R, m, [&](auto w) {
+        constexpr int C = decltype(w)::idx;
+        ad = R.rd[C] + m * row_bytes<DV, C>();
+      });
+      const uint32_t* dw = reinterpret_cast<const uint32_t*>(codes + ad);
+      x[2 * m] = __uint_as_float(dw[0]);
+      x[2 * m + 1] = __uint_as_float(dw[1]);
+    }
+#pragma unroll
+    for (int m = 0; m < 32; ++m) {
+      by_class(R, m, [&](auto w) {
+        constexpr int B = decltype(w)::bits;
+        float z0, z1;
+        decode_pair<B>(__float_as_uint(x[2 * m]), __float_as_uint(x[2 * m + 1]), p, z0, z1);
+        if constexpr (B == 16) {
+          const float f = sm.rowc[4][r0 + m];
+          x[2 * m] = f * z0;
+          x[2 * m + 1] = f * z1;
+        } else {
+          x[2 * m] = c0 * z0;
+          x[2 * m + 1] = c1 * z1;
+        }
+      });
     }
     if constexpr (OP == OP_UNPACK) {
       float* S = a.S_out + (long long)tile * DK * DV;
 #pragma unroll
       for (int m = 0; m < 32; ++m) {
-        const float f = sm.bits[r0 + m] == 16 ? 1.f : sm.rowc[3][r0 + m];
+        const float f = sm.rowc[3][r0 + m];
         *reinterpret_cast<float2*>(S + rkey[r0 + m] * DV + j0) = make_float2(f * x[2 * m], f * x[2 * m + 1]);
       }
       return;
@@ -327,36 +460,36 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
     const int si = r0 + p;
     const float s = p < 16 ? sh[0] : sh[1];
     const float rp = sm.rowc[3][si];
-    if (sm.bits[si] == 16) {
+    if (rbits == 16) {
       r_ptr[si] = __float2half_rn(0.0f);
-      sm.rowc[4][si] = rp;  // FP16 rows: X = rho Xt
+      sm.rowc[4][si] = rp;  // FP16 rows: X = Xt (row factor 1)
       sm.rowc[5][si] = 0.f;
-      sm.rowc[6][si] = 0.f;
     } else {
-      const int key = rkey[si];
-      const float wi = a.P.w[h * DK + key], iq = frcp(sm.qb[si]);
+      const float wi = a.P.w[h * DK + rk];
+      const float iq = frcp((float)((1 << (rbits - 1)) - 1));
       // the hardware square root (1 ulp) only feeds an FP16 rounding
       const float ri =
-          fp16_scale(__builtin_amdgcn_sqrtf(rp * s * (1.0f / (float)DV) * a.P.winv[h * DK + key]));
+          fp16_scale(__builtin_amdgcn_sqrtf(rp * s * (1.0f / (float)DV) * a.P.winv[h * DK + rk]));
       r_ptr[si] = __float2half_rn(ri);
-      const float ww = wi * wi * ri * ri * iq;
       sm.rowc[4][si] = rp * frcp(ri);
-      sm.rowc[5][si] = ww;
-      sm.rowc[6][si] = ww * iq;
+      sm.rowc[5][si] = wi * wi * ri * ri * iq;
     }
   }
   wave_sync();
   // pass 3: P = X / r on integer rows (column absmax), X on FP16 rows
   float mx0 = 0.f, mx1 = 0.f;
 #pragma unroll
-  for (int m = 0; m < 32; ++m) {
-    const int s = r0 + m;
-    const float f = sm.rowc[4][s];
-    x[2 * m] *= f;
-    x[2 * m + 1] *= f;
-    if (rowu<WU>(sm.bits[s]) != 16) {
-      mx0 = fmaxf(mx0, fabsf(x[2 * m]));
-      mx1 = fmaxf(mx1, fabsf(x[2 * m + 1]));
+  for (int m = 0; m < 32; m += 4) {
+    const float4 f4 = *reinterpret_cast<const float4*>(&sm.rowc[4][r0 + m]);
+    const float fv[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      x[2 * (m + u)] *= fv[u];
+      x[2 * (m + u) + 1] *= fv[u];
+      if (!(R.msk[4] & (1u << (m + u)))) {
+        mx0 = fmaxf(mx0, fabsf(x[2 * (m + u)]));
+        mx1 = fmaxf(mx1, fabsf(x[2 * (m + u) + 1]));
+      }
     }
   }
   sm.colM[rb][p] = make_float2(mx0, mx1);
@@ -378,35 +511,25 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   }
   const float cz0 = fp16_scale(m0), cz1 = fp16_scale(m1);
   const float ic0 = frcp(cz0), ic1 = frcp(cz1);
+  float tau[4][2];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float qb = (float)((1 << (2 * c + 1)) - 1);  // widths 2, 4, 6, 8
+    tau[c][0] = qb * ic0;
+    tau[c][1] = qb * ic1;
+  }
   // below the FP16 maximum every code lies within +-q_b unclamped; a wave
   // holding a saturated column clamps all its codes (a no-op on the others)
   const bool sat = __ballot(fmaxf(m0, m1) > kFp16Max) != 0ull;
-  // pass 4: codes (magic rounding, per-row q_b) and the refit sums; the new
-  // codes go into the staged head in place
-  float N0 = 0.f, N1 = 0.f, D0 = 0.f, D1 = 0.f;
-#pragma unroll
-  for (int m = 0; m < 32; ++m) {
-    const int s = r0 + m;
-    const int b = rowu<WU>(sm.bits[s]), off = rowu<WU>(sm.off[s]);
-    if (b == 16) {
-      *reinterpret_cast<uint32_t*>(codes + off + 4 * p) =
-          half_bits(x[2 * m]) | (half_bits(x[2 * m + 1]) << 16);
-      continue;
-    }
-    const float qb = rowu<WU>(sm.qb[s]), ln = sm.rowc[5][s], ld = sm.rowc[6][s];
-    const float pv0 = x[2 * m], pv1 = x[2 * m + 1];
-    float mg0 = fmaf(pv0, qb * ic0, kMagic), mg1 = fmaf(pv1, qb * ic1, kMagic);
-    if (sat) {  // a column scale saturated at the FP16 maximum
-      mg0 = __builtin_amdgcn_fmed3f(mg0, kMagic - qb, kMagic + qb);
-      mg1 = __builtin_amdgcn_fmed3f(mg1, kMagic - qb, kMagic + qb);
-    }
-    const float z0 = mg0 - kMagic, z1 = mg1 - kMagic;
-    N0 = fmaf(ln * z0, pv0, N0);
-    N1 = fmaf(ln * z1, pv1, N1);
-    D0 = fmaf(ld * z0, z0, D0);
-    D1 = fmaf(ld * z1, z1, D1);
-    write_pair(codes, off, b, p, mg0, mg1);
-  }
+  // pass 4: codes and the refit sums; the new codes go into the staged head
+  float N0 = 0.f, N1 = 0.f;
+  DSums Ds;
+  if (sat) codes_refit<DK, DV, true>(x, R, &sm.rowc[5][r0], tau, codes, p, N0, N1, Ds);
+  else codes_refit<DK, DV, false>(x, R, &sm.rowc[5][r0], tau, codes, p, N0, N1, Ds);
+  const float D0 = Ds.d2a + Ds.d4a * (1.0f / 7.0f) + Ds.d6a * (1.0f / 31.0f) +
+                   Ds.d8a * (1.0f / 127.0f);
+  const float D1 = Ds.d2b + Ds.d4b * (1.0f / 7.0f) + Ds.d6b * (1.0f / 31.0f) +
+                   Ds.d8b * (1.0f / 127.0f);
   sm.colC[rb][p] = make_float4(N0, N1, D0, D1);
   __syncthreads();
   for (int i = t * 16; i < code_bytes; i += NT * 16)

@@ -10,9 +10,10 @@ float64 and walks the quantizer one decision at a time:
   the two binary16 neighbours and the GPU chose the other neighbour.  The
   initial column scale c0 is not stored; where it is such a near-tie the
   oracle keeps whichever neighbour reproduces the GPU's codes of the column.
-  An FP16 pivot value is formed from two terms, D S_hat and beta k e^T; its
-  tie window also covers 4 fp32 ulps of those terms (where they cancel, fp32
-  cannot decide the rounding that float64 decides).
+  An FP16 pivot value is formed from two terms, D S_hat and beta k e^T, and
+  e_j = v_j - sum_i k_i (D S_hat)_ij is itself a float32 dot product; its tie
+  window also covers 4 fp32 ulps of the magnitudes of all those terms (where
+  they cancel, fp32 cannot decide the rounding that float64 decides).
 * integer codes: identical, except |dz| = 1 where the oracle's pre-rounding
   value is within 1e-3 code units of a half-integer (an exact tie up to fp32
   arithmetic);
@@ -143,9 +144,10 @@ def check_uniform(where, X, bits, gpu, rep: Report):
 
 
 def check_step(where, X, w, row_bits, gpu, rep: Report, mag=None):
-    """mag: elementwise |D S_hat| + |beta k e^T|, the size of the terms X is
-    formed from; a pivot value within 4 fp32 ulps of those terms of an FP16
-    rounding midpoint is an exact tie up to fp32 arithmetic."""
+    """mag: elementwise size of the terms X is formed from (|D S_hat|,
+    |beta k e^T| and |beta k_i| times the terms of e_j); a pivot value within
+    4 fp32 ulps of those terms of an FP16 rounding midpoint is an exact tie up
+    to fp32 arithmetic."""
     row_bits = np.asarray(row_bits)
     piv = row_bits == N.PIVOT_BITS
     keep = ~piv
@@ -273,7 +275,9 @@ def check_decode_head(where, desc, h, before: bytes, after: bytes, inp: dict, y_
     if mode == "uniform":
         check_uniform(where, X, int(desc["bits"]), st1, rep)
     else:
-        mag = np.abs(Sd) + np.abs(X - Sd)
+        # terms of X: D S_hat, beta k e^T, and those of the dot product e_j
+        e_terms = np.abs(inp["v"]) + np.abs(inp["k"]) @ np.abs(Sd)
+        mag = np.abs(Sd) + np.abs(X - Sd) + np.outer(np.abs(inp["beta"] * inp["k"]), e_terms)
         check_step(where, X, w, row_bits_of(desc, h), st1, rep, mag=mag)
 
 

@@ -46,7 +46,7 @@ def _compare_steps(pool, w, slots, steps, tiles):
     return rep
 
 
-@pytest.mark.parametrize("shape", [(128, 128), (64, 64)])
+@pytest.mark.parametrize("shape", [(128, 128), (64, 64), (128, 64), (64, 128)])
 def test_kda_decode_teacher_forced(shape):
     rng = np.random.default_rng(40 + shape[0])
     dk, dv = shape
