@@ -33,8 +33,9 @@ namespace {
 
 template <int DK, int DV>
 struct SmemKdaCore {
-  float rowc[6][DK];  // 0 kappa, 1 gamma, 2 theta, 3 rho, 4 pi or rho (FP16 rows),
-                      // 5 lambda = w^2 r^2 / q_b (0 on FP16 rows)
+  float rowc[8][DK];  // 0 kappa, 1 gamma, 2 theta, 3 rho, 4 pi or rho (FP16 rows),
+                      // 5 lambda = w^2 r^2 / q_b, 6 mu = lambda / q_b, 7 q_b
+                      // (5-7 are 0 on FP16 rows)
   float2 colA[DK / 32][DV / 2];
   float2 colB[DK / 32][DV / 2];
   float2 colM[DK / 32][DV / 2];
@@ -80,18 +81,43 @@ struct Wc {
   static constexpr int idx = B == 2 ? 0 : B == 4 ? 1 : B == 6 ? 2 : B == 8 ? 3 : 4;
 };
 
+// LDS accesses by byte address.  The lane's field addresses below are kept
+// as plain integers (passed through an empty asm) so that each row's access
+// is one register plus an instruction offset.
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) unsigned short lds_u16;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+__device__ __forceinline__ int lds_addr(const void* ptr) { return (int)(uintptr_t)(const lds_u8*)ptr; }
+__device__ __forceinline__ uint32_t lds_ld32(int a) { return *(const lds_u32*)(uintptr_t)a; }
+__device__ __forceinline__ void lds_st8(int a, uint32_t v) { *(lds_u8*)(uintptr_t)a = (unsigned char)v; }
+__device__ __forceinline__ void lds_st16(int a, uint32_t v) { *(lds_u16*)(uintptr_t)a = (unsigned short)v; }
+__device__ __forceinline__ void lds_st32(int a, uint32_t v) { *(lds_u32*)(uintptr_t)a = v; }
+
 // The width classes of one row block: bit m of msk[c] marks row m of the
-// block as class c (2, 4, 6, 8 bits, FP16).  rd[c] and wr[c] are byte
-// addresses, relative to the staged head, for row 0 of class c numbered from
-// the class's first row: row m of the class is read at rd[c] + m * (DV *
-// width / 8) (the dword holding the lane's first field bit) and written at
-// wr[c] + m * (DV * width / 8) (the lane's bytes).  With 64 lanes per block
-// the masks are wave-uniform (scalar registers); with 32 a wave holds two
-// blocks and they are per lane.
+// block as class c (2, 4, 6, 8 bits, FP16), and b0[c] is the LDS byte address
+// of a row 0 of class c numbered from the class's first row, so row m of the
+// class starts at b0[c] + m * (DV * width / 8).  With 64 lanes per block these
+// are wave-uniform (scalar registers); with 32 a wave holds two blocks and
+// they are per lane.
 struct RowCls {
   uint32_t msk[5];
-  int rd[5], wr[5];
+  int b0[5];
 };
+
+// Lane addresses of each class for one pass: the row start b0[c] plus the
+// lane's byte in the row, read (the dword holding the lane's first field
+// bit) or written (the lane's bytes; 2- and 6-bit fields are written per
+// group of four lanes).  Formed at the start of the pass that uses them.
+template <bool WRITE>
+__device__ __forceinline__ void lane_addrs(const RowCls& R, int p, int (&a)[5]) {
+  const int rdb[5] = {4 * (p >> 3), 4 * (p >> 2), 4 * ((12 * p) >> 5), 4 * (p >> 1), 4 * p};
+  const int wrb[5] = {2 * (p >> 2), p, 6 * (p >> 2) + 2 * (p & 3), 2 * p, 4 * p};
+#pragma unroll
+  for (int c = 0; c < 5; ++c) {
+    a[c] = R.b0[c] + (WRITE ? wrb[c] : rdb[c]);
+    asm volatile("" : "+v"(a[c]));
+  }
+}
 
 template <int DV, int C>
 constexpr int row_bytes() {
@@ -109,6 +135,18 @@ __device__ __forceinline__ void by_class(const RowCls& R, int m, F&& f) {
   else if (R.msk[3] & bit) f(Wc<8>{});
   else if (R.msk[4] & bit) f(Wc<16>{});
   else if (R.msk[0] & bit) f(Wc<2>{});
+}
+
+// Each pass over the rows tests the masks afresh: an empty asm that "changes"
+// them stops the compiler from carrying one pass's per-row tests into the
+// next as lane-mask values (whose use as a branch condition costs vector
+// instructions per row).
+template <bool WU>
+__device__ __forceinline__ void fresh_masks(RowCls& R) {
+  if constexpr (WU) {
+#pragma unroll
+    for (int c = 0; c < 5; ++c) asm volatile("" : "+s"(R.msk[c]));
+  }
 }
 
 // lane i takes the value of lane i + n of its 16-lane row (n = 1, 2)
@@ -139,75 +177,69 @@ __device__ __forceinline__ void decode_pair(uint32_t lo, uint32_t hi, int p, flo
 // group of four lanes fill two or six bytes, which lanes of the group write as
 // 16-bit words (lane q of a 6-bit group writes bytes 2q, 2q+1).
 template <int B>
-__device__ __forceinline__ void write_pair(unsigned char* codes, int a, int p, float m0, float m1) {
+__device__ __forceinline__ void write_pair(int a, int p, float m0, float m1) {
   const uint32_t u0 = __float_as_uint(m0), u1 = __float_as_uint(m1);
   if constexpr (B == 4) {
-    codes[a] = (unsigned char)((u0 & 15u) | ((u1 & 15u) << 4));
+    lds_st8(a, (u0 & 15u) | ((u1 & 15u) << 4));
   } else if constexpr (B == 8) {
-    *reinterpret_cast<unsigned short*>(codes + a) = (unsigned short)((u0 & 0xffu) | ((u1 & 0xffu) << 8));
+    lds_st16(a, (u0 & 0xffu) | ((u1 & 0xffu) << 8));
   } else if constexpr (B == 2) {
     const uint32_t nib = (u0 & 3u) | ((u1 & 3u) << 2);
     const uint32_t n1 = nib | (from_next<1>(nib) << 4);
     const uint32_t n2 = n1 | (from_next<2>(n1) << 8);
-    if ((p & 3) == 0) *reinterpret_cast<unsigned short*>(codes + a) = (unsigned short)n2;
+    if ((p & 3) == 0) lds_st16(a, n2);
   } else {
     const uint32_t f = (u0 & 63u) | ((u1 & 63u) << 6);
     const uint32_t nx = from_next<1>(f);
     const int q = p & 3;
-    if (q < 3)
-      *reinterpret_cast<unsigned short*>(codes + a) =
-          (unsigned short)((f >> (4 * q)) | (nx << (12 - 4 * q)));
+    if (q < 3) lds_st16(a, (f >> (4 * q)) | (nx << (12 - 4 * q)));
   }
 }
 
-// Refit sums of one width class: D_c = sum_s lambda_s z^2 (divided by q_b at
-// the end), kept as named scalars so that a row's branch updates two of them.
-struct DSums {
-  float d2a = 0.f, d2b = 0.f, d4a = 0.f, d4b = 0.f, d6a = 0.f, d6b = 0.f, d8a = 0.f, d8b = 0.f;
-};
-template <int C>
-__device__ __forceinline__ void fma_d(DSums& D, float t0, float z0, float t1, float z1) {
-  if constexpr (C == 0) { D.d2a = fmaf(t0, z0, D.d2a); D.d2b = fmaf(t1, z1, D.d2b); }
-  else if constexpr (C == 1) { D.d4a = fmaf(t0, z0, D.d4a); D.d4b = fmaf(t1, z1, D.d4b); }
-  else if constexpr (C == 2) { D.d6a = fmaf(t0, z0, D.d6a); D.d6b = fmaf(t1, z1, D.d6b); }
-  else { D.d8a = fmaf(t0, z0, D.d8a); D.d8b = fmaf(t1, z1, D.d8b); }
-}
-
-// pass 4 over the lane's rows: codes by magic rounding with the per-width
-// scale tau[c] = q_b / c0_j, the fixed-code refit sums (N over all integer
-// rows, D per width) and the new codes (or FP16 values) written into the
-// staged head
+// pass 4 over the lane's rows: codes by magic rounding with the scale
+// q_b / c0_j (q_b of each row from the row table, the magic constant mgc
+// held in a scalar register), the
+// fixed-code refit sums N = sum_s lambda_s z P and D = sum_s mu_s z^2, the
+// same arithmetic on every row (an FP16 row has q_b = 0, so z = 0, and zero
+// weights), then the new codes (or FP16 values) written into the staged head
+// by code specialised for the row's width
 template <int DK, int DV, bool SAT>
 __device__ __forceinline__ void codes_refit(float (&x)[64], const RowCls& R, const float* lam,
-                                            const float (&tau)[4][2], unsigned char* codes, int p,
-                                            float& N0, float& N1, DSums& D) {
+                                            const float* mu, const float* qbr, float ic0,
+                                            float ic1, float mgc, int p, float& N0, float& N1,
+                                            float& D0, float& D1) {
+  int wra[5];
+  lane_addrs<true>(R, p, wra);
 #pragma unroll
   for (int m4 = 0; m4 < 32; m4 += 4) {
     const float4 l4 = *reinterpret_cast<const float4*>(lam + m4);
-    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+    const float4 u4 = *reinterpret_cast<const float4*>(mu + m4);
+    const float4 q4 = *reinterpret_cast<const float4*>(qbr + m4);
+    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
+    const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int m = m4 + u;
+      const float qb = qv[u];
+      const float pv0 = x[2 * m], pv1 = x[2 * m + 1];
+      float mg0 = fmaf(pv0, qb * ic0, mgc), mg1 = fmaf(pv1, qb * ic1, mgc);
+      if constexpr (SAT) {  // a column scale saturated at the FP16 maximum
+        mg0 = __builtin_amdgcn_fmed3f(mg0, mgc - qb, mgc + qb);
+        mg1 = __builtin_amdgcn_fmed3f(mg1, mgc - qb, mgc + qb);
+      }
+      const float z0 = mg0 - mgc, z1 = mg1 - mgc;
+      N0 = fmaf(lv[u] * z0, pv0, N0);
+      N1 = fmaf(lv[u] * z1, pv1, N1);
+      D0 = fmaf(uv[u] * z0, z0, D0);
+      D1 = fmaf(uv[u] * z1, z1, D1);
+      // the sums are complete here: kept from sinking below the writes, which
+      // would hold every row's rounded values live at once
+      asm volatile("" : "+v"(N0), "+v"(N1), "+v"(D0), "+v"(D1));
       by_class(R, m, [&](auto w) {
         constexpr int B = decltype(w)::bits, C = decltype(w)::idx;
-        const int a = R.wr[C] + m * row_bytes<DV, C>();
-        if constexpr (B == 16) {
-          *reinterpret_cast<uint32_t*>(codes + a) = half_bits(x[2 * m]) | (half_bits(x[2 * m + 1]) << 16);
-        } else {
-          constexpr float QB = (float)((1 << (B - 1)) - 1);
-          const float pv0 = x[2 * m], pv1 = x[2 * m + 1];
-          float mg0 = fmaf(pv0, tau[C][0], kMagic), mg1 = fmaf(pv1, tau[C][1], kMagic);
-          if constexpr (SAT) {  // a column scale saturated at the FP16 maximum
-            mg0 = __builtin_amdgcn_fmed3f(mg0, kMagic - QB, kMagic + QB);
-            mg1 = __builtin_amdgcn_fmed3f(mg1, kMagic - QB, kMagic + QB);
-          }
-          const float z0 = mg0 - kMagic, z1 = mg1 - kMagic;
-          const float t0 = lv[u] * z0, t1 = lv[u] * z1;
-          N0 = fmaf(t0, pv0, N0);
-          N1 = fmaf(t1, pv1, N1);
-          fma_d<C>(D, t0, z0, t1, z1);
-          write_pair<B>(codes, a, p, mg0, mg1);
-        }
+        const int a = wra[C] + m * row_bytes<DV, C>();
+        if constexpr (B == 16) lds_st32(a, half_bits(pv0) | (half_bits(pv1) << 16));
+        else write_pair<B>(a, p, mg0, mg1);
       });
     }
   }
@@ -250,20 +282,14 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   {
     constexpr int W[5] = {2, 4, 6, 8, 16};
     const int lane = t & 63, half = WU ? 0 : (lane & 32);
-    // byte of the lane's fields in a row: read, and written (2 and 6 bits
-    // write per group of four lanes)
-    const int rdb[5] = {4 * (p >> 3), 4 * (p >> 2), 4 * ((12 * p) >> 5), 4 * (p >> 1), 4 * p};
-    const int wrb[5] = {2 * (p >> 2), p, 6 * (p >> 2) + 2 * (p & 3), 2 * p, 4 * p};
 #pragma unroll
     for (int c = 0; c < 5; ++c) {
       const unsigned long long bal = __ballot(p < 32 && rbits == W[c]);
       const uint32_t mk = (uint32_t)(bal >> half);
       const int lo = mk ? __builtin_ctz(mk) : 0;
       const int first = WU ? __builtin_amdgcn_readlane(roff, lo) : __shfl(roff, half + lo);
-      const int b0 = first - lo * (DV * W[c] / 8);
       R.msk[c] = mk;
-      R.rd[c] = b0 + rdb[c];
-      R.wr[c] = b0 + wrb[c];
+      R.b0[c] = lds_addr(codes) + first - lo * (DV * W[c] / 8);
     }
   }
   float x[64];
@@ -356,6 +382,9 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
       }
     }
     __syncthreads();  // codes staged, per-row constants ready
+    fresh_masks<WU>(R);
+    int rda[5];
+    lane_addrs<false>(R, p, rda);
     // all rows' fields are read before any is decoded, so the LDS reads of
     // the 32 rows overlap: the width only selects the address, and one
     // two-dword read (outside the branches) serves every width; x holds the
@@ -365,12 +394,12 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
       int ad = 0;
       by_class(R, m, [&](auto w) {
         constexpr int C = decltype(w)::idx;
-        ad = R.rd[C] + m * row_bytes<DV, C>();
+        ad = rda[C] + m * row_bytes<DV, C>();
       });
-      const uint32_t* dw = reinterpret_cast<const uint32_t*>(codes + ad);
-      x[2 * m] = __uint_as_float(dw[0]);
-      x[2 * m + 1] = __uint_as_float(dw[1]);
+      x[2 * m] = __uint_as_float(lds_ld32(ad));
+      x[2 * m + 1] = __uint_as_float(lds_ld32(ad + 4));
     }
+    fresh_masks<WU>(R);
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
       by_class(R, m, [&](auto w) {
@@ -464,18 +493,24 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
       r_ptr[si] = __float2half_rn(0.0f);
       sm.rowc[4][si] = rp;  // FP16 rows: X = Xt (row factor 1)
       sm.rowc[5][si] = 0.f;
+      sm.rowc[6][si] = 0.f;
+      sm.rowc[7][si] = 0.f;
     } else {
       const float wi = a.P.w[h * DK + rk];
-      const float iq = frcp((float)((1 << (rbits - 1)) - 1));
+      const float qb = (float)((1 << (rbits - 1)) - 1), iq = frcp(qb);
       // the hardware square root (1 ulp) only feeds an FP16 rounding
       const float ri =
           fp16_scale(__builtin_amdgcn_sqrtf(rp * s * (1.0f / (float)DV) * a.P.winv[h * DK + rk]));
       r_ptr[si] = __float2half_rn(ri);
       sm.rowc[4][si] = rp * frcp(ri);
-      sm.rowc[5][si] = wi * wi * ri * ri * iq;
+      const float lam = wi * wi * ri * ri * iq;
+      sm.rowc[5][si] = lam;
+      sm.rowc[6][si] = lam * iq;
+      sm.rowc[7][si] = qb;
     }
   }
   wave_sync();
+  fresh_masks<WU>(R);
   // pass 3: P = X / r on integer rows (column absmax), X on FP16 rows
   float mx0 = 0.f, mx1 = 0.f;
 #pragma unroll
@@ -511,25 +546,20 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   }
   const float cz0 = fp16_scale(m0), cz1 = fp16_scale(m1);
   const float ic0 = frcp(cz0), ic1 = frcp(cz1);
-  float tau[4][2];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const float qb = (float)((1 << (2 * c + 1)) - 1);  // widths 2, 4, 6, 8
-    tau[c][0] = qb * ic0;
-    tau[c][1] = qb * ic1;
-  }
   // below the FP16 maximum every code lies within +-q_b unclamped; a wave
   // holding a saturated column clamps all its codes (a no-op on the others)
   const bool sat = __ballot(fmaxf(m0, m1) > kFp16Max) != 0ull;
   // pass 4: codes and the refit sums; the new codes go into the staged head
-  float N0 = 0.f, N1 = 0.f;
-  DSums Ds;
-  if (sat) codes_refit<DK, DV, true>(x, R, &sm.rowc[5][r0], tau, codes, p, N0, N1, Ds);
-  else codes_refit<DK, DV, false>(x, R, &sm.rowc[5][r0], tau, codes, p, N0, N1, Ds);
-  const float D0 = Ds.d2a + Ds.d4a * (1.0f / 7.0f) + Ds.d6a * (1.0f / 31.0f) +
-                   Ds.d8a * (1.0f / 127.0f);
-  const float D1 = Ds.d2b + Ds.d4b * (1.0f / 7.0f) + Ds.d6b * (1.0f / 31.0f) +
-                   Ds.d8b * (1.0f / 127.0f);
+  float N0 = 0.f, N1 = 0.f, D0 = 0.f, D1 = 0.f;
+  float mgc = kMagic;
+  asm volatile("" : "+s"(mgc));
+  fresh_masks<WU>(R);
+  if (sat)
+    codes_refit<DK, DV, true>(x, R, &sm.rowc[5][r0], &sm.rowc[6][r0], &sm.rowc[7][r0], ic0, ic1,
+                              mgc, p, N0, N1, D0, D1);
+  else
+    codes_refit<DK, DV, false>(x, R, &sm.rowc[5][r0], &sm.rowc[6][r0], &sm.rowc[7][r0], ic0, ic1,
+                               mgc, p, N0, N1, D0, D1);
   sm.colC[rb][p] = make_float4(N0, N1, D0, D1);
   __syncthreads();
   for (int i = t * 16; i < code_bytes; i += NT * 16)
