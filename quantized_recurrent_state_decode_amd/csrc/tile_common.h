@@ -223,6 +223,56 @@ __device__ __forceinline__ float wuni(float v) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
 
+// LDS accesses by byte address.  An address kept as a plain integer (passed
+// through an empty asm) stays in one register, and the accesses built on it
+// carry their constant parts as instruction offsets.
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) unsigned short lds_u16;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+__device__ __forceinline__ int lds_addr(const void* ptr) { return (int)(uintptr_t)(const lds_u8*)ptr; }
+__device__ __forceinline__ uint32_t lds_ld32(int a) { return *(const lds_u32*)(uintptr_t)a; }
+__device__ __forceinline__ float4 lds_ld4(int a) {
+  const f32x4 v = *(const lds_f32x4*)(uintptr_t)a;
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void lds_st8(int a, uint32_t v) { *(lds_u8*)(uintptr_t)a = (unsigned char)v; }
+__device__ __forceinline__ void lds_st16(int a, uint32_t v) { *(lds_u16*)(uintptr_t)a = (unsigned short)v; }
+__device__ __forceinline__ void lds_st32(int a, uint32_t v) { *(lds_u32*)(uintptr_t)a = v; }
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Lane i of a 16-lane row takes the value of the lane the DPP control names
+// (quad_perm 0xB1: xor 1, 0x4E: xor 2; 0x141: half-row mirror; 0x140: row mirror).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// Sum over the 16 lanes of each row, in every lane of the row.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return v;
+}
+// Combination of each lane's value with the lane 16 (swap16) or 32 (swap32)
+// away: v_permlane16/32_swap exchange the odd 16-lane rows (the upper 32
+// lanes) of one copy with the even rows (lower 32 lanes) of the other.
+__device__ __forceinline__ void swap16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ bool resolve_tile(const TileArgs& a, int tile, int& h,
                                              unsigned char*& base) {
   if (a.out) {  // quantize-only: head head_ids[tile], or tile % H without ids

@@ -45,7 +45,6 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
 // Rows m .. m + R - 1 of both columns go into one output dword: R = 4 at 4 bits
 // (rows 4d .. 4d+3), 2 at 8 bits, 8 at 2 bits.  6-bit fields straddle dwords
@@ -80,8 +79,8 @@ __device__ __forceinline__ void pack_rows6(const float* mg, uint32_t* w) {
 // Codes by magic rounding and the fixed-code weighted least-squares column
 // sums (N_j, D_j), packed into w as they are produced.
 template <int BITS, bool CLAMP>
-__device__ __forceinline__ void codes_refit(float (&x)[64], const float* lam, float tau0,
-                                            float tau1, float4& nd, uint32_t (&w)[2 * BITS]) {
+__device__ __forceinline__ void codes_refit(float (&x)[64], int lam, float tau0, float tau1,
+                                            float4& nd, uint32_t (&w)[2 * BITS]) {
   constexpr float QB = (float)((1 << (BITS - 1)) - 1);
   constexpr int R = BITS == 6 ? 8 : 16 / BITS;   // rows per output dword (3 dwords at 6 bits)
   constexpr int RG = R < 4 ? 4 : R;              // rows per ordered group
@@ -97,7 +96,7 @@ __device__ __forceinline__ void codes_refit(float (&x)[64], const float* lam, fl
     }
 #pragma unroll
     for (int m = g; m < g + RG; m += 4) {
-      const float4 l4 = ld4(lam + m);
+      const float4 l4 = lds_ld4(lam + 4 * m);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -135,13 +134,12 @@ __device__ __forceinline__ void codes_refit(float (&x)[64], const float* lam, fl
 
 // Uniform rowwise codes: magic rounding of Xt * sigma_i, packed into w.
 template <int BITS>
-__device__ __forceinline__ void codes_rowwise(float (&x)[64], const float* sig,
-                                              uint32_t (&w)[2 * BITS]) {
+__device__ __forceinline__ void codes_rowwise(float (&x)[64], int sig, uint32_t (&w)[2 * BITS]) {
   constexpr float QB = (float)((1 << (BITS - 1)) - 1);
   constexpr int R = BITS == 6 ? 4 : 16 / BITS;
 #pragma unroll
   for (int m = 0; m < 32; m += 4) {
-    const float4 s4 = ld4(sig + m);
+    const float4 s4 = lds_ld4(sig + 4 * m);
     const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -170,6 +168,8 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
   const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p;
   const int r0 = 32 * rb;                     // first row of this lane's block
   constexpr int op = OP;
+  // LDS address of row r0 of the per-row constants (array k at + 4 k DK)
+  const int rcb = lds_addr(&sm.rowc[0][r0]);
   __half* rs_ptr = reinterpret_cast<__half*>(base + wuni(a.P.r_off[h]));
   __half* c_ptr = UNI ? nullptr : reinterpret_cast<__half*>(base + wuni(a.P.c_off[h]));
   const long long tk = (long long)tile * DK, tv = (long long)tile * DV;
@@ -197,7 +197,7 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
     if (p < 32) {
       const int i = r0 + p;
       const float rsi = __half2float(rs_ptr[i]);
-      const float sc = UNI ? rsi : rsi / QB;  // dequantisation row factor
+      const float sc = UNI ? rsi : rsi * (1.0f / QB);  // dequantisation row factor
       if (op == OP_UNPACK) {
         sm.rowc[3][i] = sc;
       } else {
@@ -212,11 +212,12 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
         sm.rowc[1][i] = bk * frcp(rp);     // gamma
         sm.rowc[2][i] = qq * rp;           // theta: readout weight on Xt
         sm.rowc[3][i] = rp;
-        // sum of kappa over the block's 32 rows (offset of the unpacked codes)
-        float ksum = kap;
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) ksum += __shfl_xor(ksum, o);
-        if (p == 0) sm.ksum[rb] = ksum;
+        // sum of kappa over the block's 32 rows (offset of the unpacked codes):
+        // each 16-lane row sums its lanes, then row_bcast:15 adds the first
+        // row's total into the second (row mask 0b1010), read at p = 16
+        float ksum = row16_sum(kap);
+        ksum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ksum), 0x142, 0xa, 0xf, false));
+        if (p == 16) sm.ksum[rb] = ksum;
       }
     }
     unpack_offset<BITS>(wd, x);
@@ -236,7 +237,7 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int m = 0; m < 32; m += 4) {
-      const float4 k4 = ld4(&sm.rowc[0][r0 + m]);
+      const float4 k4 = lds_ld4(rcb + 4 * (0 * DK + m));
       const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -259,7 +260,7 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
     const float o0 = -OFF * c0, o1 = -OFF * c1;
 #pragma unroll
     for (int m = 0; m < 32; m += 4) {
-      const float4 g4 = ld4(&sm.rowc[1][r0 + m]), t4 = ld4(&sm.rowc[2][r0 + m]);
+      const float4 g4 = lds_ld4(rcb + 4 * (1 * DK + m)), t4 = lds_ld4(rcb + 4 * (2 * DK + m));
       const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, tv4[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -294,10 +295,14 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
       const float vv = sm.rowt[rb][mm][part * 16 + pp];
       s = UNI ? fmaxf(s, vv) : s + vv;
     }
-#pragma unroll
-    for (int o = 16; o < NP; o <<= 1) {
-      const float ov = __shfl_xor(s, o);
-      s = UNI ? fmaxf(s, ov) : s + ov;
+    {  // combine the parts 16 (and 32) lanes apart
+      float a0, b0;
+      swap16(s, a0, b0);
+      s = UNI ? fmaxf(a0, b0) : a0 + b0;
+      if constexpr (NP == 64) {
+        swap32(s, a0, b0);
+        s = UNI ? fmaxf(a0, b0) : a0 + b0;
+      }
     }
     sh[hf] = s;
     wave_sync();
@@ -334,13 +339,13 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
         *reinterpret_cast<float2*>(a.y + tv + j0) = make_float2(s0, s1);
       }
     }
-    codes_rowwise<BITS>(x, &sm.rowc[4][r0], wd);
+    codes_rowwise<BITS>(x, rcb + 4 * (4 * DK), wd);
   } else {
     // pass 3: P = X / r_i and the column absmax
     float mx0 = 0.f, mx1 = 0.f;
 #pragma unroll
     for (int m = 0; m < 32; m += 4) {
-      const float4 p4 = ld4(&sm.rowc[4][r0 + m]);
+      const float4 p4 = lds_ld4(rcb + 4 * (4 * DK + m));
       const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -378,8 +383,8 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
     const bool sat = __ballot(fmaxf(m0, m1) > kFp16Max) != 0ull;
     // pass 4: codes by magic rounding, fixed-code weighted least-squares sums
     float4 nd;
-    if (sat) codes_refit<BITS, true>(x, &sm.rowc[5][r0], tau0, tau1, nd, wd);
-    else codes_refit<BITS, false>(x, &sm.rowc[5][r0], tau0, tau1, nd, wd);
+    if (sat) codes_refit<BITS, true>(x, rcb + 4 * (5 * DK), tau0, tau1, nd, wd);
+    else codes_refit<BITS, false>(x, rcb + 4 * (5 * DK), tau0, tau1, nd, wd);
     sm.colC[rb][p] = nd;
     __syncthreads();
     if (rb == 0) {

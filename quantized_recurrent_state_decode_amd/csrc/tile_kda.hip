@@ -81,18 +81,6 @@ struct Wc {
   static constexpr int idx = B == 2 ? 0 : B == 4 ? 1 : B == 6 ? 2 : B == 8 ? 3 : 4;
 };
 
-// LDS accesses by byte address.  The lane's field addresses below are kept
-// as plain integers (passed through an empty asm) so that each row's access
-// is one register plus an instruction offset.
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-typedef __attribute__((address_space(3))) unsigned short lds_u16;
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
-__device__ __forceinline__ int lds_addr(const void* ptr) { return (int)(uintptr_t)(const lds_u8*)ptr; }
-__device__ __forceinline__ uint32_t lds_ld32(int a) { return *(const lds_u32*)(uintptr_t)a; }
-__device__ __forceinline__ void lds_st8(int a, uint32_t v) { *(lds_u8*)(uintptr_t)a = (unsigned char)v; }
-__device__ __forceinline__ void lds_st16(int a, uint32_t v) { *(lds_u16*)(uintptr_t)a = (unsigned short)v; }
-__device__ __forceinline__ void lds_st32(int a, uint32_t v) { *(lds_u32*)(uintptr_t)a = v; }
-
 // The width classes of one row block: bit m of msk[c] marks row m of the
 // block as class c (2, 4, 6, 8 bits, FP16), and b0[c] is the LDS byte address
 // of a row 0 of class c numbered from the class's first row, so row m of the
@@ -256,26 +244,50 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   float(*rowt)[16][NP + 1] = reinterpret_cast<float(*)[16][NP + 1]>(kda_dyn);
   const int tile = blockIdx.x;
   const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p, r0 = 32 * rb;
-  int h = 0;
-  unsigned char* base = nullptr;
-  if (!resolve_tile(a, tile, h, base)) {
-    if (OP == OP_DECODE && t < DV) a.y[(long long)tile * DV + t] = __builtin_nanf("");
-    return;
-  }
   const long long tk = (long long)tile * DK, tv = (long long)tile * DV;
+  // The loads that do not depend on the slot go out before the slot is
+  // resolved: the head's row metadata (the owner lanes p < 32 hold storage
+  // row r0 + p) and, once the key rows arrive, the token's per-row inputs.
+  // The slot id travels alongside, so a tile's start waits on two round
+  // trips (slot -> codes, metadata -> inputs) rather than three.
+  int h = 0, slot = 0;
+  unsigned char* base = nullptr;
+  bool ok = true;
+  if (a.out) {
+    ok = resolve_tile(a, tile, h, base);
+  } else {
+    const int bi = tile / a.P.H;
+    h = tile - bi * a.P.H;
+    slot = wuni(a.slots[bi]);
+  }
   const int* rkey = a.P.row_key + h * DK;
-  const int code_bytes = wuni(a.P.r_off[h]);
-  __half* r_ptr = reinterpret_cast<__half*>(base + code_bytes);
-  __half* c_ptr = reinterpret_cast<__half*>(base + wuni(a.P.c_off[h]));
-  // per-storage-row metadata of the block's rows, held by the owner lanes
-  // p < 32 (loaded first: the key row indexes the token's inputs)
   int rk = 0, rbits = 16, roff = 0;
-  if (p < 32) {
+  if (ok && p < 32) {
     const int s = r0 + p;
     rk = rkey[s];
     rbits = a.P.row_bits[h * DK + s];
     roff = a.P.row_off[h * DK + s];
   }
+  float d = 0.f, kk = 0.f, qq = 0.f, beta = 0.f;
+  if constexpr (OP == OP_DECODE) {
+    if (ok && p < 32) {
+      d = a.gate[tk + rk];
+      kk = a.k[tk + rk];
+      qq = a.q[tk + rk];
+    }
+    beta = a.beta[tile];
+  }
+  if (!a.out) {
+    ok = slot >= 0 && (long long)slot < a.n_slots;
+    base = a.pool + (long long)(ok ? slot : 0) * a.P.slot_bytes + wuni(a.P.head_off[h]);
+  }
+  if (!ok) {
+    if (OP == OP_DECODE && t < DV) a.y[(long long)tile * DV + t] = __builtin_nanf("");
+    return;
+  }
+  const int code_bytes = wuni(a.P.r_off[h]);
+  __half* r_ptr = reinterpret_cast<__half*>(base + code_bytes);
+  __half* c_ptr = reinterpret_cast<__half*>(base + wuni(a.P.c_off[h]));
   // width classes of the block's rows and the lane's field addresses
   static_assert((int)sizeof(SmemKda<DK, DV>) >= 31 * 2 * DV, "LDS address bases may go negative");
   RowCls R;
@@ -314,40 +326,34 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
     constexpr int CH = 4;
     const int nch = code_bytes >> 4;
     const int spare = dyn_bytes<DK, DV>(a.P.max_code_bytes) / 16 - 1;
-    const uint4* src = reinterpret_cast<const uint4*>(base);
-    uint4* dst = reinterpret_cast<uint4*>(codes);
-    uint4 v[CH];
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4* src = reinterpret_cast<const u32x4*>(base);
+    u32x4* dst = reinterpret_cast<u32x4*>(codes);
+    u32x4 v[CH];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {  // first round, issued before the per-row inputs
+    for (int i = 0; i < CH; ++i) {  // first round, issued before the scale loads
       const int e = t + i * NT;
       v[i] = src[e < nch ? e : 0];
     }
     const float c0 = __half2float(c_ptr[j0]), c1 = __half2float(c_ptr[j0 + 1]);
-    float rs = 0.f, d = 0.f, kk = 0.f, qq = 0.f;
-    if (p < 32) {
-      rs = __half2float(r_ptr[r0 + p]);
-      if constexpr (OP == OP_DECODE) {
-        d = a.gate[tk + rk];
-        kk = a.k[tk + rk];
-        qq = a.q[tk + rk];
-      }
-    }
-    const float beta = OP == OP_DECODE ? a.beta[tile] : 0.f;
+    float rs = 0.f;
+    if (p < 32) rs = __half2float(r_ptr[r0 + p]);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int e = t + i * NT;
       dst[e < nch ? e : spare] = v[i];
     }
     for (int c = CH * NT; c < nch; c += CH * NT) {  // heads larger than one round
+      u32x4 w[CH];
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const int e = c + t + i * NT;
-        v[i] = src[e < nch ? e : 0];
+        w[i] = src[e < nch ? e : 0];
       }
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const int e = c + t + i * NT;
-        dst[e < nch ? e : spare] = v[i];
+        dst[e < nch ? e : spare] = w[i];
       }
     }
     if (p < 32) {
