@@ -199,14 +199,14 @@ __device__ __forceinline__ void codes_refit(float (&x)[64], const RowCls& R, con
   int wra[5];
   lane_addrs<true>(R, p, wra);
 #pragma unroll
-  for (int m4 = 0; m4 < 32; m4 += 4) {
-    const float4 l4 = *reinterpret_cast<const float4*>(lam + m4);
-    const float4 u4 = *reinterpret_cast<const float4*>(mu + m4);
-    const float4 q4 = *reinterpret_cast<const float4*>(qbr + m4);
-    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
-    const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
+  for (int m4 = 0; m4 < 32; m4 += 2) {
+    const float2 l4 = *reinterpret_cast<const float2*>(lam + m4);
+    const float2 u4 = *reinterpret_cast<const float2*>(mu + m4);
+    const float2 q4 = *reinterpret_cast<const float2*>(qbr + m4);
+    const float lv[2] = {l4.x, l4.y}, uv[2] = {u4.x, u4.y};
+    const float qv[2] = {q4.x, q4.y};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2; ++u) {
       const int m = m4 + u;
       const float qb = qv[u];
       const float pv0 = x[2 * m], pv1 = x[2 * m + 1];
@@ -235,7 +235,7 @@ __device__ __forceinline__ void codes_refit(float (&x)[64], const RowCls& R, con
 
 template <int DK, int DV, int OP>
 __global__ __launch_bounds__((DK / 32) * (DV / 2))
-__attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
+__attribute__((amdgpu_waves_per_eu(5, 8))) void kda_tile_kernel(TileArgs a) {
   using G = Geo<DK, DV>;
   constexpr int NP = G::NP, NRB = G::NRB, NT = G::NT;
   constexpr bool WU = NP % 64 == 0;  // a wave's lanes share their rows
