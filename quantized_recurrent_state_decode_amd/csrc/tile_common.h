@@ -259,6 +259,13 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f<0x140>(v);
   return v;
 }
+// Sum over each 32-lane half of the wave (lanes 0-31, 32-63), valid in its
+// upper 16 lanes (p = 16 .. 31 of the half): the 16-lane row sums, then
+// row_bcast:15 adds the first row's total into the second (row mask 0b1010).
+__device__ __forceinline__ float half32_sum_hi(float v) {
+  v = row16_sum(v);
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+}
 // Combination of each lane's value with the lane 16 (swap16) or 32 (swap32)
 // away: v_permlane16/32_swap exchange the odd 16-lane rows (the upper 32
 // lanes) of one copy with the even rows (lower 32 lanes) of the other.
@@ -272,6 +279,23 @@ __device__ __forceinline__ void swap32(float v, float& a, float& b) {
   a = __uint_as_float(r[0]);
   b = __uint_as_float(r[1]);
 }
+
+// Sum of the parts of a transposed row statistic: lane p holds part p >> 4
+// of row p & 15, so the parts sit 16 (and, with 64 lanes per row block, 32)
+// lanes apart.
+template <int NP>
+__device__ __forceinline__ float parts_sum(float v) {
+  float a, b;
+  swap16(v, a, b);
+  v = a + b;
+  if constexpr (NP == 64) {
+    swap32(v, a, b);
+    v = a + b;
+  }
+  return v;
+}
+// Sum over the 64 lanes of the wave, in every lane.
+__device__ __forceinline__ float wave_sum(float v) { return parts_sum<64>(row16_sum(v)); }
 
 __device__ __forceinline__ bool resolve_tile(const TileArgs& a, int tile, int& h,
                                              unsigned char*& base) {

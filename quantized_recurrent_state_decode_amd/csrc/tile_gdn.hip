@@ -212,11 +212,8 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
         sm.rowc[1][i] = bk * frcp(rp);     // gamma
         sm.rowc[2][i] = qq * rp;           // theta: readout weight on Xt
         sm.rowc[3][i] = rp;
-        // sum of kappa over the block's 32 rows (offset of the unpacked codes):
-        // each 16-lane row sums its lanes, then row_bcast:15 adds the first
-        // row's total into the second (row mask 0b1010), read at p = 16
-        float ksum = row16_sum(kap);
-        ksum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ksum), 0x142, 0xa, 0xf, false));
+        // sum of kappa over the block's 32 rows (offset of the unpacked codes)
+        const float ksum = half32_sum_hi(kap);
         if (p == 16) sm.ksum[rb] = ksum;
       }
     }

@@ -486,8 +486,7 @@ __attribute__((amdgpu_waves_per_eu(5, 8))) void kda_tile_kernel(TileArgs a) {
     float s = rowt[rb][mm][part * 16];
 #pragma unroll
     for (int pp = 1; pp < 16; ++pp) s += rowt[rb][mm][part * 16 + pp];
-#pragma unroll
-    for (int o = 16; o < NP; o <<= 1) s += __shfl_xor(s, o);
+    s = parts_sum<NP>(s);
     sh[hf] = s;
     wave_sync();
   }

@@ -203,22 +203,16 @@ __device__ __forceinline__ void fit_compensators(float (&x)[64], const WinPtrs& 
         float sv = sm.u.rowt[rb][mm][part * 16];
 #pragma unroll
         for (int pp = 1; pp < 16; ++pp) sv += sm.u.rowt[rb][mm][part * 16 + pp];
-#pragma unroll
-        for (int o = 16; o < NP; o <<= 1) sv += __shfl_xor(sv, o);
-        sh[hf] = sv;
+        sh[hf] = parts_sum<NP>(sv);
         wave_sync();
       }
       // |a|^2 partial and M^T a partial of the row block go out together;
       // buffers alternate by iteration so one barrier per iteration suffices
       float2(*part)[NP] = (it & 1) ? sm.colB : sm.colA;
-      float q2 = 0.f;
-      if (p < 32) {
-        const float ai = p < 16 ? sh[0] : sh[1];
-        sm.va[r0 + p] = ai;
-        q2 = ai * ai;
-      }
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) q2 += __shfl_xor(q2, o);
+      if (p < 32) sm.va[r0 + p] = p < 16 ? sh[0] : sh[1];
+      // |a|^2 over the block: each 16-lane row holds the block's 16 row pairs
+      // (sh[0], sh[1])
+      const float q2 = row16_sum(fmaf(sh[0], sh[0], sh[1] * sh[1]));
       if (p == 0) sm.red[it & 1][rb] = q2;
       wave_sync();
       float c0 = 0.f, c1 = 0.f;
@@ -241,7 +235,7 @@ __device__ __forceinline__ void fit_compensators(float (&x)[64], const WinPtrs& 
         inv = 0.f;
         break;
       }
-      inv = 1.0f / sqrtf(na2);
+      inv = __builtin_amdgcn_rsqf(na2);  // a scale error only rescales the pair
       // b = M^T a / |a|
       b0 = 0.f;
       b1 = 0.f;
@@ -254,16 +248,15 @@ __device__ __forceinline__ void fit_compensators(float (&x)[64], const WinPtrs& 
       b1 *= inv;
     }
     // sigma = |b| over the columns (row block 0 holds each column once)
-    float s2 = rb == 0 ? fmaf(b0, b0, b1 * b1) : 0.f;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) s2 += __shfl_xor(s2, o);
+    const float s2 = wave_sum(rb == 0 ? fmaf(b0, b0, b1 * b1) : 0.f);
     if (t == 0) sm.red[0][NRB] = s2;
     __syncthreads();
     const float sigma = sqrtf(sm.red[0][NRB]);
     const bool zero = !(inv > 0.f) || !(sigma > 0.f);
     const float sq = zero ? 0.f : sqrtf(sigma);
-    const float u0 = zero ? 0.f : __half2float(half_sat(b0 / sq));
-    const float u1 = zero ? 0.f : __half2float(half_sat(b1 / sq));
+    const float isq = zero ? 0.f : frcp(sq);
+    const float u0 = __half2float(half_sat(b0 * isq));
+    const float u1 = __half2float(half_sat(b1 * isq));
     if (p < 32) {
       const int i = r0 + p;
       const __half kh = half_sat(zero ? 0.f : sq * (sm.va[i] * inv));
@@ -311,8 +304,7 @@ __device__ __forceinline__ void encode_boundary(float (&x)[64], const WinPtrs& w
     float s = 0.f;
 #pragma unroll
     for (int pp = 0; pp < 16; ++pp) s += sm.u.rowt[rb][mm][part * 16 + pp];
-#pragma unroll
-    for (int o = 16; o < NP; o <<= 1) s += __shfl_xor(s, o);
+    s = parts_sum<NP>(s);
     if (part == 0) {
       const int a = r0 + 16 * hf + mm;
       const float ca = fmaxf(sqrtf(s / (float)DV), c_floor);
@@ -505,12 +497,10 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     sm.cx1[r] = c1;
     sm.cq[r] = c2;
     wp.K[ell * DK + r] = kn;  // the new record's key (record slot ell is free)
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-      c1 += __shfl_xor(c1, o);
-      c2 += __shfl_xor(c2, o);
-    }
-    if (p == 0) {
+    // sums over the block's 32 rows, valid at p = 16 .. 31
+    c1 = half32_sum_hi(c1);
+    c2 = half32_sum_hi(c2);
+    if (p == 16) {
       sm.csum[rb][0] = c1;
       sm.csum[rb][1] = c2;
     }
