@@ -235,7 +235,7 @@ __device__ __forceinline__ void codes_refit(float (&x)[64], const RowCls& R, con
 
 template <int DK, int DV, int OP>
 __global__ __launch_bounds__((DK / 32) * (DV / 2))
-__attribute__((amdgpu_waves_per_eu(5, 8))) void kda_tile_kernel(TileArgs a) {
+__attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   using G = Geo<DK, DV>;
   constexpr int NP = G::NP, NRB = G::NRB, NT = G::NT;
   constexpr bool WU = NP % 64 == 0;  // a wave's lanes share their rows
@@ -268,7 +268,13 @@ __attribute__((amdgpu_waves_per_eu(5, 8))) void kda_tile_kernel(TileArgs a) {
     rbits = a.P.row_bits[h * DK + s];
     roff = a.P.row_off[h * DK + s];
   }
-  float d = 0.f, kk = 0.f, qq = 0.f, beta = 0.f;
+  // the row's impact factor (and its inverse) go out with the token's inputs;
+  // they wait in LDS for the row-scale pass, so the key row need not stay live
+  float d = 0.f, kk = 0.f, qq = 0.f, beta = 0.f, wv = 0.f, wiv = 0.f;
+  if (ok && p < 32 && OP != OP_UNPACK) {
+    wv = a.P.w[h * DK + rk];
+    wiv = a.P.winv[h * DK + rk];
+  }
   if constexpr (OP == OP_DECODE) {
     if (ok && p < 32) {
       d = a.gate[tk + rk];
@@ -315,7 +321,13 @@ __attribute__((amdgpu_waves_per_eu(5, 8))) void kda_tile_kernel(TileArgs a) {
       x[2 * m] = v2.x;
       x[2 * m + 1] = v2.y;
     }
-    if (p < 32) sm.rowc[3][r0 + p] = 1.0f;
+    if (p < 32) {
+      const int s = r0 + p;
+      sm.rowc[3][s] = 1.0f;
+      sm.rowc[5][s] = wv;
+      sm.rowc[6][s] = wiv;
+      sm.rowc[7][s] = rbits == 16 ? 0.f : (float)((1 << (rbits - 1)) - 1);
+    }
     __syncthreads();
   } else {
     // The head's code rows are staged through registers, CH 16-byte chunks
@@ -361,6 +373,9 @@ __attribute__((amdgpu_waves_per_eu(5, 8))) void kda_tile_kernel(TileArgs a) {
       const bool piv = rbits == 16;
       const float qb = piv ? 1.f : (float)((1 << (rbits - 1)) - 1);
       const float sc = piv ? 1.f : rs * frcp(qb);
+      sm.rowc[5][s] = wv;
+      sm.rowc[6][s] = wiv;
+      sm.rowc[7][s] = piv ? 0.f : qb;
       if constexpr (OP == OP_UNPACK) {
         sm.rowc[3][s] = sc;
         sm.rowc[4][s] = 1.0f;
@@ -491,27 +506,26 @@ __attribute__((amdgpu_waves_per_eu(5, 8))) void kda_tile_kernel(TileArgs a) {
     wave_sync();
   }
   if (p < 32) {
-    const int si = r0 + p;
+    // (the row index is laundered so that the address of r_ptr[si] is formed
+    // here rather than kept live from the row-scale load)
+    const int si = opaque(r0 + p);
     const float s = p < 16 ? sh[0] : sh[1];
-    const float rp = sm.rowc[3][si];
-    if (rbits == 16) {
+    const float rp = sm.rowc[3][si], qb = sm.rowc[7][si];
+    if (qb == 0.f) {  // FP16 row
       r_ptr[si] = __float2half_rn(0.0f);
       sm.rowc[4][si] = rp;  // FP16 rows: X = Xt (row factor 1)
       sm.rowc[5][si] = 0.f;
       sm.rowc[6][si] = 0.f;
-      sm.rowc[7][si] = 0.f;
     } else {
-      const float wi = a.P.w[h * DK + rk];
-      const float qb = (float)((1 << (rbits - 1)) - 1), iq = frcp(qb);
+      const float wi = sm.rowc[5][si], iq = frcp(qb);
       // the hardware square root (1 ulp) only feeds an FP16 rounding
       const float ri =
-          fp16_scale(__builtin_amdgcn_sqrtf(rp * s * (1.0f / (float)DV) * a.P.winv[h * DK + rk]));
+          fp16_scale(__builtin_amdgcn_sqrtf(rp * s * (1.0f / (float)DV) * sm.rowc[6][si]));
       r_ptr[si] = __float2half_rn(ri);
       sm.rowc[4][si] = rp * frcp(ri);
       const float lam = wi * wi * ri * ri * iq;
       sm.rowc[5][si] = lam;
       sm.rowc[6][si] = lam * iq;
-      sm.rowc[7][si] = qb;
     }
   }
   wave_sync();
@@ -526,9 +540,20 @@ __attribute__((amdgpu_waves_per_eu(5, 8))) void kda_tile_kernel(TileArgs a) {
     for (int u = 0; u < 4; ++u) {
       x[2 * (m + u)] *= fv[u];
       x[2 * (m + u) + 1] *= fv[u];
-      if (!(R.msk[4] & (1u << (m + u)))) {
-        mx0 = fmaxf(mx0, fabsf(x[2 * (m + u)]));
-        mx1 = fmaxf(mx1, fabsf(x[2 * (m + u) + 1]));
+    }
+  }
+  if (R.msk[4] == 0u) {  // no FP16 rows in the block (the common case)
+#pragma unroll
+    for (int m = 0; m < 32; ++m) {
+      mx0 = fmaxf(mx0, fabsf(x[2 * m]));
+      mx1 = fmaxf(mx1, fabsf(x[2 * m + 1]));
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 32; ++m) {
+      if (!(R.msk[4] & (1u << m))) {
+        mx0 = fmaxf(mx0, fabsf(x[2 * m]));
+        mx1 = fmaxf(mx1, fabsf(x[2 * m + 1]));
       }
     }
   }
