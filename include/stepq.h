@@ -84,6 +84,10 @@
 extern "C" {
 #endif
 
+/* Every entry point returns a status and never throws.  A call with an empty
+ * batch (B = 0, T = 0 or n_tiles = 0) is a no-op that launches nothing; its
+ * batch-sized arrays may then be null, while the plan, device tables and pool
+ * must still be valid. */
 typedef int32_t sq_status;
 enum {
   SQ_OK = 0,

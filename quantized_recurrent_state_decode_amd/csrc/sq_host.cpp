@@ -528,9 +528,10 @@ extern "C" sq_status sq_pool_init(const sq_plan* P, const void* dev_plan, void* 
 extern "C" sq_status sq_pool_pack(const sq_plan* P, const void* dev_plan, void* pool,
                                   int64_t n_slots, const int32_t* slots, int32_t B,
                                   const float* S, hipStream_t st) {
-  if (!P || !dev_plan || !pool || !slots || !S || n_slots <= 0 || B < 0)
+  if (!P || !dev_plan || !pool || n_slots <= 0 || B < 0)
     return fail(SQ_EINVAL, "bad arguments to sq_pool_pack");
-  if (B == 0) return ok();
+  if (B == 0) return ok();  // the batch arrays may be null
+  if (!slots || !S) return fail(SQ_EINVAL, "bad arguments to sq_pool_pack");
   sq_status s = validate_slots(slots, B, n_slots, st);
   if (s) return s;
   TileArgs a = base_args(P, dev_plan, OP_PACK);
@@ -548,9 +549,10 @@ extern "C" sq_status sq_pool_pack(const sq_plan* P, const void* dev_plan, void* 
 extern "C" sq_status sq_pool_unpack(const sq_plan* P, const void* dev_plan, const void* pool,
                                     int64_t n_slots, const int32_t* slots, int32_t B,
                                     float* S_out, hipStream_t st) {
-  if (!P || !dev_plan || !pool || !slots || !S_out || n_slots <= 0 || B < 0)
+  if (!P || !dev_plan || !pool || n_slots <= 0 || B < 0)
     return fail(SQ_EINVAL, "bad arguments to sq_pool_unpack");
-  if (B == 0) return ok();
+  if (B == 0) return ok();  // the batch arrays may be null
+  if (!slots || !S_out) return fail(SQ_EINVAL, "bad arguments to sq_pool_unpack");
   sq_status s = validate_slots(slots, B, n_slots, st);
   if (s) return s;
   TileArgs a = base_args(P, dev_plan, OP_UNPACK);
@@ -570,10 +572,11 @@ extern "C" sq_status sq_decode_step(const sq_plan* P, const void* dev_plan, void
                                     const float* q, const float* k, const float* v,
                                     const float* beta, const float* gate, float* y,
                                     hipStream_t st) {
-  if (!P || !dev_plan || !pool || !slots || !q || !k || !v || !beta || !gate || !y ||
-      n_slots <= 0 || B < 0)
+  if (!P || !dev_plan || !pool || n_slots <= 0 || B < 0)
     return fail(SQ_EINVAL, "bad arguments to sq_decode_step");
-  if (B == 0) return ok();
+  if (B == 0) return ok();  // the batch arrays may be null
+  if (!slots || !q || !k || !v || !beta || !gate || !y)
+    return fail(SQ_EINVAL, "bad arguments to sq_decode_step");
   sq_status s = validate_slots(slots, B, n_slots, st);
   if (s) return s;
   TileArgs a = base_args(P, dev_plan, OP_DECODE);
@@ -596,10 +599,11 @@ extern "C" sq_status sq_decode_step(const sq_plan* P, const void* dev_plan, void
 extern "C" sq_status sq_window_flush(const sq_plan* P, const void* dev_plan, void* pool,
                                      int64_t n_slots, const int32_t* slots, int32_t B,
                                      hipStream_t st) {
-  if (!P || !dev_plan || !pool || !slots || n_slots <= 0 || B < 0)
+  if (!P || !dev_plan || !pool || n_slots <= 0 || B < 0)
     return fail(SQ_EINVAL, "bad arguments to sq_window_flush");
   if (P->mode != SQ_MODE_WINDOW) return fail(SQ_EPLAN_MISMATCH, "sq_window_flush needs a window plan");
-  if (B == 0) return ok();
+  if (B == 0) return ok();  // the slot array may be null
+  if (!slots) return fail(SQ_EINVAL, "bad arguments to sq_window_flush");
   sq_status s = validate_slots(slots, B, n_slots, st);
   if (s) return s;
   TileArgs a = base_args(P, dev_plan, OP_FLUSH);
@@ -616,9 +620,9 @@ extern "C" sq_status sq_window_flush(const sq_plan* P, const void* dev_plan, voi
 extern "C" sq_status sq_quantize_tiles(const sq_plan* P, const void* dev_plan, const float* X,
                                        int32_t n_tiles, const int32_t* head_ids, void* out,
                                        hipStream_t st) {
-  if (!P || !dev_plan || !X || !head_ids || !out || n_tiles < 0)
-    return fail(SQ_EINVAL, "bad arguments to sq_quantize_tiles");
-  if (n_tiles == 0) return ok();
+  if (!P || !dev_plan || n_tiles < 0) return fail(SQ_EINVAL, "bad arguments to sq_quantize_tiles");
+  if (n_tiles == 0) return ok();  // the tile arrays may be null
+  if (!X || !head_ids || !out) return fail(SQ_EINVAL, "bad arguments to sq_quantize_tiles");
   TileArgs a = base_args(P, dev_plan, OP_PACK);
   a.X = X;
   a.head_ids = head_ids;
@@ -686,9 +690,10 @@ extern "C" sq_status sq_prefill_chunk(int32_t kind, int32_t H, int32_t dk, int32
   if (kind != SQ_KIND_GDN && kind != SQ_KIND_KDA) return fail(SQ_EINVAL, "bad kind %d", kind);
   sq_status s = check_dims(H, dk, dv);
   if (s) return s;
-  if (B < 0 || T < 0 || !S || !q || !k || !v || !beta || !gate || !y)
+  if (B < 0 || T < 0) return fail(SQ_EINVAL, "bad arguments to sq_prefill_chunk");
+  if (B == 0 || T == 0) return ok();  // the arrays may be null
+  if (!S || !q || !k || !v || !beta || !gate || !y)
     return fail(SQ_EINVAL, "bad arguments to sq_prefill_chunk");
-  if (B == 0 || T == 0) return ok();
   hipError_t e = launch_prefill_chunk(kind, H, dk, dv, B, T, S, q, k, v, beta, gate, y, st);
   if (e != hipSuccess) return hip_fail(e, "launching prefill chunk");
   return ok();
@@ -702,9 +707,10 @@ extern "C" sq_status sq_dense_step(int32_t kind, int32_t H, int32_t dk, int32_t 
   if (kind != SQ_KIND_GDN && kind != SQ_KIND_KDA) return fail(SQ_EINVAL, "bad kind %d", kind);
   sq_status s = check_dims(H, dk, dv);
   if (s) return s;
-  if (!S || !slots || !q || !k || !v || !beta || !gate || !y || n_slots <= 0 || B < 0)
+  if (!S || n_slots <= 0 || B < 0) return fail(SQ_EINVAL, "bad arguments to sq_dense_step");
+  if (B == 0) return ok();  // the batch arrays may be null
+  if (!slots || !q || !k || !v || !beta || !gate || !y)
     return fail(SQ_EINVAL, "bad arguments to sq_dense_step");
-  if (B == 0) return ok();
   s = validate_slots(slots, B, n_slots, st);
   if (s) return s;
   hipError_t e = launch_dense_step(kind, H, dk, dv, S, n_slots, slots, B, q, k, v, beta, gate, y, st);

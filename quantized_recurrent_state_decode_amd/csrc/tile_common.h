@@ -223,6 +223,14 @@ __device__ __forceinline__ float wuni(float v) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
 
+// Orders LDS accesses among the lanes of one wave: rows owned by a single wave
+// only need the wave's own writes visible, not a workgroup barrier.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // LDS accesses by byte address.  An address kept as a plain integer (passed
 // through an empty asm) stays in one register, and the accesses built on it
 // carry their constant parts as instruction offsets.

@@ -37,13 +37,6 @@ struct SmemGdn {
   float rowt[DK / 32][16][DV / 2 + 1];        // row partials of 16 rows, transposed
 };
 
-// Rows are owned by one wave (or half-wave), so row-wise LDS traffic only
-// needs ordering inside the wave.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 
 // Rows m .. m + R - 1 of both columns go into one output dword: R = 4 at 4 bits

@@ -68,11 +68,6 @@ __host__ __device__ constexpr int dyn_bytes(int max_code_bytes) {
   return ((max_code_bytes > transpose ? max_code_bytes : transpose) + 15) / 16 * 16 + 16;
 }
 
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Width classes 2, 4, 6, 8 bits and FP16 (16).
 template <int B>

@@ -94,11 +94,6 @@ __device__ __forceinline__ __half half_sat(float v) {
   return __float2half_rn(fminf(fmaxf(v, -kFp16Max), kFp16Max));
 }
 
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // The records and compensator pairs held by a head, staged through
 // registers: `issue` starts every load (a fixed number per thread,

@@ -233,8 +233,19 @@ def test_error_codes():
     assert lib.sq_pool_pack(p, None, None, 1, None, 1, None, None) == sq.SQ_EINVAL
     assert lib.sq_window_flush(p, 1, 1, 1, 1, 1, None) == sq.SQ_EPLAN_MISMATCH
     assert lib.sq_plan_query(None, None) == sq.SQ_EINVAL
-    # batch 0 is a no-op
+    # batch 0 is a no-op, with or without batch arrays; batch 1 needs them
     assert lib.sq_decode_step(p, 1, 1, 1, 1, 0, 1, 1, 1, 1, 1, 1, None) == sq.SQ_OK
+    assert lib.sq_decode_step(p, 1, 1, 1, None, 0, None, None, None, None, None, None,
+                              None) == sq.SQ_OK
+    assert lib.sq_decode_step(p, 1, 1, 1, None, 1, None, None, None, None, None, None,
+                              None) == sq.SQ_EINVAL
+    assert lib.sq_pool_pack(p, 1, 1, 1, None, 0, None, None) == sq.SQ_OK
+    assert lib.sq_pool_unpack(p, 1, 1, 1, None, 0, None, None) == sq.SQ_OK
+    assert lib.sq_quantize_tiles(p, 1, None, 0, None, None, None) == sq.SQ_OK
+    assert lib.sq_quantize_tiles(p, 1, None, 2, None, None, None) == sq.SQ_EINVAL
+    # the plan, device tables and pool are still required
+    assert lib.sq_decode_step(p, None, 1, 1, None, 0, None, None, None, None, None, None,
+                              None) == sq.SQ_EINVAL
 
 
 def test_binding_refuses_without_library(monkeypatch, tmp_path):
