@@ -50,7 +50,7 @@ def _plan(sq, w):
             return sq.sq_plan_create_window_lowrank(w.heads, w.d_k, w.d_v, w.window, w.comp_rank,
                                                     w.power_iters)
         return sq.sq_plan_create_window(w.heads, w.d_k, w.d_v, w.window)
-    with open(os.path.join(ROOT, "tests", "golden", f"calib_{w.name}.json")) as f:
+    with open(os.path.join(ROOT, "tests", "golden", f"calib_{w.calib or w.name}.json")) as f:
         st = json.load(f)
     stats = {"kind": 0 if st["kind"] == "gdn" else 1, "heads": st["heads"], "d_k": st["d_k"],
              "d_v": st["d_v"], "cand_bits": st["cand_bits"], "ell": np.array(st["ell"]),
@@ -412,11 +412,14 @@ def measure_prefill(sq, w, args) -> dict:
 def same_hardware(sq, args, value: float) -> dict:
     """The pool workload's shape (same batch, slots, heads, d, inputs and
     timing protocol) with the fp32 state kept dense, and with uniform rowwise
-    INT4: the denominators of the packed path's speed-up on this GPU."""
+    INT4: the denominators of the packed path's speed-up on this GPU.  Then
+    the 6-bit plan of the mid workload at batch 512 against the fp32 state of
+    that shape (the setting of the pages' 6-bit, batch-512 comparison)."""
     import torch
     from synth import inputs as SI
     res = {}
-    for key, name in (("fp32_dense", "gdn_pool_fp32"), ("uniform_int4", "gdn_pool_int4")):
+    for key, name in (("fp32_dense", "gdn_pool_fp32"), ("uniform_int4", "gdn_pool_int4"),
+                      ("step6_b512", "gdn_b512_step6"), ("fp32_dense_b512", "gdn_b512_fp32")):
         w = SI.workload(name)
         m = measure(sq, w, args)
         res[key] = {"workload": name, "steps_per_s": 1e3 / m["ms_per_step"],
@@ -428,6 +431,8 @@ def same_hardware(sq, args, value: float) -> dict:
         torch.cuda.empty_cache()
     res["speedup_vs_fp32_dense"] = value / res["fp32_dense"]["steps_per_s"]
     res["speedup_vs_uniform_int4"] = value / res["uniform_int4"]["steps_per_s"]
+    res["speedup_step6_b512_vs_fp32_dense"] = (res["step6_b512"]["steps_per_s"]
+                                              / res["fp32_dense_b512"]["steps_per_s"])
     return res
 
 

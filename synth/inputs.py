@@ -66,6 +66,7 @@ class Workload:
     gamma: float = 0.25
     key_gain_sigma: float = 0.0         # log-normal gain spread on key channels
     value_gain_sigma: float = 0.0       # log-normal gain spread on value channels
+    calib: Optional[str] = None         # workload whose calibration statistics give the plan
 
     @property
     def tiles(self) -> int:
@@ -102,6 +103,15 @@ WORKLOADS: Dict[str, Workload] = {
     "gdn_pool_int4": Workload(
         name="gdn_pool_int4", kind="gdn", mode="uniform", batch=512, n_slots=1024, heads=48,
         d_k=128, d_v=128, steps=256, seed=3, bits=4, half_life=64.0),
+    # the mid workload's heads and 6-bit plan at batch 512 (the pages' 6-bit, batch-512 setting),
+    # and the same shape with the fp32 state kept dense: a same-hardware 6-bit speed-up
+    "gdn_b512_step6": Workload(
+        name="gdn_b512_step6", kind="gdn", mode="step", batch=512, n_slots=512, heads=16,
+        d_k=128, d_v=128, steps=256, seed=1, nominal_bits=6.0, cand_bits=(4, 6, 8),
+        pivot_frac=0.02, half_life_range=(1.0, 4096.0), calib="gdn_mid_step6"),
+    "gdn_b512_fp32": Workload(
+        name="gdn_b512_fp32", kind="gdn", mode="dense", batch=512, n_slots=512, heads=16,
+        d_k=128, d_v=128, steps=256, seed=1, half_life_range=(1.0, 4096.0)),
     # per-window variant: INT8 boundary + FP32 records, p = 16
     "gdn_window16": Workload(
         name="gdn_window16", kind="gdn", mode="window", batch=256, n_slots=256, heads=32,
