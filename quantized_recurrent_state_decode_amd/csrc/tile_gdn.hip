@@ -342,10 +342,11 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
         x[2 * (m + u)] *= pv[u];
         x[2 * (m + u) + 1] *= pv[u];
       }
-      mx0 = fmaxf(mx0, fmaxf(fmaxf(fabsf(x[2 * m]), fabsf(x[2 * m + 2])),
-                             fmaxf(fabsf(x[2 * m + 4]), fabsf(x[2 * m + 6]))));
-      mx1 = fmaxf(mx1, fmaxf(fmaxf(fabsf(x[2 * m + 1]), fabsf(x[2 * m + 3])),
-                             fmaxf(fabsf(x[2 * m + 5]), fabsf(x[2 * m + 7]))));
+      // a chain of three-input maxima: two new values per instruction
+      mx0 = fmaxf(fmaxf(mx0, fabsf(x[2 * m])), fabsf(x[2 * m + 2]));
+      mx0 = fmaxf(fmaxf(mx0, fabsf(x[2 * m + 4])), fabsf(x[2 * m + 6]));
+      mx1 = fmaxf(fmaxf(mx1, fabsf(x[2 * m + 1])), fabsf(x[2 * m + 3]));
+      mx1 = fmaxf(fmaxf(mx1, fabsf(x[2 * m + 5])), fabsf(x[2 * m + 7]));
     }
     sm.colM[rb][p] = make_float2(mx0, mx1);
     __syncthreads();
@@ -580,10 +581,10 @@ template <int DK, int DV, int BITS, bool UNI>
 __global__ __launch_bounds__((DK / 32) * (DV / 2))
 __attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_class_kernel(TileArgs a) {
   __shared__ SmemGdn<DK, DV> sm;
-  const int t = blockIdx.x;
-  const int n = a.cls_n[0];
-  const int bi = t / n;
-  const int h = wuni(a.P.cls_heads[a.cls_first[0] + (t - bi * n)]);
+  // grid (heads of the class, batch rows): the same order as tile
+  // bi * n + j, without a division
+  const int bi = blockIdx.y;
+  const int h = wuni(a.P.cls_heads[a.cls_first[0] + (int)blockIdx.x]);
   const int tile = bi * a.P.H + h;
   const int slot = wuni(a.slots[bi]);
   if (slot < 0 || (long long)slot >= a.n_slots) {
@@ -612,13 +613,14 @@ template <int DK, int DV>
 hipError_t launch_decode(const TileArgs& a, bool solo, hipStream_t s) {
   if (a.n_tiles <= 0) return hipSuccess;
   const dim3 grid(a.n_tiles), block((DK / 32) * (DV / 2));
-  if (solo) {
+  if (solo && a.B <= 65535) {
+    const dim3 grid2(a.cls_n[0], a.B);
     switch (a.cls_bits[0]) {
-      case 2: return launch_solo<DK, DV, 2>(a, grid, block, s);
-      case 4: return launch_solo<DK, DV, 4>(a, grid, block, s);
-      case 6: return launch_solo<DK, DV, 6>(a, grid, block, s);
-      case 8: return launch_solo<DK, DV, 8>(a, grid, block, s);
-      case 16: return launch_solo<DK, DV, 16>(a, grid, block, s);
+      case 2: return launch_solo<DK, DV, 2>(a, grid2, block, s);
+      case 4: return launch_solo<DK, DV, 4>(a, grid2, block, s);
+      case 6: return launch_solo<DK, DV, 6>(a, grid2, block, s);
+      case 8: return launch_solo<DK, DV, 8>(a, grid2, block, s);
+      case 16: return launch_solo<DK, DV, 16>(a, grid2, block, s);
       default: return hipErrorInvalidValue;
     }
   }
