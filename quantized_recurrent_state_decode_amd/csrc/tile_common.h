@@ -126,11 +126,95 @@ __device__ __forceinline__ void unpack_offset(const uint32_t (&w)[2 * BITS], flo
   }
 }
 
+// Codes as binary16 subnormals.  An offset-binary code u placed in the low
+// bits of a half (exponent field 0) is the subnormal u * 2^-24, exactly; a
+// mixed-precision FMA (v_fma_mix_f32, binary16 denormals kept) reads it
+// straight from its half, so the code costs no conversion instruction and the
+// factor 2^24 goes into the other operand (the exact product is unchanged).
+// unpack_half<BITS> fills 32 registers with two codes each: register
+// hreg(n), half hhi(n) holds value n = 2m + c (any width up to 8 bits:
+// 2^(BITS-1) + z < 1024 fits the 10-bit significand).
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+template <int BITS>
+__device__ __forceinline__ constexpr int hreg(int n) {
+  if constexpr (BITS == 2) return 8 * (n >> 4) + (n & 7);       // n, n + 8
+  else if constexpr (BITS == 8) return 2 * (n >> 2) + (n & 1);  // n, n + 2
+  else return 4 * (n >> 3) + (n & 3);                           // n, n + 4 (4 and 6 bits)
+}
+template <int BITS>
+__device__ __forceinline__ constexpr int hhi(int n) {
+  return BITS == 2 ? (n >> 3) & 1 : BITS == 8 ? (n >> 1) & 1 : (n >> 2) & 1;
+}
+// value n as a float (u * 2^-24): folds into the FMA that consumes it
+template <int BITS>
+__device__ __forceinline__ float hcode(const uint32_t (&h)[32], int n) {
+  const half2v v = __builtin_bit_cast(half2v, h[hreg<BITS>(n)]);
+  return (float)(hhi<BITS>(n) ? v.y : v.x);
+}
+template <int BITS>
+__device__ __forceinline__ void unpack_half(const uint32_t (&w)[2 * BITS], uint32_t (&h)[32]) {
+  // each register takes the fields 16 bits apart: shift the dword by the
+  // field's offset, flip the sign bits, keep BITS bits of each half
+  constexpr uint32_t keep = ((1u << BITS) - 1u) * 0x00010001u;
+  constexpr uint32_t sgn = (1u << (BITS - 1)) * 0x00010001u;
+  if constexpr (BITS == 6) {
+    // 16 fields per 3 dwords, field t at bit 6t.  Fields t and t + 4 are three
+    // bytes apart at the same offset within their byte, so one byte
+    // permutation brings both 16 bits apart and one shift aligns them.
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = (j & 3) + 8 * (j >> 2);    // fields t, t + 4 -> register 8g + j
+        const int b0 = (6 * t) >> 3, sh = (6 * t) & 7, dlo = b0 >> 2;
+        const int bytes[4] = {b0, b0 + 1, b0 + 3, b0 + 4};
+        uint32_t sel = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)            // byte 12 lies past the group: zero
+          sel |= (uint32_t)(bytes[k] < 12 ? bytes[k] - 4 * dlo : 0x0c) << (8 * k);
+        const uint32_t lo = w[3 * g + dlo], hi = dlo < 2 ? w[3 * g + dlo + 1] : lo;
+        h[8 * g + j] = ((__builtin_amdgcn_perm(hi, lo, sel) >> sh) ^ sgn) & keep;
+      }
+    }
+  } else {
+    constexpr int per = 16 / BITS;               // registers per dword
+#pragma unroll
+    for (int d = 0; d < 2 * BITS; ++d) {
+#pragma unroll
+      for (int j = 0; j < per; ++j) h[per * d + j] = ((w[d] >> (BITS * j)) ^ sgn) & keep;
+    }
+  }
+}
+
 // dword of the low bytes of four floats' bit patterns
 __device__ __forceinline__ uint32_t low_bytes4(float a, float b, float c, float d) {
   const uint32_t ab = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0c0c0400u);
   const uint32_t cd = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x0c0c0400u);
   return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+// 16 six-bit fields (the low bits of mg[0..15]) into 3 dwords, field t at
+// bit 6t.  v_alignbit shifts a dword right and brings the next field's low
+// bits in at the top, one instruction per field and no masks: a dword is
+// built from the fields that end in it, the last shift sized to leave its
+// first field at bit 0.
+__device__ __forceinline__ void pack6(const float* mg, uint32_t* w) {
+  auto in = [&](uint32_t acc, int t, int sh) {
+    return __builtin_amdgcn_alignbit(__float_as_uint(mg[t]), acc, sh);
+  };
+  uint32_t a = __float_as_uint(mg[0]) << 26;   // fields 0..5 (field 5: its low 2 bits)
+#pragma unroll
+  for (int t = 1; t < 5; ++t) a = in(a, t, 6);
+  w[0] = in(a, 5, 2);
+  a = __float_as_uint(mg[5]) << 26;            // fields 5 (high 4 bits) .. 10 (low 4)
+#pragma unroll
+  for (int t = 6; t < 10; ++t) a = in(a, t, 6);
+  w[1] = in(a, 10, 4);
+  a = __float_as_uint(mg[10]) << 26;           // fields 10 (high 2 bits) .. 15
+#pragma unroll
+  for (int t = 11; t < 16; ++t) a = in(a, t, 6);
+  w[2] = a;
 }
 
 template <int BITS>
@@ -160,14 +244,7 @@ __device__ __forceinline__ void pack_magic(const float (&mg)[64], uint32_t (&w)[
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 2 * BITS; ++i) w[i] = 0u;
-#pragma unroll
-    for (int n = 0; n < 64; ++n) {
-      const uint32_t val = __float_as_uint(mg[n]) & ((1u << BITS) - 1u);
-      const int pos = n * BITS, wi = pos >> 5, off = pos & 31;
-      w[wi] |= val << off;
-      if (off + BITS > 32) w[wi + 1] |= val >> (32 - off);
-    }
+    for (int g = 0; g < 4; ++g) pack6(&mg[16 * g], &w[3 * g]);
   }
 }
 

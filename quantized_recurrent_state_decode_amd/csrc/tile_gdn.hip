@@ -59,16 +59,6 @@ __device__ __forceinline__ uint32_t pack_rows(const float* mg) {
   }
 }
 
-// 16 six-bit fields (rows m .. m+7, both columns) fill exactly 3 dwords.
-__device__ __forceinline__ void pack_rows6(const float* mg, uint32_t* w) {
-  uint32_t v[16];
-#pragma unroll
-  for (int n = 0; n < 16; ++n) v[n] = __float_as_uint(mg[n]) & 63u;
-  w[0] = v[0] | (v[1] << 6) | (v[2] << 12) | (v[3] << 18) | (v[4] << 24) | (v[5] << 30);
-  w[1] = (v[5] >> 2) | (v[6] << 4) | (v[7] << 10) | (v[8] << 16) | (v[9] << 22) | (v[10] << 28);
-  w[2] = (v[10] >> 4) | (v[11] << 2) | (v[12] << 8) | (v[13] << 14) | (v[14] << 20) | (v[15] << 26);
-}
-
 // Codes by magic rounding and the fixed-code weighted least-squares column
 // sums (N_j, D_j), packed into w as they are produced.
 template <int BITS, bool CLAMP>
@@ -110,7 +100,7 @@ __device__ __forceinline__ void codes_refit(float (&x)[64], int lam, float tau0,
       }
     }
     if constexpr (BITS == 6) {
-      pack_rows6(&x[2 * g], &w[3 * (g / 8)]);
+      pack6(&x[2 * g], &w[3 * (g / 8)]);
 #pragma unroll
       for (int k = 0; k < 3; ++k) asm volatile("" : "+v"(w[3 * (g / 8) + k]));
     } else {
@@ -180,6 +170,14 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
     if (p < 32) sm.rowc[3][r0 + p] = 1.0f;
     wave_sync();
   } else {
+    // uniform decode reads the codes as binary16 subnormals (u 2^-24): the
+    // retrieval weights and column scales that multiply them carry 2^24.  On
+    // STEP heads the mixed-precision FMAs made the wave slower despite fewer
+    // instructions (more cycles per wave, more waits on LDS issue), and at
+    // d_v = 64 (a wave spans two row blocks) the longer live range spills;
+    // those tiles convert the codes to floats.
+    constexpr bool HC = OP == OP_DECODE && DV == 128 && UNI;
+    constexpr float HS = HC ? 0x1p24f : 1.0f;
     uint32_t wd[2 * BITS];
     load_chunk<BITS, NP>(base, rb, p, wd);
     float c0 = 1.0f, c1 = 1.0f;
@@ -201,7 +199,7 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
         // (rp - rho) c_j z_ij is below 2^-60 of the write term
         const float rp = fmaxf(rho, fmaxf(fabsf(bk) * 0x1p-60f, 0x1p-100f));
         const float kap = kk * rho;
-        sm.rowc[0][i] = kap;               // kappa: key retrieval weight
+        sm.rowc[0][i] = kap * HS;          // kappa: key retrieval weight
         sm.rowc[1][i] = bk * frcp(rp);     // gamma
         sm.rowc[2][i] = qq * rp;           // theta: readout weight on Xt
         sm.rowc[3][i] = rp;
@@ -210,7 +208,14 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
         if (p == 16) sm.ksum[rb] = ksum;
       }
     }
-    unpack_offset<BITS>(wd, x);
+    uint32_t hc[32];
+    if constexpr (HC) unpack_half<BITS>(wd, hc);
+    else unpack_offset<BITS>(wd, x);
+    // unpacked code n (an offset-binary integer, times 2^-24 when HC)
+    auto code = [&](int n) -> float {
+      if constexpr (HC) return hcode<BITS>(hc, n);
+      else return x[n];
+    };
     wave_sync();
     if (op == OP_UNPACK) {
       float* S = a.S_out + (long long)tile * DK * DV;
@@ -231,8 +236,8 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
       const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        a0 = fmaf(kv[u], x[2 * (m + u)], a0);
-        a1 = fmaf(kv[u], x[2 * (m + u) + 1], a1);
+        a0 = fmaf(kv[u], code(2 * (m + u)), a0);
+        a1 = fmaf(kv[u], code(2 * (m + u) + 1), a1);
       }
     }
     sm.colA[rb][p] = make_float2(fmaf(-OFF, ks, a0), fmaf(-OFF, ks, a1));
@@ -247,15 +252,15 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
     const float2 vv = *reinterpret_cast<const float2*>(a.v + tv + j0);
     const float e0 = vv.x - c0 * d0, e1 = vv.y - c1 * d1;
     // pass 2: Xt = c_j (u - off) + gamma_i e_j, readout partials
-    const float o0 = -OFF * c0, o1 = -OFF * c1;
+    const float o0 = -OFF * c0, o1 = -OFF * c1, cs0 = c0 * HS, cs1 = c1 * HS;
 #pragma unroll
     for (int m = 0; m < 32; m += 4) {
       const float4 g4 = lds_ld4(rcb + 4 * (1 * DK + m)), t4 = lds_ld4(rcb + 4 * (2 * DK + m));
       const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, tv4[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float v0 = fmaf(c0, x[2 * (m + u)], fmaf(gv[u], e0, o0));
-        const float v1 = fmaf(c1, x[2 * (m + u) + 1], fmaf(gv[u], e1, o1));
+        const float v0 = fmaf(cs0, code(2 * (m + u)), fmaf(gv[u], e0, o0));
+        const float v1 = fmaf(cs1, code(2 * (m + u) + 1), fmaf(gv[u], e1, o1));
         x[2 * (m + u)] = v0;
         x[2 * (m + u) + 1] = v1;
         y0 = fmaf(tv4[u], v0, y0);
