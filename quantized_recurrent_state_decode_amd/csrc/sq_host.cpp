@@ -247,14 +247,20 @@ hipError_t dispatch(const sq_plan* P, const TileArgs& a, hipStream_t st) {
   std::stable_sort(order, order + 5, [&](int x, int y) { return P->cls_count[x] > P->cls_count[y]; });
   int n = 0;
   while (n < 5 && P->cls_count[order[n]]) ++n;
-  int first = 0;
-  if (n == 1 || (long long)a.B * P->cls_count[order[0]] >= kSoloTiles) {
-    TileArgs b = class_args(P, a, order, 0, 1);
-    hipError_t e = launch_decode_gdn(b, true, st);
-    if (e != hipSuccess || n == 1) return e;
-    first = 1;
+  if (n == 1) return launch_decode_gdn(class_args(P, a, order, 0, 1), true, st);
+  if ((long long)a.B * P->cls_count[order[0]] < kSoloTiles)
+    return launch_decode_gdn(class_args(P, a, order, 0, n), false, st);
+  if (P->mode == SQ_MODE_STEP) {
+    // one split launch: the other classes' tiles in rows ahead of the largest
+    // class's batch rows
+    TileArgs b = class_args(P, a, order, 0, n);
+    const int n0 = b.cls_n[0];
+    b.pre_rows = (b.n_tiles - b.cls_end[0] + n0 - 1) / n0;
+    if ((long long)b.B + b.pre_rows <= 65535) return launch_split_gdn(b, st);
   }
-  return launch_decode_gdn(class_args(P, a, order, first, n), false, st);
+  hipError_t e = launch_decode_gdn(class_args(P, a, order, 0, 1), true, st);
+  if (e != hipSuccess) return e;
+  return launch_decode_gdn(class_args(P, a, order, 1, n), false, st);
 }
 
 TileArgs base_args(const sq_plan* P, const void* dev_plan, int op) {

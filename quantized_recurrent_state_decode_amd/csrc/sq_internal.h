@@ -72,6 +72,9 @@ struct TileArgs {
   // cls_bits[i]; its tiles are blockIdx in [cls_end[i-1], cls_end[i]).
   int n_cls;
   int cls_first[5], cls_n[5], cls_bits[5], cls_end[5];
+  // split launch (STEP GDN): grid rows of cls_n[0] workgroups ahead of class
+  // 0's batch rows, which run the tiles of classes 1 .. n_cls-1
+  int pre_rows;
 };
 
 // Kernel launchers (defined in the .hip files).
@@ -79,6 +82,7 @@ hipError_t launch_tile_gdn(const TileArgs& a, hipStream_t s);     // uniform + S
 // decode by width class: solo = class 0 alone in its width-specialised kernel,
 // else every class of a in one merged launch
 hipError_t launch_decode_gdn(const TileArgs& a, bool solo, hipStream_t s);
+hipError_t launch_split_gdn(const TileArgs& a, hipStream_t s);
 hipError_t launch_tile_kda(const TileArgs& a, hipStream_t s);     // STEP KDA
 hipError_t launch_tile_window(const TileArgs& a, hipStream_t s);  // per-window variant
 hipError_t launch_calib_gate(int kind, int H, int dk, int n, const float* q, const float* k,

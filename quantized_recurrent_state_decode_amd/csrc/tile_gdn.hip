@@ -548,11 +548,9 @@ __device__ __forceinline__ int pick5(const int (&v)[5], int i) {
 // class head t % cls_n).  The width is uniform over a workgroup, so each
 // workgroup runs exactly one of the width-specialised bodies; the kernel's
 // register budget is the largest of them.
+// Tile t of the class list: class c holds t in [cls_end[c-1], cls_end[c]).
 template <int DK, int DV, bool UNI>
-__global__ __launch_bounds__((DK / 32) * (DV / 2))
-__attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_decode_kernel(TileArgs a) {
-  __shared__ SmemGdn<DK, DV> sm;
-  int t = blockIdx.x;
+__device__ __forceinline__ void merged_tile(const TileArgs& a, int t, SmemGdn<DK, DV>& sm) {
   int c = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) c += t >= a.cls_end[j] ? 1 : 0;
@@ -580,16 +578,10 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_decode_kernel(TileArgs a) {
   }
 }
 
-// Decode of class 0 alone with its width fixed at compile time: the register
-// allocation and schedule are those of that width only.
+// Tile of class 0 at batch row bi, class head j, its width fixed at compile time.
 template <int DK, int DV, int BITS, bool UNI>
-__global__ __launch_bounds__((DK / 32) * (DV / 2))
-__attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_class_kernel(TileArgs a) {
-  __shared__ SmemGdn<DK, DV> sm;
-  // grid (heads of the class, batch rows): the same order as tile
-  // bi * n + j, without a division
-  const int bi = blockIdx.y;
-  const int h = wuni(a.P.cls_heads[a.cls_first[0] + (int)blockIdx.x]);
+__device__ __forceinline__ void class0_tile(const TileArgs& a, int bi, int j, SmemGdn<DK, DV>& sm) {
+  const int h = wuni(a.P.cls_heads[a.cls_first[0] + j]);
   const int tile = bi * a.P.H + h;
   const int slot = wuni(a.slots[bi]);
   if (slot < 0 || (long long)slot >= a.n_slots) {
@@ -599,6 +591,46 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_class_kernel(TileArgs a) {
   unsigned char* base = a.pool + (long long)slot * a.P.slot_bytes + wuni(a.P.head_off[h]);
   if constexpr (BITS == 16) pivot_tile<DK, DV, OP_DECODE>(a, tile, h, base, sm);
   else quant_tile<DK, DV, BITS, UNI, OP_DECODE>(a, tile, h, base, sm);
+}
+
+// Decode of every code-width class in one grid.  Class i covers blockIdx in
+// [cls_end[i-1], cls_end[i]); inside a class, tile t = (batch row t / cls_n,
+// class head t % cls_n).  The width is uniform over a workgroup, so each
+// workgroup runs exactly one of the width-specialised bodies; the kernel's
+// register budget is the largest of them.
+template <int DK, int DV, bool UNI>
+__global__ __launch_bounds__((DK / 32) * (DV / 2))
+__attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_decode_kernel(TileArgs a) {
+  __shared__ SmemGdn<DK, DV> sm;
+  merged_tile<DK, DV, UNI>(a, blockIdx.x, sm);
+}
+
+// STEP decode of class 0 in its width-specialised body plus the other classes
+// in one grid: rows y < pre_rows (cls_n[0] workgroups each) take the other
+// classes' tiles first, so the heavier FP16 and small-class tiles start with
+// the first wave of workgroups instead of in a second launch after the last.
+template <int DK, int DV, int BITS>
+__global__ __launch_bounds__((DK / 32) * (DV / 2))
+__attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_split_kernel(TileArgs a) {
+  __shared__ SmemGdn<DK, DV> sm;
+  const int y = blockIdx.y;
+  if (y < a.pre_rows) {
+    const int t = a.cls_end[0] + y * (int)gridDim.x + (int)blockIdx.x;
+    if (t < a.n_tiles) merged_tile<DK, DV, false>(a, t, sm);
+    return;
+  }
+  class0_tile<DK, DV, BITS, false>(a, y - a.pre_rows, blockIdx.x, sm);
+}
+
+// Decode of class 0 alone with its width fixed at compile time: the register
+// allocation and schedule are those of that width only.
+template <int DK, int DV, int BITS, bool UNI>
+__global__ __launch_bounds__((DK / 32) * (DV / 2))
+__attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_class_kernel(TileArgs a) {
+  __shared__ SmemGdn<DK, DV> sm;
+  // grid (heads of the class, batch rows): the same order as tile
+  // bi * n + j, without a division
+  class0_tile<DK, DV, BITS, UNI>(a, blockIdx.y, blockIdx.x, sm);
 }
 
 template <int DK, int DV, int BITS>
@@ -654,6 +686,30 @@ hipError_t launch_decode_gdn(const TileArgs& a, bool solo, hipStream_t s) {
   if (dk == 64 && dv == 64) return launch_decode<64, 64>(a, solo, s);
   if (dk == 128 && dv == 64) return launch_decode<128, 64>(a, solo, s);
   if (dk == 64 && dv == 128) return launch_decode<64, 128>(a, solo, s);
+  return hipErrorInvalidValue;
+}
+
+template <int DK, int DV>
+hipError_t launch_split(const TileArgs& a, hipStream_t s) {
+  const dim3 grid(a.cls_n[0], a.B + a.pre_rows), block((DK / 32) * (DV / 2));
+  switch (a.cls_bits[0]) {
+    case 2: hipLaunchKernelGGL((gdn_split_kernel<DK, DV, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gdn_split_kernel<DK, DV, 4>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((gdn_split_kernel<DK, DV, 6>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((gdn_split_kernel<DK, DV, 8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((gdn_split_kernel<DK, DV, 16>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_split_gdn(const TileArgs& a, hipStream_t s) {
+  if (a.P.mode != SQ_MODE_STEP || a.B + a.pre_rows > 65535) return hipErrorInvalidValue;
+  const int dk = a.P.dk, dv = a.P.dv;
+  if (dk == 128 && dv == 128) return launch_split<128, 128>(a, s);
+  if (dk == 64 && dv == 64) return launch_split<64, 64>(a, s);
+  if (dk == 128 && dv == 64) return launch_split<128, 64>(a, s);
+  if (dk == 64 && dv == 128) return launch_split<64, 128>(a, s);
   return hipErrorInvalidValue;
 }
 

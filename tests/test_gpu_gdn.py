@@ -290,8 +290,9 @@ def _full_size_pool_sampled(plan, extra_tiles):
 
 
 def test_full_size_gdn_pool_sampled():
-    """Nominal 4-bit STEP at the pool shape: 45 4-bit heads in their own
-    launch, two 2-bit heads and the FP16 pivot head in the merged launch."""
+    """Nominal 4-bit STEP at the pool shape, one split launch: the 45 4-bit
+    heads in the width-specialised body, the two 2-bit heads and the FP16
+    pivot head in the grid rows ahead of them."""
     rng = np.random.default_rng(34)
     bits = np.full(48, 4)
     bits[[5, 29]] = 2
