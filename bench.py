@@ -30,10 +30,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "state-update steps/s and HBM GB/s (% of peak) at batch 512, 1 GPU"
-# kernels one decode step launches (GDN STEP: the largest code-width class alone,
-# the other classes in one merged launch)
-KERNEL = {"step": "gdn_class_kernel<128,128,b> for the largest code-width class + "
-                  "gdn_decode_kernel<128,128> for the other classes",
+# the kernel one decode step launches
+KERNEL = {"step": "gdn_split_kernel<128,128,b> (largest code-width class in its width-specialised "
+                  "body, the other classes in leading grid rows) when that class has >= 16,384 tiles, "
+                  "else gdn_decode_kernel<128,128>",
           "uniform": "gdn_class_kernel<d,d,b,uniform>", "window": "window_tile_kernel<128,128,16>",
           "kda": "kda_tile_kernel<128,128>", "dense": "dense_kernel<128,128> (fp32 state)"}
 # sources whose change invalidates a committed traffic measurement, per kernel family
