@@ -200,6 +200,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gdn_pool_step4")
     ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the timed steps one by one instead of replaying them as a HIP graph")
     ap.add_argument("--input-sets", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -258,6 +260,8 @@ def main():
                    "slot_bytes": (w.heads * w.d_k * w.d_v * 4 if desc is None else desc["slot_bytes"]),
                    "layers_rotated": args.layers,
                    "input_sets": args.input_sets, "algorithmic_bytes_per_step": abytes,
+                   "timed_loop": ("eager launches" if args.eager else
+                                  "one HIP graph replay of the K steps (captured after warm-up)"),
                    "state_gbs": gbs_step, "pct_of_hbm_peak": 100.0 * gbs_step / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": gbs_kernel, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": gbs_kernel / HBM_PEAK_GBS,
@@ -322,28 +326,44 @@ def measure(sq, w, args) -> dict:
     stream = torch.cuda.current_stream()
     kind = 0 if w.kind == "gdn" else 1
 
-    def step(i):
+    def step(i, st=None):
+        st = stream if st is None else st
         pl = pools[i % len(pools)]
         s = sets[i % len(sets)]
         if dense:
             sq.sq_dense_step(kind, w.heads, w.d_k, w.d_v, pl["pool"], w.n_slots, slots_dev,
                              w.batch, s["q"], s["k"], s["v"], s["beta"], s["gate"],
-                             y[i % len(sets)], stream)
+                             y[i % len(sets)], st)
         else:
             sq.sq_decode_step(plan, pl["dev_plan"], pl["pool"], w.n_slots, slots_dev, w.batch,
                               s["q"], s["k"], s["v"], s["beta"], s["gate"], y[i % len(sets)],
-                              stream)
+                              st)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    graph = None
+    if not args.eager:
+        # the K timed steps captured once as a HIP graph (the same launches,
+        # arguments and in-place pool updates); one untimed replay first
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            for i in range(args.steps):
+                step(args.warmup + i, cap)
+        graph.replay()
+        torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(args.warmup + i)
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
+    del graph
 
     # per-launch durations with events on the launch stream (second pass)
     n_ev = min(args.steps, 64)
