@@ -493,42 +493,45 @@ __device__ __forceinline__ void pivot_tile(const TileArgs& a, const int tile, co
 }
 
 // ---------------------------------------------------------------------------
-// STEP GDN decode of a 4-bit 128 x 128 head with the delta-rule write on the
-// matrix cores (STEPQuant Sec. 3 Eq. 1, Sec. 4.3, App. A and C).
+// STEP GDN decode of a 4-bit 128 x 128 head with the linear algebra of the
+// step on the matrix cores (STEPQuant Sec. 3 Eq. 1, Sec. 4.3, App. A and C).
 //
 // Geometry.  Wave w owns rows 32w .. 32w + 31.  Lane l (n = l & 31, g = l >> 5)
 // loads piece g (rows 16g .. 16g + 15 of the row block) of the chunks of
 // column pairs n and n + 32, so it holds rows 32w + 16g + r (r = 0..15) of the
-// four columns col(c, n) = 2n + (c & 1) + 64 (c >> 1), value xb[c][r].  This
-// is the accumulator layout of a 32 x 32 MFMA block c whose output row i is
-// the wave's row sig(i) = 16 ((i >> 2) & 1) + 4 (i >> 3) + (i & 3) and whose
-// output column j is col(c, j); the slot layout is the same as for every
-// other tile-uniform head.
+// four columns col(c, n) = 2n + (c & 1) + 64 (c >> 1).  Kept as bf16 pairs
+// (bw[c][hf]: rows 8 hf .. 8 hf + 7), these are the right operand of a 32 x 32
+// x 16 bf16 MFMA whose K index 8g + p is the wave's row 16g + 8hf + p, and the
+// accumulator of a 32 x 32 block c holds, on lane l, exactly the lane's own
+// rows and columns (output row i is the wave's row
+// sig(i) = 16 ((i >> 2) & 1) + 4 (i >> 3) + (i & 3)).  The slot layout is the
+// same as for every other tile-uniform head.
 //
-// Arithmetic.  With rho_i = alpha r_i / q_b (the retained row factor),
-// g_i = beta k_i / rho_i and h_j = e_j / c_j, the updated tile is
-// X_ij = rho_i c_j Xh_ij / 16 with
-//   Xh_ij = 16 z_ij + 16 g_i h_j
-// the product of the column 16 g and the row h added to the unpacked codes:
-// one v_mfma_f32_32x32x2_f32 per block and no vector instruction per element.
-// A code is unpacked as 16 z: its nibble is moved to the top of a byte, which
-// a sign-extending byte select converts, one instruction per code.
+// Arithmetic.  A code is unpacked as 16 z (its nibble moved to the top of a
+// byte, which a sign-extending byte select converts), exact in bf16.  With
+// rho_i = alpha r_i / q_b (the retained row factor), g_i = beta k_i / rho_i and
+// h_j = e_j / c_j, the updated tile is X_ij = rho_i c_j Xh_ij / 16 with
+//   Xh_ij = 16 z_ij + 16 g_i h_j.
 // Key retrieval and readout are column sums of the old codes, taken by
-// bf16 MFMAs whose left operand holds three bf16 parts of each row weight
-// (their sum is the fp32 weight to 2^-24) and whose right operand holds the
-// codes, exact in bf16:
+// 16 x 16 x 32 bf16 MFMAs whose left operand holds three bf16 parts of each
+// row weight (their sum is the fp32 weight to 2^-24):
 //   delta_j = c_j sum_i kappa_i z_ij,   kappa_i = k_i rho_i
-//   y_j     = c_j sum_i theta_i z_ij + e_j beta (q . k),   theta_i = q_i rho_i
-// Everything after the write works on Xh, the column factor c_j entering the
-// column statistics once per column:
-//   m_i     = rho_i / (16 d_v) sum_j c_j |Xh_ij|
-//   P_ij    = X_ij / r_i = c_j P'_ij,   P'_ij = pi_i Xh_ij, pi_i = rho_i / (16 r_i)
-//   c0_j    = FP16(c_j max_i |P'_ij|),        z_ij = rne(P'_ij tau_j), tau_j = q_b c_j / c0_j
-//   c_j'    = FP16(q_b c_j N'_j / D_j),       N'_j = sum_i lambda_i z P', D_j = sum_i lambda_i z^2
+//   y_j     = c_j sum_i theta_i z_ij + e_j beta (q . k),   theta_i = q_i rho_i.
+// Xh itself is built block by block for the row statistic: an identity left
+// operand copies 16 z into the accumulator and one v_mfma_f32_32x32x2_f32
+// adds the product of the column 16 g and the row h:
+//   m_i = rho_i / (16 d_v) sum_j c_j |Xh_ij|.
+// Once r_i is known, P_ij = X_ij / r_i = c_j P'_ij is built the same way with a
+// diagonal left operand (three bf16 parts of pi_i = rho_i / (16 r_i)) and the
+// column 16 pi_i g_i, so no vector instruction scales an element:
+//   P'_ij = pi_i Xh_ij
+//   c0_j  = FP16(c_j max_i |P'_ij|),   z_ij = rne(P'_ij tau_j), tau_j = q_b c_j / c0_j
+//   c_j'  = FP16(q_b c_j N'_j / D_j),  N'_j = sum_i lambda_i z P', D_j = sum_i lambda_i z^2
 // with lambda_i = w_i^2 r_i^2 / q_b, as in the vector body above.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 // the three bf16 parts of x (round to nearest even each time): x - b0 and
 // x - b0 - b1 are exact in fp32, and b0 + b1 + b2 = x to 2^-24 relative
@@ -544,25 +547,22 @@ __device__ __forceinline__ void bf16_parts(float x, unsigned short (&b)[3]) {
 constexpr int kMxRowT = 16 * 36 + 32;  // row partials of one half-wave: [r][n], row stride 36
 
 struct alignas(16) SmemMx {
-  float rowc[6][128];      // per row: 4 pi, 5 lambda
+  float rowc[6][128];      // per row: 5 lambda
   float colA[4][128];      // per wave and column: retrieval, readout, max |P'|
   float colB[4][128];
   float colM[4][128];
   float2 colC[4][128];     // (N', D)
+  // row partials; afterwards each wave's first 1.5 KB hold the diagonal
+  // operand of pi: [part][row][8 bf16], the part at position row & 7
   float rowt[4][2 * kMxRowT];
-  unsigned short spl[6][128];  // bf16 parts of kappa (0..2) and theta (3..5) per row
-  uint32_t zro[4][8];          // 32 zero bytes per wave: the unused MFMA rows
-  float qk[4];                 // per wave: sum_i q_i k_i
+  unsigned short spl[6][128];    // bf16 parts of kappa (0..2) and theta (3..5) per row
+  unsigned short dgi[4][32][8];  // per wave: the identity as a diagonal operand
+  uint32_t zro[4][8];            // 32 zero bytes per wave: the unused MFMA rows
+  float qk[4];                   // per wave: sum_i q_i k_i
 };
 
 // wave row of MFMA output row i (i < 32)
 __device__ __forceinline__ int mx_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
-// sum of a value and the one 32 lanes away, in both lanes
-__device__ __forceinline__ float pair_sum(float v) {
-  float a, b;
-  swap32(v, a, b);
-  return a + b;
-}
 // Two half-wave sums from one exchange: v_permlane32_swap trades the upper
 // half of u with the lower half of v, so the lower 32 lanes receive
 // u[l] + u[l + 32] and the upper 32 lanes v[l - 32] + v[l].
@@ -573,6 +573,9 @@ __device__ __forceinline__ float halves_sum(float u, float v) {
 __device__ __forceinline__ float halves_max(float u, float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(u), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ bf16x8 lds_bf16x8(int addr) {
+  return __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(uintptr_t)addr);
 }
 
 template <bool CLAMP>
@@ -617,7 +620,7 @@ __device__ __forceinline__ void step4_mfma_tile(const TileArgs& a, const int til
   constexpr float QB = 7.0f;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 31, g = l >> 5;
   const int r0 = 32 * w + 16 * g;             // first of the lane's 16 rows
-  const int ro = 32 * w + mx_row(n);          // row whose constants lane n (< 32) derives
+  const int rw = mx_row(n), ro = 32 * w + rw; // row whose constants lane n (< 32) derives
   __half* rs_ptr = reinterpret_cast<__half*>(base + wuni(a.P.r_off[h]));
   __half* c_ptr = reinterpret_cast<__half*>(base + wuni(a.P.c_off[h]));
   const long long tk = (long long)tile * 128, tv = (long long)tile * 128;
@@ -633,6 +636,8 @@ __device__ __forceinline__ void step4_mfma_tile(const TileArgs& a, const int til
   const float2 vb = *reinterpret_cast<const float2*>(a.v + tv + 2 * n + 64);
   const float vv[4] = {va.x, va.y, vb.x, vb.y};
 
+  // the identity as a diagonal operand: row rw's entry holds 1.0 at position rw & 7
+  *(__attribute__((address_space(3))) uint2*)(uintptr_t)lds_addr(&sm.dgi[w][0][4 * l]) = make_uint2(0u, 0u);
   const float beta = wuni(a.beta[tile]);
   float gam = 0.f, rp = 0.f, qk = 0.f;
   if (g == 0) {
@@ -654,6 +659,7 @@ __device__ __forceinline__ void step4_mfma_tile(const TileArgs& a, const int til
     bf16_parts(the * 0.0625f, bp);
 #pragma unroll
     for (int q = 0; q < 3; ++q) sm.spl[3 + q][ro] = bp[q];
+    sm.dgi[w][rw][rw & 7] = 0x3f80u;   // bf16 1.0
   } else if (n < 8) {
     sm.zro[w][n] = 0u;
   }
@@ -662,8 +668,9 @@ __device__ __forceinline__ void step4_mfma_tile(const TileArgs& a, const int til
 
   // unpack: dword d of a piece holds rows 4d .. 4d+3 of its column pair, the
   // even column in the low nibbles; each nibble goes to the top of its byte,
-  // which then reads as the signed byte 16 z
-  f32x16 xb[4];
+  // which then reads as the signed byte 16 z; bf16 pairs of rows 2q, 2q + 1
+  // are the high halves of two such floats
+  u32x4 bw[4][2];
   {
     const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
@@ -671,10 +678,18 @@ __device__ __forceinline__ void step4_mfma_tile(const TileArgs& a, const int til
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const uint32_t lo = (pw[4 * q + d] << 4) & 0xf0f0f0f0u, hi = pw[4 * q + d] & 0xf0f0f0f0u;
+        float fl[4], fh[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          xb[2 * q][4 * d + k] = (float)(signed char)(lo >> (8 * k));
-          xb[2 * q + 1][4 * d + k] = (float)(signed char)(hi >> (8 * k));
+          fl[k] = (float)(signed char)(lo >> (8 * k));
+          fh[k] = (float)(signed char)(hi >> (8 * k));
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          bw[2 * q][d >> 1][2 * (d & 1) + e] =
+              __builtin_amdgcn_perm(__float_as_uint(fl[2 * e + 1]), __float_as_uint(fl[2 * e]), 0x07060302u);
+          bw[2 * q + 1][d >> 1][2 * (d & 1) + e] =
+              __builtin_amdgcn_perm(__float_as_uint(fh[2 * e + 1]), __float_as_uint(fh[2 * e]), 0x07060302u);
         }
       }
     }
@@ -694,21 +709,13 @@ __device__ __forceinline__ void step4_mfma_tile(const TileArgs& a, const int til
     const bool use = sp < 3 && (qq & 1) == (G & 1);
     const int aaddr = use ? lds_addr(&sm.spl[3 * (qq >> 1) + sp][32 * w + 16 * (G >> 1)])
                           : lds_addr(&sm.zro[w][0]);
-    const bf16x8 A0 = __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)aaddr);
-    const bf16x8 A1 = __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(aaddr + 16));
+    const bf16x8 A0 = lds_bf16x8(aaddr), A1 = lds_bf16x8(aaddr + 16);
     float s[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        u32x4 bw;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)   // bf16 of the codes: the high halves of their floats
-          bw[q] = __builtin_amdgcn_perm(__float_as_uint(xb[c][8 * hf + 2 * q + 1]),
-                                        __float_as_uint(xb[c][8 * hf + 2 * q]), 0x07060302u);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hf ? A1 : A0, __builtin_bit_cast(bf16x8, bw), acc, 0, 0, 0);
-      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8, bw[c][0]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8, bw[c][1]), acc, 0, 0, 0);
       s[c] = (acc[0] + acc[1]) + acc[2];
     }
     float* dst = g ? &sm.colB[w][0] : &sm.colA[w][0];
@@ -737,61 +744,90 @@ __device__ __forceinline__ void step4_mfma_tile(const TileArgs& a, const int til
     eo0 = g ? e[2] : e[0];
     eo1 = g ? e[3] : e[1];
   }
-  // pass 2: Xh = 16 z + (16 g_i) h_j on the matrix cores (the second K
-  // index carries zeros)
-#pragma unroll
-  for (int c = 0; c < 4; ++c) xb[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(gam, hh[c], xb[c], 0, 0, 0);
-
-  // the row statistic sum_j c_j |Xh_ij|
+  // The left operand of a diagonal product for chunk hf: lane l holds row
+  // i = n, K positions 8g + p = rows 16g + 8hf + p; its entry is the row's
+  // own if that row lies among them, else zeros.
+  const bool dsel0 = (rw >> 4) == g && ((rw >> 3) & 1) == 0;
+  const bool dsel1 = (rw >> 4) == g && ((rw >> 3) & 1) == 1;
+  // pass 2: Xh = 16 z + (16 g_i) h_j block by block (the second K index of the
+  // fp32 MFMA carries zeros), and the row statistic sum_j c_j |Xh_ij|
   {
+    const int zaddr = lds_addr(&sm.zro[w][0]), iaddr = lds_addr(&sm.dgi[w][rw][0]);
+    const bf16x8 I0 = lds_bf16x8(dsel0 ? iaddr : zaddr), I1 = lds_bf16x8(dsel1 ? iaddr : zaddr);
+    float rs[16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      f32x16 x = {};
+      x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(I0, __builtin_bit_cast(bf16x8, bw[c][0]), x, 0, 0, 0);
+      x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(I1, __builtin_bit_cast(bf16x8, bw[c][1]), x, 0, 0, 0);
+      x = __builtin_amdgcn_mfma_f32_32x32x2f32(gam, hh[c], x, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rs[r] = c == 0 ? cc[0] * fabsf(x[r]) : fmaf(cc[c], fabsf(x[r]), rs[r]);
+    }
     const int rt = lds_addr(&sm.rowt[w][g * kMxRowT + n]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float s = cc[0] * fabsf(xb[0][r]);
-      s = fmaf(cc[1], fabsf(xb[1][r]), s);
-      s = fmaf(cc[2], fabsf(xb[2][r]), s);
-      s = fmaf(cc[3], fabsf(xb[3][r]), s);
-      *(__attribute__((address_space(3))) float*)(uintptr_t)(rt + 4 * 36 * r) = s;
-    }
+    for (int r = 0; r < 16; ++r) *(__attribute__((address_space(3))) float*)(uintptr_t)(rt + 4 * 36 * r) = rs[r];
   }
   wave_sync();
+  float gpi = 0.f;
+  const int dgp = lds_addr(&sm.rowt[w][0]);   // diagonal operand of pi: 3 x 32 x 16 bytes
   {
     // lane l sums half (l >> 5) of row mx_row(l & 31) over the 32 lanes of its half-wave
-    const int rr = mx_row(n);
-    const int rd = lds_addr(&sm.rowt[w][(rr >> 4) * kMxRowT + (rr & 15) * 36 + 16 * g]);
+    const int rd = lds_addr(&sm.rowt[w][(rw >> 4) * kMxRowT + (rw & 15) * 36 + 16 * g]);
     float s = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 v4 = lds_ld4(rd + 16 * q);
       s += (v4.x + v4.y) + (v4.z + v4.w);
     }
-    s = pair_sum(s);
+    s = halves_sum(s, s);
+    // the partials are read: the region now takes the diagonal operand of pi
+    const uint2 z2 = make_uint2(0u, 0u);
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      *(__attribute__((address_space(3))) uint2*)(uintptr_t)(dgp + 512 * q + 8 * l) = z2;
     if (g == 0) {
       const float wi = a.P.w[h * 128 + ro];
       // the hardware square root (1 ulp) only feeds an FP16 rounding
       const float ri =
           fp16_scale(__builtin_amdgcn_sqrtf(rp * s * (1.0f / 2048.0f) * a.P.winv[h * 128 + ro]));
       rs_ptr[ro] = __float2half_rn(ri);
-      sm.rowc[4][ro] = rp * 0.0625f * frcp(ri);        // pi: P' = Xh pi_i
+      const float pi = rp * 0.0625f * frcp(ri);        // pi: P' = Xh pi_i
+      gpi = gam * pi;
       sm.rowc[5][ro] = wi * wi * ri * ri * (1.0f / QB);  // lambda: refit weight
+      unsigned short bp[3];
+      bf16_parts(pi, bp);
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        *(__attribute__((address_space(3))) unsigned short*)(uintptr_t)(dgp + 512 * q + 16 * rw + 2 * (rw & 7)) = bp[q];
     }
   }
   wave_sync();
-  // pass 3: P' = pi_i Xh and the column maxima of |P'|
-  float mx[4] = {0.f, 0.f, 0.f, 0.f};
+  // pass 3: P' = pi_i Xh = diag(pi) 16 z + (16 pi_i g_i) h_j on the matrix
+  // cores, and the column maxima of |P'|
+  f32x16 xb[4];
+  float mx[4];
   {
-    const int pcb = lds_addr(&sm.rowc[4][r0]);
+    const int zaddr = lds_addr(&sm.zro[w][0]);
+    bf16x8 Pa[3][2];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const float4 p4 = lds_ld4(pcb + 16 * d);
-      const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+    for (int q = 0; q < 3; ++q) {
+      Pa[q][0] = lds_bf16x8(dsel0 ? dgp + 512 * q + 16 * rw : zaddr);
+      Pa[q][1] = lds_bf16x8(dsel1 ? dgp + 512 * q + 16 * rw : zaddr);
+    }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 4; ++c) {
+      f32x16 x = {};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) xb[c][4 * d + k] *= pv[k];
-        mx[c] = fmaxf(fmaxf(mx[c], fabsf(xb[c][4 * d])), fabsf(xb[c][4 * d + 1]));
-        mx[c] = fmaxf(fmaxf(mx[c], fabsf(xb[c][4 * d + 2])), fabsf(xb[c][4 * d + 3]));
+      for (int q = 0; q < 3; ++q) {
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pa[q][0], __builtin_bit_cast(bf16x8, bw[c][0]), x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pa[q][1], __builtin_bit_cast(bf16x8, bw[c][1]), x, 0, 0, 0);
       }
+      xb[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(gpi, hh[c], x, 0, 0, 0);
+      float m = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) m = fmaxf(fmaxf(m, fabsf(xb[c][r])), fabsf(xb[c][r + 1]));
+      mx[c] = m;
     }
     *reinterpret_cast<float2*>(&sm.colM[w][2 * n + 64 * g]) =
         make_float2(halves_max(mx[0], mx[2]), halves_max(mx[1], mx[3]));
