@@ -492,428 +492,10 @@ __device__ __forceinline__ void pivot_tile(const TileArgs& a, const int tile, co
   store_chunk<16, NP>(base, rb, p, wd);
 }
 
-// ---------------------------------------------------------------------------
-// STEP GDN decode of a 4-bit 128 x 128 head with the linear algebra of the
-// step on the matrix cores (STEPQuant Sec. 3 Eq. 1, Sec. 4.3, App. A and C).
-//
-// Geometry.  Wave w owns rows 32w .. 32w + 31.  Lane l (n = l & 31, g = l >> 5)
-// loads piece g (rows 16g .. 16g + 15 of the row block) of the chunks of
-// column pairs n and n + 32, so it holds rows 32w + 16g + r (r = 0..15) of the
-// four columns col(c, n) = 2n + (c & 1) + 64 (c >> 1).  Kept as bf16 pairs
-// (bw[c][hf]: rows 8 hf .. 8 hf + 7), these are the right operand of a 32 x 32
-// x 16 bf16 MFMA whose K index 8g + p is the wave's row 16g + 8hf + p, and the
-// accumulator of a 32 x 32 block c holds, on lane l, exactly the lane's own
-// rows and columns (output row i is the wave's row
-// sig(i) = 16 ((i >> 2) & 1) + 4 (i >> 3) + (i & 3)).  The slot layout is the
-// same as for every other tile-uniform head.
-//
-// Arithmetic.  A code is unpacked as 16 z (its nibble moved to the top of a
-// byte, which a sign-extending byte select converts), exact in bf16.  With
-// rho_i = alpha r_i / q_b (the retained row factor), g_i = beta k_i / rho_i and
-// h_j = e_j / c_j, the updated tile is X_ij = rho_i c_j Xh_ij / 16 with
-//   Xh_ij = 16 z_ij + 16 g_i h_j.
-// Key retrieval and readout are column sums of the old codes, taken by
-// 16 x 16 x 32 bf16 MFMAs whose left operand holds three bf16 parts of each
-// row weight (their sum is the fp32 weight to 2^-24):
-//   delta_j = c_j sum_i kappa_i z_ij,   kappa_i = k_i rho_i
-//   y_j     = c_j sum_i theta_i z_ij + e_j beta (q . k),   theta_i = q_i rho_i.
-// Xh itself is built block by block for the row statistic: an identity left
-// operand copies 16 z into the accumulator and one v_mfma_f32_32x32x2_f32
-// adds the product of the column 16 g and the row h:
-//   m_i = rho_i / (16 d_v) sum_j c_j |Xh_ij|.
-// Once r_i is known, P_ij = X_ij / r_i = c_j P'_ij is built the same way with a
-// diagonal left operand (three bf16 parts of pi_i = rho_i / (16 r_i)) and the
-// column 16 pi_i g_i, so no vector instruction scales an element:
-//   P'_ij = pi_i Xh_ij
-//   c0_j  = FP16(c_j max_i |P'_ij|),   z_ij = rne(P'_ij tau_j), tau_j = q_b c_j / c0_j
-//   c_j'  = FP16(q_b c_j N'_j / D_j),  N'_j = sum_i lambda_i z P', D_j = sum_i lambda_i z^2
-// with lambda_i = w_i^2 r_i^2 / q_b, as in the vector body above.
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-
-// the three bf16 parts of x (round to nearest even each time): x - b0 and
-// x - b0 - b1 are exact in fp32, and b0 + b1 + b2 = x to 2^-24 relative
-__device__ __forceinline__ void bf16_parts(float x, unsigned short (&b)[3]) {
-#pragma unroll
-  for (int s = 0; s < 3; ++s) {
-    const __bf16 v = (__bf16)x;
-    b[s] = __builtin_bit_cast(unsigned short, v);
-    x -= (float)v;
-  }
-}
-
-constexpr int kMxRowT = 16 * 36 + 32;  // row partials of one half-wave: [r][n], row stride 36
-
-struct alignas(16) SmemMx {
-  float rowc[6][128];      // per row: 5 lambda
-  float colA[4][128];      // per wave and column: retrieval, readout, max |P'|
-  float colB[4][128];
-  float colM[4][128];
-  float2 colC[4][128];     // (N', D)
-  // row partials; afterwards each wave's first 1.5 KB hold the diagonal
-  // operand of pi: [part][row][8 bf16], the part at position row & 7
-  float rowt[4][2 * kMxRowT];
-  unsigned short spl[6][128];    // bf16 parts of kappa (0..2) and theta (3..5) per row
-  unsigned short dgi[4][32][8];  // per wave: the identity as a diagonal operand
-  uint32_t zro[4][8];            // 32 zero bytes per wave: the unused MFMA rows
-  float qk[4];                   // per wave: sum_i q_i k_i
-};
-
-// wave row of MFMA output row i (i < 32)
-__device__ __forceinline__ int mx_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
-// Two half-wave sums from one exchange: v_permlane32_swap trades the upper
-// half of u with the lower half of v, so the lower 32 lanes receive
-// u[l] + u[l + 32] and the upper 32 lanes v[l - 32] + v[l].
-__device__ __forceinline__ float halves_sum(float u, float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(u), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float halves_max(float u, float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(u), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ bf16x8 lds_bf16x8(int addr) {
-  return __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(uintptr_t)addr);
-}
-
-template <bool CLAMP>
-__device__ __forceinline__ void codes_refit_mx(f32x16 (&xb)[4], int lam, const float (&tau)[4],
-                                               float (&N)[4], float (&D)[4], uint32_t (&wd)[8]) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) N[c] = D[c] = 0.f;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const float4 l4 = lds_ld4(lam + 16 * d);
-    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float pv = xb[c][4 * d + k];
-        float m = fmaf(pv, tau[c], kMagic);
-        if constexpr (CLAMP) m = __builtin_amdgcn_fmed3f(m, kMagic - 7.f, kMagic + 7.f);
-        const float z = m - kMagic;
-        const float t = lv[k] * z;
-        N[c] = fmaf(t, pv, N[c]);
-        D[c] = fmaf(t, z, D[c]);
-        xb[c][4 * d + k] = m;
-      }
-    }
-    // dword d of each piece: rows 4d .. 4d+3, the even column in the low
-    // nibbles and the odd one in the high nibbles
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t lo = low_bytes4(xb[2 * q][4 * d], xb[2 * q][4 * d + 1], xb[2 * q][4 * d + 2],
-                                     xb[2 * q][4 * d + 3]);
-      const uint32_t hi = low_bytes4(xb[2 * q + 1][4 * d], xb[2 * q + 1][4 * d + 1],
-                                     xb[2 * q + 1][4 * d + 2], xb[2 * q + 1][4 * d + 3]);
-      wd[4 * q + d] = (lo & 0x0f0f0f0fu) | ((hi << 4) & 0xf0f0f0f0u);
-      asm volatile("" : "+v"(wd[4 * q + d]));
-    }
-  }
-}
-
-__device__ __forceinline__ void step4_mfma_tile(const TileArgs& a, const int tile, const int h,
-                                                unsigned char* base, SmemMx& sm) {
-  constexpr float QB = 7.0f;
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, n = l & 31, g = l >> 5;
-  const int r0 = 32 * w + 16 * g;             // first of the lane's 16 rows
-  const int rw = mx_row(n), ro = 32 * w + rw; // row whose constants lane n (< 32) derives
-  __half* rs_ptr = reinterpret_cast<__half*>(base + wuni(a.P.r_off[h]));
-  __half* c_ptr = reinterpret_cast<__half*>(base + wuni(a.P.c_off[h]));
-  const long long tk = (long long)tile * 128, tv = (long long)tile * 128;
-
-  // piece g of the chunks (row block w, column pair n) and (w, n + 32)
-  const int off0 = ((2 * w + g) * 64 + n) * 16;
-  const uint4 p0 = *reinterpret_cast<const uint4*>(base + off0);
-  const uint4 p1 = *reinterpret_cast<const uint4*>(base + off0 + 32 * 16);
-  const __half2 ca = *reinterpret_cast<const __half2*>(c_ptr + 2 * n);
-  const __half2 cb = *reinterpret_cast<const __half2*>(c_ptr + 2 * n + 64);
-  const float cc[4] = {__low2float(ca), __high2float(ca), __low2float(cb), __high2float(cb)};
-  const float2 va = *reinterpret_cast<const float2*>(a.v + tv + 2 * n);
-  const float2 vb = *reinterpret_cast<const float2*>(a.v + tv + 2 * n + 64);
-  const float vv[4] = {va.x, va.y, vb.x, vb.y};
-
-  // the identity as a diagonal operand: row rw's entry holds 1.0 at position rw & 7
-  *(__attribute__((address_space(3))) uint2*)(uintptr_t)lds_addr(&sm.dgi[w][0][4 * l]) = make_uint2(0u, 0u);
-  const float beta = wuni(a.beta[tile]);
-  float gam = 0.f, rp = 0.f, qk = 0.f;
-  if (g == 0) {
-    const float rsi = __half2float(rs_ptr[ro]);
-    const float alpha = wuni(a.gate[tile]);
-    const float kk = a.k[tk + ro], qq = a.q[tk + ro], bk = beta * kk;
-    const float rho = alpha * (rsi * (1.0f / QB));
-    // a vanishing retention keeps the division finite; the dropped part
-    // (rp - rho) c_j z_ij is below 2^-60 of the write term
-    rp = fmaxf(rho, fmaxf(fabsf(bk) * 0x1p-60f, 0x1p-100f));
-    const float kap = kk * rho;    // kappa: key retrieval weight
-    const float the = qq * rho;    // theta: readout weight on the old codes
-    qk = qq * kk;
-    gam = 16.0f * bk * frcp(rp);   // 16 g_i, the write's row factor
-    unsigned short bp[3];
-    bf16_parts(kap * 0.0625f, bp);   // the codes enter as 16 z
-#pragma unroll
-    for (int q = 0; q < 3; ++q) sm.spl[q][ro] = bp[q];
-    bf16_parts(the * 0.0625f, bp);
-#pragma unroll
-    for (int q = 0; q < 3; ++q) sm.spl[3 + q][ro] = bp[q];
-    sm.dgi[w][rw][rw & 7] = 0x3f80u;   // bf16 1.0
-  } else if (n < 8) {
-    sm.zro[w][n] = 0u;
-  }
-  // q . k over the wave's 32 rows
-  const float qks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(half32_sum_hi(qk)), 16));
-
-  // unpack: dword d of a piece holds rows 4d .. 4d+3 of its column pair, the
-  // even column in the low nibbles; each nibble goes to the top of its byte,
-  // which then reads as the signed byte 16 z; bf16 pairs of rows 2q, 2q + 1
-  // are the high halves of two such floats
-  u32x4 bw[4][2];
-  {
-    const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t lo = (pw[4 * q + d] << 4) & 0xf0f0f0f0u, hi = pw[4 * q + d] & 0xf0f0f0f0u;
-        float fl[4], fh[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          fl[k] = (float)(signed char)(lo >> (8 * k));
-          fh[k] = (float)(signed char)(hi >> (8 * k));
-        }
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          bw[2 * q][d >> 1][2 * (d & 1) + e] =
-              __builtin_amdgcn_perm(__float_as_uint(fl[2 * e + 1]), __float_as_uint(fl[2 * e]), 0x07060302u);
-          bw[2 * q + 1][d >> 1][2 * (d & 1) + e] =
-              __builtin_amdgcn_perm(__float_as_uint(fh[2 * e + 1]), __float_as_uint(fh[2 * e]), 0x07060302u);
-        }
-      }
-    }
-  }
-  if (l == 0) sm.qk[w] = qks;
-  wave_sync();
-  // pass 1: the column sums sum_i kappa_i z_ij (lanes l < 32) and
-  // sum_i theta_i z_ij (lanes l >= 32) over the wave's rows, on 16 x 16 x 32
-  // bf16 MFMAs.  Operand lane l sits in K-group G = l >> 4 and holds rows
-  // 16 (G >> 1) + 8 hf .. + 7 of column col(c, l & 31), so the groups 0, 2
-  // carry the columns of lanes n < 16 and the groups 1, 3 those of n >= 16;
-  // left-operand row i = 4 q + s takes part s (< 3) of kappa (q = 0, 1) or
-  // theta (q = 2, 3) from the groups of parity q & 1, and output row i lands
-  // in lane group q, on the lanes of its own column.
-  {
-    const int G = l >> 4, i = l & 15, qq = i >> 2, sp = i & 3;
-    const bool use = sp < 3 && (qq & 1) == (G & 1);
-    const int aaddr = use ? lds_addr(&sm.spl[3 * (qq >> 1) + sp][32 * w + 16 * (G >> 1)])
-                          : lds_addr(&sm.zro[w][0]);
-    const bf16x8 A0 = lds_bf16x8(aaddr), A1 = lds_bf16x8(aaddr + 16);
-    float s[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8, bw[c][0]), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8, bw[c][1]), acc, 0, 0, 0);
-      s[c] = (acc[0] + acc[1]) + acc[2];
-    }
-    float* dst = g ? &sm.colB[w][0] : &sm.colA[w][0];
-    *reinterpret_cast<float2*>(dst + 2 * n) = make_float2(s[0], s[1]);
-    *reinterpret_cast<float2*>(dst + 2 * n + 64) = make_float2(s[2], s[3]);
-  }
-  __syncthreads();
-  float hh[4], eo0, eo1;
-  {
-    float dsum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float2 x0 = *reinterpret_cast<const float2*>(&sm.colA[r][2 * n]);
-      const float2 x1 = *reinterpret_cast<const float2*>(&sm.colA[r][2 * n + 64]);
-      dsum[0] += x0.x;
-      dsum[1] += x0.y;
-      dsum[2] += x1.x;
-      dsum[3] += x1.y;
-    }
-    float e[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      e[c] = vv[c] - cc[c] * dsum[c];      // e_j = v_j - delta_j (beta is in g_i)
-      hh[c] = g ? 0.f : e[c] * frcp(cc[c]);
-    }
-    eo0 = g ? e[2] : e[0];
-    eo1 = g ? e[3] : e[1];
-  }
-  // The left operand of a diagonal product for chunk hf: lane l holds row
-  // i = n, K positions 8g + p = rows 16g + 8hf + p; its entry is the row's
-  // own if that row lies among them, else zeros.
-  const bool dsel0 = (rw >> 4) == g && ((rw >> 3) & 1) == 0;
-  const bool dsel1 = (rw >> 4) == g && ((rw >> 3) & 1) == 1;
-  // pass 2: Xh = 16 z + (16 g_i) h_j block by block (the second K index of the
-  // fp32 MFMA carries zeros), and the row statistic sum_j c_j |Xh_ij|
-  {
-    const int zaddr = lds_addr(&sm.zro[w][0]), iaddr = lds_addr(&sm.dgi[w][rw][0]);
-    const bf16x8 I0 = lds_bf16x8(dsel0 ? iaddr : zaddr), I1 = lds_bf16x8(dsel1 ? iaddr : zaddr);
-    float rs[16];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      f32x16 x = {};
-      x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(I0, __builtin_bit_cast(bf16x8, bw[c][0]), x, 0, 0, 0);
-      x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(I1, __builtin_bit_cast(bf16x8, bw[c][1]), x, 0, 0, 0);
-      x = __builtin_amdgcn_mfma_f32_32x32x2f32(gam, hh[c], x, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) rs[r] = c == 0 ? cc[0] * fabsf(x[r]) : fmaf(cc[c], fabsf(x[r]), rs[r]);
-    }
-    const int rt = lds_addr(&sm.rowt[w][g * kMxRowT + n]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) *(__attribute__((address_space(3))) float*)(uintptr_t)(rt + 4 * 36 * r) = rs[r];
-  }
-  wave_sync();
-  float gpi = 0.f;
-  const int dgp = lds_addr(&sm.rowt[w][0]);   // diagonal operand of pi: 3 x 32 x 16 bytes
-  {
-    // lane l sums half (l >> 5) of row mx_row(l & 31) over the 32 lanes of its half-wave
-    const int rd = lds_addr(&sm.rowt[w][(rw >> 4) * kMxRowT + (rw & 15) * 36 + 16 * g]);
-    float s = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 v4 = lds_ld4(rd + 16 * q);
-      s += (v4.x + v4.y) + (v4.z + v4.w);
-    }
-    s = halves_sum(s, s);
-    // the partials are read: the region now takes the diagonal operand of pi
-    const uint2 z2 = make_uint2(0u, 0u);
-#pragma unroll
-    for (int q = 0; q < 3; ++q)
-      *(__attribute__((address_space(3))) uint2*)(uintptr_t)(dgp + 512 * q + 8 * l) = z2;
-    if (g == 0) {
-      const float wi = a.P.w[h * 128 + ro];
-      // the hardware square root (1 ulp) only feeds an FP16 rounding
-      const float ri =
-          fp16_scale(__builtin_amdgcn_sqrtf(rp * s * (1.0f / 2048.0f) * a.P.winv[h * 128 + ro]));
-      rs_ptr[ro] = __float2half_rn(ri);
-      const float pi = rp * 0.0625f * frcp(ri);        // pi: P' = Xh pi_i
-      gpi = gam * pi;
-      sm.rowc[5][ro] = wi * wi * ri * ri * (1.0f / QB);  // lambda: refit weight
-      unsigned short bp[3];
-      bf16_parts(pi, bp);
-#pragma unroll
-      for (int q = 0; q < 3; ++q)
-        *(__attribute__((address_space(3))) unsigned short*)(uintptr_t)(dgp + 512 * q + 16 * rw + 2 * (rw & 7)) = bp[q];
-    }
-  }
-  wave_sync();
-  // pass 3: P' = pi_i Xh = diag(pi) 16 z + (16 pi_i g_i) h_j on the matrix
-  // cores, and the column maxima of |P'|
-  f32x16 xb[4];
-  float mx[4];
-  {
-    const int zaddr = lds_addr(&sm.zro[w][0]);
-    bf16x8 Pa[3][2];
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      Pa[q][0] = lds_bf16x8(dsel0 ? dgp + 512 * q + 16 * rw : zaddr);
-      Pa[q][1] = lds_bf16x8(dsel1 ? dgp + 512 * q + 16 * rw : zaddr);
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      f32x16 x = {};
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pa[q][0], __builtin_bit_cast(bf16x8, bw[c][0]), x, 0, 0, 0);
-        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pa[q][1], __builtin_bit_cast(bf16x8, bw[c][1]), x, 0, 0, 0);
-      }
-      xb[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(gpi, hh[c], x, 0, 0, 0);
-      float m = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) m = fmaxf(fmaxf(m, fabsf(xb[c][r])), fabsf(xb[c][r + 1]));
-      mx[c] = m;
-    }
-    *reinterpret_cast<float2*>(&sm.colM[w][2 * n + 64 * g]) =
-        make_float2(halves_max(mx[0], mx[2]), halves_max(mx[1], mx[3]));
-  }
-  __syncthreads();
-  if (w == 0) {  // head output y_j = c_j sum over the waves + e_j beta (q . k)
-    float s0 = 0.f, s1 = 0.f, qkt = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float2 x = *reinterpret_cast<const float2*>(&sm.colB[r][2 * n + 64 * g]);
-      s0 += x.x;
-      s1 += x.y;
-      qkt += sm.qk[r];
-    }
-    const float bq = beta * qkt;
-    const float c0 = g ? cc[2] : cc[0], c1 = g ? cc[3] : cc[1];
-    *reinterpret_cast<float2*>(a.y + tv + 2 * n + 64 * g) = make_float2(fmaf(c0, s0, eo0 * bq), fmaf(c1, s1, eo1 * bq));
-  }
-  float tau[4], cmax = 0.f, cz0, cz1;
-  {
-    float m[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float2 x0 = *reinterpret_cast<const float2*>(&sm.colM[r][2 * n]);
-      const float2 x1 = *reinterpret_cast<const float2*>(&sm.colM[r][2 * n + 64]);
-      m[0] = fmaxf(m[0], x0.x);
-      m[1] = fmaxf(m[1], x0.y);
-      m[2] = fmaxf(m[2], x1.x);
-      m[3] = fmaxf(m[3], x1.y);
-    }
-    float cz[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float mc = cc[c] * m[c];               // max_i |X_ij| / r_i
-      cmax = fmaxf(cmax, mc);
-      cz[c] = fp16_scale(mc);
-      tau[c] = QB * cc[c] * frcp(cz[c]);
-    }
-    cz0 = g ? cz[2] : cz[0];
-    cz1 = g ? cz[3] : cz[1];
-  }
-  const float co0 = g ? cc[2] : cc[0], co1 = g ? cc[3] : cc[1];
-  // below the FP16 maximum, c0 >= max |P| (1 - 2^-11) keeps every code within
-  // +-7 without a clamp; a wave holding a saturated column clamps all of its
-  // codes (a no-op on the others), the decision staying wave-uniform
-  const bool sat = __ballot(cmax > kFp16Max) != 0ull;
-  float N[4], D[4];
-  uint32_t wd[8];
-  const int lcb = lds_addr(&sm.rowc[5][r0]);
-  if (sat) codes_refit_mx<true>(xb, lcb, tau, N, D, wd);
-  else codes_refit_mx<false>(xb, lcb, tau, N, D, wd);
-  *reinterpret_cast<float4*>(&sm.colC[w][2 * n + 64 * g]) =
-      make_float4(halves_sum(N[0], N[2]), halves_sum(D[0], D[2]), halves_sum(N[1], N[3]),
-                  halves_sum(D[1], D[3]));
-  __syncthreads();
-  if (w == 0) {
-    float n0 = 0.f, n1 = 0.f, d0 = 0.f, d1 = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float4 x = *reinterpret_cast<const float4*>(&sm.colC[r][2 * n + 64 * g]);
-      n0 += x.x;
-      d0 += x.y;
-      n1 += x.z;
-      d1 += x.w;
-    }
-    const float cf0 = d0 > 0.f ? fp16_scale(QB * co0 * n0 * frcp(d0)) : cz0;
-    const float cf1 = d1 > 0.f ? fp16_scale(QB * co1 * n1 * frcp(d1)) : cz1;
-    *reinterpret_cast<__half2*>(c_ptr + 2 * n + 64 * g) = __halves2half2(__float2half_rn(cf0), __float2half_rn(cf1));
-  }
-  *reinterpret_cast<uint4*>(base + off0) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-  *reinterpret_cast<uint4*>(base + off0 + 32 * 16) = make_uint4(wd[4], wd[5], wd[6], wd[7]);
-}
-
-// LDS of a tile kernel: the vector body's layout, or the MFMA body's where
-// that one runs (128 x 128 heads)
-template <int DK, int DV>
-constexpr size_t smem_bytes() {
-  return (DK == 128 && DV == 128 && sizeof(SmemMx) > sizeof(SmemGdn<DK, DV>)) ? sizeof(SmemMx)
-                                                                              : sizeof(SmemGdn<DK, DV>);
-}
-
 template <int DK, int DV, int OP>
 __global__ __launch_bounds__((DK / 32) * (DV / 2))
 __attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_tile_kernel(TileArgs a) {
-  __shared__ __align__(16) unsigned char smraw[smem_bytes<DK, DV>()];
-  SmemGdn<DK, DV>& sm = *reinterpret_cast<SmemGdn<DK, DV>*>(smraw);
+  __shared__ SmemGdn<DK, DV> sm;
   const int tile = blockIdx.x;
   int h = 0;
   unsigned char* base = nullptr;
@@ -986,12 +568,7 @@ __device__ __forceinline__ void merged_tile(const TileArgs& a, int t, SmemGdn<DK
   unsigned char* base = a.pool + (long long)slot * a.P.slot_bytes + wuni(a.P.head_off[h]);
   switch (bits) {
     case 2: quant_tile<DK, DV, 2, UNI, OP_DECODE>(a, tile, h, base, sm); break;
-    case 4:
-      if constexpr (!UNI && DK == 128 && DV == 128)
-        step4_mfma_tile(a, tile, h, base, *reinterpret_cast<SmemMx*>(&sm));
-      else
-        quant_tile<DK, DV, 4, UNI, OP_DECODE>(a, tile, h, base, sm);
-      break;
+    case 4: quant_tile<DK, DV, 4, UNI, OP_DECODE>(a, tile, h, base, sm); break;
     case 6: quant_tile<DK, DV, 6, UNI, OP_DECODE>(a, tile, h, base, sm); break;
     case 8: quant_tile<DK, DV, 8, UNI, OP_DECODE>(a, tile, h, base, sm); break;
     case 16:
@@ -1013,8 +590,6 @@ __device__ __forceinline__ void class0_tile(const TileArgs& a, int bi, int j, Sm
   }
   unsigned char* base = a.pool + (long long)slot * a.P.slot_bytes + wuni(a.P.head_off[h]);
   if constexpr (BITS == 16) pivot_tile<DK, DV, OP_DECODE>(a, tile, h, base, sm);
-  else if constexpr (BITS == 4 && !UNI && DK == 128 && DV == 128)
-    step4_mfma_tile(a, tile, h, base, *reinterpret_cast<SmemMx*>(&sm));
   else quant_tile<DK, DV, BITS, UNI, OP_DECODE>(a, tile, h, base, sm);
 }
 
@@ -1026,8 +601,7 @@ __device__ __forceinline__ void class0_tile(const TileArgs& a, int bi, int j, Sm
 template <int DK, int DV, bool UNI>
 __global__ __launch_bounds__((DK / 32) * (DV / 2))
 __attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_decode_kernel(TileArgs a) {
-  __shared__ __align__(16) unsigned char smraw[smem_bytes<DK, DV>()];
-  SmemGdn<DK, DV>& sm = *reinterpret_cast<SmemGdn<DK, DV>*>(smraw);
+  __shared__ SmemGdn<DK, DV> sm;
   merged_tile<DK, DV, UNI>(a, blockIdx.x, sm);
 }
 
@@ -1038,8 +612,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_decode_kernel(TileArgs a) {
 template <int DK, int DV, int BITS>
 __global__ __launch_bounds__((DK / 32) * (DV / 2))
 __attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_split_kernel(TileArgs a) {
-  __shared__ __align__(16) unsigned char smraw[smem_bytes<DK, DV>()];
-  SmemGdn<DK, DV>& sm = *reinterpret_cast<SmemGdn<DK, DV>*>(smraw);
+  __shared__ SmemGdn<DK, DV> sm;
   const int y = blockIdx.y;
   if (y < a.pre_rows) {
     const int t = a.cls_end[0] + y * (int)gridDim.x + (int)blockIdx.x;
@@ -1054,8 +627,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_split_kernel(TileArgs a) {
 template <int DK, int DV, int BITS, bool UNI>
 __global__ __launch_bounds__((DK / 32) * (DV / 2))
 __attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_class_kernel(TileArgs a) {
-  __shared__ __align__(16) unsigned char smraw[smem_bytes<DK, DV>()];
-  SmemGdn<DK, DV>& sm = *reinterpret_cast<SmemGdn<DK, DV>*>(smraw);
+  __shared__ SmemGdn<DK, DV> sm;
   // grid (heads of the class, batch rows): the same order as tile
   // bi * n + j, without a division
   class0_tile<DK, DV, BITS, UNI>(a, blockIdx.y, blockIdx.x, sm);
