@@ -77,6 +77,23 @@ def measured_traffic(workload: str, family: str):
     return int(fields["traffic_bytes_per_step"])
 
 
+def measured_valu(workload: str, family: str):
+    """VALU instructions per decode step from the committed rocprofv3
+    SQ_INSTS_VALU summary of this workload, if the decode kernel sources are
+    still the ones the counter was taken on (else None)."""
+    path = os.path.join(ROOT, "profiles", f"valu_issue_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("valu_instructions_per_step", "kernel_source_sha256_16"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash(family):
+        return None
+    return int(fields["valu_instructions_per_step"])
+
+
 def kernel_source_hash(family: str) -> str:
     """First 16 hex digits of the sha256 of the decode sources of a kernel
     family (its kernel file, the shared tile header, the internal header and
@@ -272,6 +289,14 @@ def main():
                      "launch": "one decode call (sq_decode_step with all its kernel launches, or "
                                "sq_dense_step in dense mode), HIP events on the launch stream"},
     }
+    valu = measured_valu(w.name, family)
+    if valu is not None:
+        # the issue rate the decode launch sustains: 64 lanes per VALU
+        # instruction over the launch, against the chip's non-packed lane rate
+        lane_ops = 64.0 * valu / (launch_ms * 1e-3)
+        out["roofline"]["alu_issue"] = {"achieved": lane_ops / 1e12, "peak": VALU_PEAK / 1e12,
+                                        "unit": "T lane-ops/s", "frac": lane_ops / VALU_PEAK,
+                                        "valu_instructions_per_launch": valu}
     if not args.no_cpu and desc is not None:
         torch.cuda.synchronize()
         sb = desc["slot_bytes"]
