@@ -345,3 +345,45 @@ def test_full_size_fp32_dense_pool_sampled():
         assert np.linalg.norm(got - ref[0]) <= 1e-5 * np.linalg.norm(ref[0]), (b, h)
         assert np.linalg.norm(yh[b, h] - yr[0]) <= 1e-5 * np.linalg.norm(yr[0]), (b, h)
     assert np.array_equal(S[idle].cpu().numpy(), idle_before)
+
+
+def _calibrated_plan(name):
+    """The plan the bench builds for a workload: sq_calibrate_bits on the
+    calibration statistics stored for it (written by the oracle)."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", f"calib_{name}.json")) as f:
+        st = json.load(f)
+    stats = {"kind": 0 if st["kind"] == "gdn" else 1, "heads": st["heads"], "d_k": st["d_k"],
+             "d_v": st["d_v"], "cand_bits": st["cand_bits"], "ell": np.array(st["ell"]),
+             "dist": np.array(st["dist"]), "omega": np.array(st["omega"])}
+    return sq.sq_calibrate_bits(stats, {"nominal_bits": st["nominal_bits"],
+                                        "pivot_frac": st["pivot_frac"], "gamma": st["gamma"],
+                                        "horizon": st["horizon"]})
+
+
+def test_full_size_gdn_mid_all_tiles():
+    """The mid workload at full size (64 slots x 16 heads, the calibrated
+    nominal-6-bit plan: 4-, 6- and 8-bit heads and one FP16 head) in the launch
+    configuration the bench times (every width class in one merged launch):
+    8 fp32 dense warm-up steps on the GPU, pack, 6 decode steps, and every one
+    of the 1,024 tiles compared teacher-forced on the first and the last."""
+    import torch
+    w = SI.workload("gdn_mid_step6", steps=6)
+    plan = _calibrated_plan("gdn_mid_step6")
+    pool = Pool(plan, w.n_slots)
+    assert sorted(set(int(b) for b in pool.desc["unit_bits"])) == [4, 6, 8, 16]
+    slots = SI.slot_ids(w)
+    sdev = to_dev(slots)
+    params = SI.gate_params(w)
+    S = torch.zeros((w.n_slots, w.heads, 128, 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((w.batch, w.heads, 128), dtype=torch.float32, device="cuda")
+    for t in range(8):
+        d = inputs_dev(SI.warmup_inputs(w, t, params))
+        sq.sq_dense_step(0, w.heads, 128, 128, S, w.n_slots, sdev, w.batch, d["q"], d["k"],
+                         d["v"], d["beta"], d["gate"], y)
+    S0 = S[sdev.long()].cpu().numpy().astype(np.float64)
+    del S
+    rep = _run_teacher_forced(pool, w, slots, S0, w.steps, compare_steps={0, w.steps - 1})
+    print("adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
+    rep.assert_ok()
