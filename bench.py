@@ -223,7 +223,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-compare", action="store_true",
-                    help="skip the fp32-dense and uniform-INT4 runs at the pool workload's shape")
+                    help="skip the same-hardware runs: fp32-dense and uniform-INT4 at the pool "
+                         "workload's shape, fp32-dense at the KDA and window shapes")
     ap.add_argument("--state-warmup", type=int, default=None,
                     help="fp32 steps that build the initial state (default: the workload's 128)")
     ap.add_argument("--prefill", type=int, default=0, metavar="T",
@@ -307,6 +308,8 @@ def main():
     del m
     if w.name == "gdn_pool_step4" and not args.no_compare:
         out["same_hardware"] = same_hardware(sq, args, out["value"])
+    elif w.name in DENSE_TWIN and not args.no_compare:
+        out["same_hardware"] = dense_twin(sq, args, out["value"], DENSE_TWIN[w.name])
     print(json.dumps(out))
 
 
@@ -479,6 +482,27 @@ def same_hardware(sq, args, value: float) -> dict:
     res["speedup_step6_b512_vs_fp32_dense"] = (res["step6_b512"]["steps_per_s"]
                                               / res["fp32_dense_b512"]["steps_per_s"])
     return res
+
+
+# the fp32-dense workload of the same shape, inputs and gates as a packed one
+DENSE_TWIN = {"kda_step6": "kda_fp32", "gdn_window16": "gdn_window_fp32",
+              "gdn_window16_r4": "gdn_window_fp32"}
+
+
+def dense_twin(sq, args, value: float, name: str) -> dict:
+    """The workload's shape (batch, slots, heads, d, inputs, gates, timing
+    protocol) with the fp32 state kept dense: the denominator of the packed
+    step's speed-up on this GPU."""
+    import torch
+    from synth import inputs as SI
+    w = SI.workload(name)
+    m = measure(sq, w, args)
+    dense = {"workload": name, "steps_per_s": 1e3 / m["ms_per_step"], "ms_per_step": m["ms_per_step"],
+             "launch_ms": m["launch_ms"], "algorithmic_bytes_per_step": m["abytes"],
+             "achieved_gbs": m["abytes"] / (m["launch_ms"] * 1e-3) / 1e9, "kernel": KERNEL["dense"]}
+    del m
+    torch.cuda.empty_cache()
+    return {"fp32_dense": dense, "speedup_vs_fp32_dense": value / dense["steps_per_s"]}
 
 
 if __name__ == "__main__":

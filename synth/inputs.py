@@ -112,6 +112,16 @@ WORKLOADS: Dict[str, Workload] = {
     "gdn_b512_fp32": Workload(
         name="gdn_b512_fp32", kind="gdn", mode="dense", batch=512, n_slots=512, heads=16,
         d_k=128, d_v=128, steps=256, seed=1, half_life_range=(1.0, 4096.0)),
+    # the KDA workload's shape, inputs and gates with the fp32 state kept dense:
+    # the same-hardware denominator of the packed KDA step
+    "kda_fp32": Workload(
+        name="kda_fp32", kind="kda", mode="dense", batch=256, n_slots=256, heads=32,
+        d_k=128, d_v=128, steps=512, seed=2, half_life_range=(1.0, 8192.0),
+        key_gain_sigma=0.9, value_gain_sigma=1.1),
+    # the window workloads' shape and inputs with the fp32 state kept dense
+    "gdn_window_fp32": Workload(
+        name="gdn_window_fp32", kind="gdn", mode="dense", batch=256, n_slots=256, heads=32,
+        d_k=128, d_v=128, steps=1024, seed=4, half_life=64.0),
     # per-window variant: INT8 boundary + FP32 records, p = 16
     "gdn_window16": Workload(
         name="gdn_window16", kind="gdn", mode="window", batch=256, n_slots=256, heads=32,
