@@ -387,3 +387,41 @@ def test_full_size_gdn_mid_all_tiles():
     rep = _run_teacher_forced(pool, w, slots, S0, w.steps, compare_steps={0, w.steps - 1})
     print("adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
     rep.assert_ok()
+
+
+def test_full_size_fp32_dense_kda_sampled():
+    """The fp32 dense KDA step (the KDA workload's same-hardware baseline) at
+    the KDA shape, 256 slots x 32 heads with per-row gates: 8 warm-up steps,
+    then one step checked on sampled tiles against the float64 recurrence
+    started from the GPU's state."""
+    import torch
+    rng = np.random.default_rng(36)
+    w = SI.workload("kda_fp32")
+    slots = SI.slot_ids(w)
+    H = w.heads
+    S = torch.zeros((w.n_slots, H, 128, 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((w.batch, H, 128), dtype=torch.float32, device="cuda")
+    sdev = to_dev(slots)
+    params = SI.gate_params(w)
+    for t in range(8):
+        d = inputs_dev(SI.warmup_inputs(w, t, params))
+        sq.sq_dense_step(1, H, 128, 128, S, w.n_slots, sdev, w.batch, d["q"], d["k"], d["v"],
+                         d["beta"], d["gate"], y)
+    sample = [(int(b), int(h)) for b, h in zip(rng.choice(w.batch, 24), rng.choice(H, 24))]
+    sample += [(0, 0), (w.batch - 1, H - 1)]
+    torch.cuda.synchronize()
+    before = {(b, h): S[int(slots[b]), h].cpu().numpy().astype(np.float64) for b, h in sample}
+    inp = SI.step_inputs(w, 0, params)
+    d = inputs_dev(inp)
+    sq.sq_dense_step(1, H, 128, 128, S, w.n_slots, sdev, w.batch, d["q"], d["k"], d["v"],
+                     d["beta"], d["gate"], y)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    for b, h in sample:
+        x = {k: inp[k][b, h].astype(np.float64) for k in ("q", "k", "v")}
+        dvec = R.gate_vector(inp["gate"][b, h].astype(np.float64), "kda", 128)
+        ref, yr = R.dense_step(before[(b, h)][None], x["q"][None], x["k"][None], x["v"][None],
+                               np.array([inp["beta"][b, h]], np.float64), dvec[None])
+        got = S[int(slots[b]), h].cpu().numpy()
+        assert np.linalg.norm(got - ref[0]) <= 1e-5 * np.linalg.norm(ref[0]), (b, h)
+        assert np.linalg.norm(yh[b, h] - yr[0]) <= 1e-5 * np.linalg.norm(yr[0]), (b, h)
