@@ -10,14 +10,37 @@ float64 and walks the quantizer one decision at a time:
   the two binary16 neighbours and the GPU chose the other neighbour.  The
   initial column scale c0 is not stored; where it is such a near-tie the
   oracle keeps whichever neighbour reproduces the GPU's codes of the column.
-  An FP16 pivot value is formed from two terms, D S_hat and beta k e^T, and
-  e_j = v_j - sum_i k_i (D S_hat)_ij is itself a float32 dot product; its tie
-  window also covers 4 fp32 ulps of the magnitudes of all those terms (where
-  they cancel, fp32 cannot decide the rounding that float64 decides).
+  An FP16 pivot value X_ij = (D S_hat)_ij + beta k_i e_j is formed in fp32
+  from e_j = v_j - sum_l k_l (D S_hat)_lj, a d_k-term fp32 sum; a GPU value
+  is also accepted if it is the binary16 rounding of a value within the fp32
+  error bound of that evaluation (below): where the terms cancel, fp32
+  cannot decide the rounding that float64 decides, and the interval can
+  span more than one binary16 step.
+* float32 window scales C, B and codes after a rebuild: the rebuilt state
+  S_p = Gamma S_hat_0 + sum_j Gamma k~_j u_j^T, minus the new compensator
+  pairs, is a sum of at most 1 + p + 2r fp32 terms per element; where those
+  terms cancel (a rank-r fit removes most of a column), its fp32 error is
+  large against the residual that is quantized, so C, B and the codes also
+  accept a GPU value within the error bound that follows from it (below).
 * integer codes: identical, except |dz| = 1 where the oracle's pre-rounding
   value is within 1e-3 code units of a half-integer (an exact tie up to fp32
   arithmetic);
-* float32 window scales C, B: within 1e-6 relative, then adopted;
+* float32 window scales C, B: within 1e-6 relative (or the rebuild's error
+  bound), then adopted;
+
+Error bounds (u = 2^-24; a sum of n fp32 terms in any order is within
+(n - 1) u of the sum of the terms' magnitudes, Higham's gamma_{n-1}; each
+product and the final rounding add u; everything is doubled for the second
+order terms):
+
+* pivot value: |X_gpu - X| <= 2u (|X| + |D S_hat| + |beta k_i| (3 |e_j| +
+  (d_k + 2) A_j)), A_j = sum_l |k_l (D S_hat)_lj|;
+* rebuilt residual: |R_gpu - R| <= 2u (2p + 2r + 6) M with M the same sum
+  over the magnitudes of every term (1 + p + 2r terms; each carries a decay
+  product Gamma of up to p fp32 factors and two more roundings); then C_a = sqrt(mean_j |R_aj|) moves by
+  at most mean_j dR_aj / (2 C_a) + u C_a, T = R / C by dR / C + |T| dC / C,
+  B_j = max_a |T_aj| by max_a dT_aj + u B_j, and the pre-rounding code
+  127 T / B by 127 (dT + |T| dB / B) / B.
 * readouts: ||y_gpu - y||_2 / ||y||_2 <= 1e-5 per (slot, head); the window
   record u_i = v_i - S_{i-1}^T (alpha_i k_i) is a readout too and is judged
   the same way; the record key beta_i k_i is exact (one fp32 product).
@@ -79,31 +102,50 @@ def _signed_neighbours(x):
 
 
 def adopt_fp16(pre, ora, gpu, clamp=True, abs_tol=0.0):
-    """(values to continue with, number adopted, failure mask).  abs_tol widens
-    the tie window to the fp32 evaluation error of the value's terms."""
+    """(values to continue with, number adopted, failure mask).
+
+    Scales (clamp): a GPU value that differs must be the other binary16
+    neighbour of an unrounded value within 1e-5 relative of their midpoint.
+    Pivot values (no clamp) with an fp32 error bound abs_tol: a GPU value that
+    differs must be the binary16 rounding of some value within abs_tol of the
+    oracle's, i.e. lie between the roundings of pre - abs_tol and pre + abs_tol
+    (where terms cancel that interval can span several binary16 steps)."""
     pre = np.asarray(pre, dtype=np.float64)
+    diff = gpu != ora
     if clamp:
         lo, hi = N.fp16_neighbours(pre)
         ref = np.clip(pre, N.FP16_MIN_NORMAL, N.FP16_MAX)
+        mid = 0.5 * (lo + hi)
+        near = np.abs(ref - mid) <= SCALE_REL * np.abs(ref)
+        ok = ~diff | (near & ((gpu == lo) | (gpu == hi)))
     else:
         lo, hi = _signed_neighbours(pre)
-        ref = pre
-    mid = 0.5 * (lo + hi)
-    near = np.abs(ref - mid) <= np.maximum(SCALE_REL * np.abs(ref), abs_tol)
-    diff = gpu != ora
-    ok = ~diff | (near & ((gpu == lo) | (gpu == hi)))
+        mid = 0.5 * (lo + hi)
+        near = np.abs(pre - mid) <= SCALE_REL * np.abs(pre)
+        ok = ~diff | (near & ((gpu == lo) | (gpu == hi)))
+        tol = np.broadcast_to(np.asarray(abs_tol, dtype=np.float64), pre.shape)
+        if np.any(tol > 0):
+            with np.errstate(over="ignore"):
+                within = (gpu >= N.fp16(pre - tol)) & (gpu <= N.fp16(pre + tol))
+            ok = ok | within
     return np.where(diff & ok, gpu, ora), int((diff & ok).sum()), ~ok
 
 
-def adopt_codes(pre, ora, gpu):
+def adopt_codes(pre, ora, gpu, tie=None):
+    """tie: per-element half-integer window in code units (default 1e-3)."""
     d = gpu - ora
     frac = np.abs(np.abs(pre - np.floor(pre)) - 0.5)
-    ok = (d == 0) | ((np.abs(d) == 1) & (frac <= CODE_TIE))
+    win = CODE_TIE if tie is None else np.maximum(CODE_TIE, tie)
+    ok = (d == 0) | ((np.abs(d) == 1) & (frac <= win))
     return np.where(ok, gpu, ora), int(((d != 0) & ok).sum()), ~ok
 
 
-def adopt_f32(ora, gpu):
-    ok = np.abs(gpu - ora) <= F32_REL * np.maximum(np.abs(ora), 1e-30)
+def adopt_f32(ora, gpu, tol=None):
+    """tol: per-element absolute error bound that widens the 1e-6 window."""
+    win = F32_REL * np.maximum(np.abs(ora), 1e-30)
+    if tol is not None:
+        win = np.maximum(win, tol)
+    ok = np.abs(gpu - ora) <= win
     return np.where(ok, gpu, ora), int(((gpu != ora) & ok).sum()), ~ok
 
 
@@ -116,10 +158,11 @@ class Report:
     def add(self, key, n):
         self.count[key] += n
 
-    def bad(self, where, what, mask):
+    def bad(self, where, what, mask, detail=None):
         n = int(np.sum(mask))
         if n:
-            self.fail.append(f"{where}: {what} ({n} mismatches)")
+            extra = "" if detail is None else f"; {detail(mask)}"
+            self.fail.append(f"{where}: {what} ({n} mismatches{extra})")
 
     def y(self, where, y_gpu, y_ref):
         rel = float(np.linalg.norm(y_gpu - y_ref) / max(np.linalg.norm(y_ref), 1e-300))
@@ -143,16 +186,15 @@ def check_uniform(where, X, bits, gpu, rep: Report):
     rep.bad(where, "codes", bad)
 
 
-def check_step(where, X, w, row_bits, gpu, rep: Report, mag=None):
-    """mag: elementwise size of the terms X is formed from (|D S_hat|,
-    |beta k e^T| and |beta k_i| times the terms of e_j); a pivot value within
-    4 fp32 ulps of those terms of an FP16 rounding midpoint is an exact tie up
-    to fp32 arithmetic."""
+def check_step(where, X, w, row_bits, gpu, rep: Report, err=None):
+    """err: elementwise fp32 error bound of X (module docstring); a pivot value
+    within it of an FP16 rounding midpoint is an exact tie up to fp32
+    arithmetic."""
     row_bits = np.asarray(row_bits)
     piv = row_bits == N.PIVOT_BITS
     keep = ~piv
     if piv.any():
-        tol = 0.0 if mag is None else 2.0 ** -22 * mag[piv]
+        tol = 0.0 if err is None else err[piv]
         h, n, bad = adopt_fp16(X[piv], N.fp16(X[piv]), gpu["h"][piv], clamp=False, abs_tol=tol)
         rep.add("pivot_adopted", n)
         rep.bad(where, "FP16 pivot values", bad)
@@ -191,17 +233,33 @@ def check_step(where, X, w, row_bits, gpu, rep: Report, mag=None):
     rep.bad(where, "column scale c (D = 0)", gpu["c"][~pos] != c0[~pos])
 
 
-def check_window_quant(where, S, gpu, rep: Report, c_floor=Q.WINDOW_C_FLOOR):
+def check_window_quant(where, S, gpu, rep: Report, c_floor=Q.WINDOW_C_FLOOR, dR=None):
+    """dR: elementwise fp32 error bound of the rebuilt residual S (module
+    docstring), or None for an exactly known S (a pack)."""
+    u = 2.0 ** -24
     C = Q.window_row_smoothing(S, c_floor)
-    C, n, bad = adopt_f32(C, gpu["C"])
+    dC = None if dR is None else dR.mean(-1) / (2 * C) + 2 * u * C
+    C, n, bad = adopt_f32(C, gpu["C"], dC)
     rep.add("f32_adopted", n)
-    rep.bad(where, "smoothing C", bad)
+    rep.bad(where, "smoothing C", bad,
+            lambda m: f"max rel diff {np.max(np.abs(gpu['C'] - C)[m] / C[m]):.2e}")
     T, B = Q.window_col_scales(S, C)
-    B, n, bad = adopt_f32(B, gpu["B"])
+    dT = dB = None
+    if dR is not None:
+        dT = dR / C[:, None] + np.abs(T) * (dC / C)[:, None]
+        dB = dT.max(axis=0) + 2 * u * B
+    B_ora = B
+    B, n, bad = adopt_f32(B, gpu["B"], dB)
     rep.add("f32_adopted", n)
-    rep.bad(where, "column scale B", bad)
+    rep.bad(where, "column scale B", bad,
+            lambda m: f"max rel diff {np.max(np.abs(gpu['B'] - B_ora)[m] / B_ora[m]):.2e}"
+            + ("" if dB is None else f", bound {np.max(dB[m] / B_ora[m]):.2e}"))
     pre_z, Z = Q.window_codes(T, B)
-    Z, n, bad = adopt_codes(pre_z, Z, gpu["Z"])
+    tie = None
+    if dT is not None:
+        safe_B = np.where(B > 0, B, 1.0)
+        tie = Q.WINDOW_CODE_MAX * (dT + np.abs(T) * (dB / safe_B)[None, :]) / safe_B[None, :]
+    Z, n, bad = adopt_codes(pre_z, Z, gpu["Z"], tie)
     rep.add("tie_codes", n)
     rep.bad(where, "window codes", bad)
 
@@ -245,7 +303,15 @@ def check_decode_head(where, desc, h, before: bytes, after: bytes, inp: dict, y_
                           float(inp["gate"]), int(desc["p"]), iters, adopt=adopt)
         rep.y(where, y_gpu, r["o"])
         if r["flushed"] is not None:
-            check_window_quant(where, r["flushed"]["R"], st1, rep)
+            p = int(desc["p"])
+            new = r["state"]
+            M = W.window_dense(np.abs(r["S0"]), new["alpha"], np.abs(new["kt"]), np.abs(new["u"]),
+                               p, None if not rank else np.abs(st0["Kc"]),
+                               None if not rank else np.abs(st0["Uc"]))
+            if rank:
+                M = M + np.abs(r["flushed"]["Kc"]).T @ np.abs(r["flushed"]["Uc"])
+            dR = 2 * 2.0 ** -24 * (2 * p + 2 * rank + 6) * M
+            check_window_quant(where, r["flushed"]["R"], st1, rep, dR=dR)
             rep.bad(where, "l after flush", np.array([st1["ell"] != 0]))
         else:
             i = int(st0["ell"])
@@ -275,10 +341,13 @@ def check_decode_head(where, desc, h, before: bytes, after: bytes, inp: dict, y_
     if mode == "uniform":
         check_uniform(where, X, int(desc["bits"]), st1, rep)
     else:
-        # terms of X: D S_hat, beta k e^T, and those of the dot product e_j
-        e_terms = np.abs(inp["v"]) + np.abs(inp["k"]) @ np.abs(Sd)
-        mag = np.abs(Sd) + np.abs(X - Sd) + np.outer(np.abs(inp["beta"] * inp["k"]), e_terms)
-        check_step(where, X, w, row_bits_of(desc, h), st1, rep, mag=mag)
+        # fp32 error bound of X = D S_hat + beta k e^T with e_j a d_k-term sum
+        u = 2.0 ** -24
+        A = np.abs(inp["k"]) @ np.abs(Sd)
+        e = inp["v"] - Sd.T @ inp["k"]
+        err = 2 * u * (np.abs(X) + np.abs(Sd) + np.outer(np.abs(inp["beta"] * inp["k"]),
+                                                        3 * np.abs(e) + (d_k + 2) * A))
+        check_step(where, X, w, row_bits_of(desc, h), st1, rep, err=err)
 
 
 def check_window_encode(where, desc, S, gpu: dict, rep: Report, init=None):
