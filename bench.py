@@ -40,6 +40,7 @@ KERNEL = {"step": "gdn_split_kernel<128,128,b> (largest code-width class in its 
 TRAFFIC_SOURCES = {"gdn": ("tile_gdn.hip",), "kda": ("tile_kda.hip",), "window": ("tile_window.hip",),
                    "dense": ("dense.hip",)}
 HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "gdn_pool_step4"
 
 
 def _plan(sq, w):
@@ -126,88 +127,200 @@ def algorithmic_bytes(desc, w) -> int:
     return int(B * H * per_tile) + io
 
 
-def build_state(sq, w, pools, slots_dev, steps):
+def _state_key(w, steps):
+    """Workloads whose warm-up states are identical (same seed, shape, gates,
+    gains and batch) share one build."""
+    return (w.kind, w.seed, w.batch, w.heads, w.d_k, w.d_v, w.half_life, w.half_life_range,
+            w.key_gain_sigma, w.value_gain_sigma, steps)
+
+
+def magnitude_contrast(S) -> dict:
+    """Maximum-to-median RMS contrast of each state tile over key rows
+    (sqrt(mean_j S_ij^2)) and over value columns, median linearly
+    interpolated (STEPQuant Sec. 4.2 and appendix B); the median over tiles."""
+    import torch
+    r = S.pow(2).mean(-1).sqrt()
+    c = S.pow(2).mean(-2).sqrt()
+    rc = r.amax(-1) / torch.quantile(r, 0.5, dim=-1)
+    cc = c.amax(-1) / torch.quantile(c, 0.5, dim=-1)
+    return {"key_rows": float(torch.quantile(rc.flatten(), 0.5)),
+            "value_columns": float(torch.quantile(cc.flatten(), 0.5)),
+            "tiles": int(rc.numel())}
+
+
+def build_state(sq, w, pools, slots_dev, steps, cache=None):
     """Warm-up state: `steps` fp32 dense steps from S = 0 with the library's
-    dense kernel, then packed into every pool."""
+    dense kernel, then packed into every pool.  Returns the state's magnitude
+    contrast."""
     import torch
     from synth import inputs as SI
-    params = SI.gate_params(w)
-    S = torch.zeros((w.batch, w.heads, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
-    ident = torch.arange(w.batch, dtype=torch.int32, device="cuda")
-    y = torch.empty((w.batch, w.heads, w.d_v), dtype=torch.float32, device="cuda")
-    for t in range(steps):
-        inp = {k: torch.from_numpy(v).cuda() for k, v in SI.warmup_inputs(w, t, params).items()}
-        sq.sq_dense_step(0 if w.kind == "gdn" else 1, w.heads, w.d_k, w.d_v, S, w.batch, ident,
-                         w.batch, inp["q"], inp["k"], inp["v"], inp["beta"], inp["gate"], y)
+    key = _state_key(w, steps)
+    if cache is not None and key in cache:
+        S, contrast = cache[key]
+    else:
+        params = SI.gate_params(w)
+        S = torch.zeros((w.batch, w.heads, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+        ident = torch.arange(w.batch, dtype=torch.int32, device="cuda")
+        y = torch.empty((w.batch, w.heads, w.d_v), dtype=torch.float32, device="cuda")
+        for t in range(steps):
+            inp = {k: torch.from_numpy(v).cuda() for k, v in SI.warmup_inputs(w, t, params).items()}
+            sq.sq_dense_step(0 if w.kind == "gdn" else 1, w.heads, w.d_k, w.d_v, S, w.batch, ident,
+                             w.batch, inp["q"], inp["k"], inp["v"], inp["beta"], inp["gate"], y)
+        contrast = magnitude_contrast(S) if steps > 0 else None
+        if cache is not None:
+            cache[key] = (S, contrast)
     for pl in pools:
         if w.mode == "dense":
             pl["pool"].index_copy_(0, slots_dev.long(), S)
         else:
             sq.sq_pool_pack(pl["plan"], pl["dev_plan"], pl["pool"], w.n_slots, slots_dev, w.batch, S)
     torch.cuda.synchronize()
-    return S
+    return contrast
 
 
-def cpu_baseline(w, desc, pool_bytes: bytes, slots, budget_s: float) -> dict:
-    """The float64 oracle, as it stands, on a bounded sample of the same
-    workload: the first slots of the live batch (all heads), teacher-forced
-    from the GPU's packed state, decode steps repeated until the time budget
-    is spent.  Reported as equivalent full-batch steps/s."""
-    from oracle import layout as OL
+def _oracle_steps(w, od, states, sets, n_steps, deadline):
+    """Decode steps of the float64 oracle on parsed slot states (a list of
+    per-slot head lists), free-running from the packed state it was given;
+    step t reads input set t % len(sets), whose batch rows are the states'
+    slots in order (inputs are made before the clock starts, as the GPU's
+    are resident).  Returns the number of (slot, head) tiles done before the
+    deadline."""
     from oracle import quantizers as Q
     from oracle import recurrence as R
     from oracle import window as OW
-    from synth import inputs as SI
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from parity import oracle_desc, row_bits_of
-    od = oracle_desc(desc)
-    nb = 1
-    sb = desc["slot_bytes"]
-    states = []
-    for b in range(nb):
-        s = int(slots[b])
-        states.append(OL.parse_slot(od, pool_bytes[b * sb:(b + 1) * sb]))
-    params = SI.gate_params(w)
+    from parity import row_bits_of
     tiles = 0
-    t0 = time.perf_counter()
-    step = 0
-    while time.perf_counter() - t0 < budget_s:
-        inp = SI.step_inputs(w, step, params)
-        for b in range(nb):
+    for step in range(n_steps):
+        inp = sets[step % len(sets)]
+        for b, sl in enumerate(states):
             for h in range(w.heads):
-                st = states[b][h]
-                q, k, v = (inp[x][b, h].astype(np.float64) for x in ("q", "k", "v"))
+                if time.perf_counter() > deadline:
+                    return tiles
+                st = sl[h]
+                q, k, v = (inp[x][b, h] for x in ("q", "k", "v"))
                 beta = float(inp["beta"][b, h])
                 if w.mode == "window":
                     r = OW.window_step(st, q, k, v, beta, float(inp["gate"][b, h]), w.window,
                                        w.power_iters)
-                    states[b][h] = r["state"]
+                    sl[h] = r["state"]
                     tiles += 1
                     continue
-                dvec = R.gate_vector(inp["gate"][b, h].astype(np.float64),
-                                     "gdn" if w.mode == "uniform" else w.kind, w.d_k)
+                dvec = R.gate_vector(inp["gate"][b, h], "gdn" if w.mode == "uniform" else w.kind,
+                                     w.d_k)
                 if w.mode == "uniform":
                     S_hat = Q.dequant_uniform(st["z"], st["s"])
                     X = R.delta_update(R.retained(S_hat, dvec), k, v, beta)
                     R.readout(X, q)
                     e = Q.quantize_uniform(X, w.bits)
-                    states[b][h] = {"z": e["z"], "s": e["s"]}
+                    sl[h] = {"z": e["z"], "s": e["s"]}
                 else:
                     rb = row_bits_of(od, h)
                     S_hat = Q.dequant_step(st["z"], st["r"], st["c"], rb, st["h"])
                     X = R.delta_update(R.retained(S_hat, dvec), k, v, beta)
                     R.readout(X, q)
-                    e = Q.quantize_step(X, desc["w"][h].astype(np.float64), rb)
-                    states[b][h] = {"z": e["z"], "r": e["r"], "c": e["c"], "h": e["h"]}
+                    e = Q.quantize_step(X, od["w"][h], rb)
+                    sl[h] = {"z": e["z"], "r": e["r"], "c": e["c"], "h": e["h"]}
                 tiles += 1
-        step += 1
+    return tiles
+
+
+def _rows(sets, idx):
+    """The given batch rows of each input set, widened to float64."""
+    return [{k: np.asarray(v[idx], dtype=np.float64) for k, v in st.items()} for st in sets]
+
+
+def _cpu_worker(job):
+    """One process of the multi-core oracle run: parse its slots from the
+    shared host copy of the pool, then run the sampled decode steps."""
+    from oracle import layout as OL
+    from synth import inputs as SI
+    w = SI.workload(job["workload"])
+    od = job["od"]
+    buf = np.load(job["path"], mmap_mode="r")
+    sb = job["slot_bytes"]
+    states = [OL.parse_slot(od, bytes(buf[i * sb:(i + 1) * sb])) for i in job["slots"]]
+    t0 = time.perf_counter()
+    tiles = _oracle_steps(w, od, states, job["sets"], job["steps"], t0 + job["budget_s"])
+    return tiles, time.perf_counter() - t0
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, desc, host: np.ndarray, sample_slots: int, steps: int, budget_s: float,
+                 single_s: float) -> dict:
+    """The float64 oracle, as it stands, on a bounded sample of the same
+    workload, free-running from the GPU's packed state: `steps` decode steps
+    of the first `sample_slots` live slots (all heads) over every host core
+    available to this process (a process pool, one BLAS thread per worker),
+    then one slot on one core.  Step t reads the GPU loop's input set t % 8,
+    made before the clock starts.  Reported as equivalent full-batch steps/s."""
+    import multiprocessing as mp
+    import tempfile
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import layout as OL
+    from parity import oracle_desc
+    od = oracle_desc(desc)
+    if desc.get("w") is not None:
+        od["w"] = desc["w"].astype(np.float64)
+    sb = desc["slot_bytes"]
+    affinity = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, affinity))
+    full = w.batch * w.heads
+    res = {"unit": "steps/s", "kind": "oracle", "cpu_model": _cpu_model(),
+           "affinity_cpus": affinity}
+    from synth import inputs as SI
+    params = SI.gate_params(w)
+    sets = [SI.step_inputs(w, i, params) for i in range(8)]   # the GPU loop's 8 input sets
+    # single core: one slot, all heads, until the budget is spent
+    states = [OL.parse_slot(od, host[:sb].tobytes())]
+    t0 = time.perf_counter()
+    tiles = _oracle_steps(w, od, states, _rows(sets, [0]), 1 << 30, t0 + single_s)
     dt = time.perf_counter() - t0
-    tiles_per_s = tiles / dt
-    return {"value": tiles_per_s / (w.batch * w.heads), "unit": "steps/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{nb} slot x {w.heads} heads, {step} steps ({tiles} tiles) in "
-                      f"{dt:.1f} s, float64 numpy, one process; value = tiles/s / "
-                      f"({w.batch} x {w.heads}) tiles per step"}
+    single = {"value": tiles / dt / full, "cores": 1, "tiles": tiles, "seconds": dt,
+              "sample": f"1 slot x {w.heads} heads, {tiles} tiles in {dt:.1f} s, one process"}
+    # every core: sample_slots slots x all heads x `steps` steps, split by slot
+    n = min(sample_slots, host.size // sb)
+    with tempfile.TemporaryDirectory(dir="/tmp") as tmp:
+        path = os.path.join(tmp, "slots.npy")
+        np.save(path, host[:n * sb])
+        jobs = [{"workload": w.name, "od": od, "path": path, "slot_bytes": sb,
+                 "slots": list(range(k, n, workers)), "sets": _rows(sets[:max(1, steps)], list(range(k, n, workers))),
+                 "steps": steps, "budget_s": budget_s} for k in range(workers)]
+        env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                              "MKL_NUM_THREADS")}
+        for k in env:
+            os.environ[k] = "1"
+        try:
+            ctx = mp.get_context("forkserver")
+            t0 = time.perf_counter()
+            with ctx.Pool(workers) as pool:
+                out = pool.map(_cpu_worker, jobs)
+            dt = time.perf_counter() - t0
+        finally:
+            for k, v in env.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+    tiles = sum(o[0] for o in out)
+    busy = max(o[1] for o in out)
+    res.update({"value": tiles / busy / full, "cores": workers, "tiles": tiles,
+                "seconds": busy, "wall_seconds_with_startup": dt,
+                "sample": f"{n} slots x {w.heads} heads x {steps} steps ({tiles} tiles done) "
+                          f"over {workers} worker processes (one BLAS thread each) in "
+                          f"{busy:.1f} s, float64 numpy; value = tiles/s / ({w.batch} x "
+                          f"{w.heads}) tiles per step",
+                "single_core": single})
+    return res
 
 
 def main():
@@ -215,13 +328,22 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="gdn_pool_step4")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--runs", type=int, default=3,
+                    help="timed runs of K steps each; the median is reported")
+    ap.add_argument("--spin-ms", type=float, default=500.0,
+                    help="after the W warm-up steps, keep launching untimed steps until this "
+                         "much wall time has passed (clocks at steady state before timing)")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of replaying them as a HIP graph")
     ap.add_argument("--input-sets", type=int, default=8)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=25.0,
+                    help="time budget of the multi-core oracle run")
+    ap.add_argument("--cpu-single-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads' block (mid, KDA, window, tiny)")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the same-hardware runs: fp32-dense and uniform-INT4 at the pool "
                          "workload's shape, fp32-dense at the KDA and window shapes")
@@ -249,7 +371,8 @@ def main():
     if args.prefill:
         print(json.dumps(measure_prefill(sq, w, args)))
         return
-    m = measure(sq, w, args)
+    cache = {}
+    m = measure(sq, w, args, cache=cache)
     abytes, ms_per_step, launch_ms, desc = m["abytes"], m["ms_per_step"], m["launch_ms"], m["desc"]
     family = "window" if w.mode == "window" else ("dense" if w.mode == "dense" else w.kind)
     gbs_step = abytes / (ms_per_step * 1e-3) / 1e9
@@ -280,6 +403,7 @@ def main():
                    "input_sets": args.input_sets, "algorithmic_bytes_per_step": abytes,
                    "timed_loop": ("eager launches" if args.eager else
                                   "one HIP graph replay of the K steps (captured after warm-up)"),
+                   "timing": m["timing"],
                    "state_gbs": gbs_step, "pct_of_hbm_peak": 100.0 * gbs_step / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": gbs_kernel, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": gbs_kernel / HBM_PEAK_GBS,
@@ -287,9 +411,13 @@ def main():
                      "kernel": KERNEL[w.mode if w.kind == "gdn" else "kda"],
                      "kernel_source_sha256_16": kernel_source_hash(family),
                      "launch_ms": launch_ms, "bytes_per_launch": abytes,
-                     "launch": "one decode call (sq_decode_step with all its kernel launches, or "
-                               "sq_dense_step in dense mode), HIP events on the launch stream"},
+                     "launch": "one decode call = one kernel launch (sq_decode_step, or "
+                               "sq_dense_step in dense mode); duration = HIP events on the launch "
+                               "stream around the K-launch graph replay, divided by K (median of "
+                               "the timed runs)"},
     }
+    if m["contrast"] is not None and w.kind == "kda":
+        out["config"]["state_contrast"] = m["contrast"]
     valu = measured_valu(w.name, family)
     if valu is not None:
         # the issue rate the decode launch sustains: 64 lanes per VALU
@@ -298,28 +426,41 @@ def main():
         out["roofline"]["alu_issue"] = {"achieved": lane_ops / 1e12, "peak": VALU_PEAK / 1e12,
                                         "unit": "T lane-ops/s", "frac": lane_ops / VALU_PEAK,
                                         "valu_instructions_per_launch": valu}
+    host = None
     if not args.no_cpu and desc is not None:
         torch.cuda.synchronize()
         sb = desc["slot_bytes"]
         pb = m["pools"][0]["pool"]
-        s0 = int(m["slots"][0])
-        host = pb[s0 * sb:(s0 + 1) * sb].cpu().numpy().tobytes()
-        out["cpu_baseline"] = cpu_baseline(w, desc, host, m["slots"], args.cpu_seconds)
+        # the live slots in batch order, as host bytes
+        idx = torch.from_numpy(m["slots"].astype(np.int64)).cuda()
+        host = pb[:w.n_slots * sb].view(w.n_slots, sb).index_select(0, idx).cpu().numpy().reshape(-1)
     del m
-    if w.name == "gdn_pool_step4" and not args.no_compare:
-        out["same_hardware"] = same_hardware(sq, args, out["value"])
+    torch.cuda.empty_cache()
+    if w.name == DEFAULT_WORKLOAD and not args.no_configs:
+        out["configs"] = configs_block(sq, args, cache)
+    if w.name == DEFAULT_WORKLOAD and not args.no_compare:
+        out["same_hardware"] = same_hardware(sq, args, out["value"], cache)
     elif w.name in DENSE_TWIN and not args.no_compare:
-        out["same_hardware"] = dense_twin(sq, args, out["value"], DENSE_TWIN[w.name])
+        out["same_hardware"] = dense_twin(sq, args, out["value"], DENSE_TWIN[w.name], cache)
+    cache.clear()
+    torch.cuda.empty_cache()
+    if host is not None:
+        out["cpu_baseline"] = cpu_baseline(w, desc, host, w.batch, 2, args.cpu_seconds,
+                                           args.cpu_single_seconds)
     print(json.dumps(out))
 
 
-def measure(sq, w, args) -> dict:
-    """Time args.steps consecutive decode steps of workload w (after
-    args.warmup untimed ones), rotating args.layers independent pools so that
-    the live state exceeds the on-package cache, then time 64 single calls
-    with HIP events on the launch stream."""
+def measure(sq, w, args, steps=None, cache=None) -> dict:
+    """Time K consecutive decode steps of workload w, K = `steps` (default
+    args.steps), rotating args.layers independent pools so that the live state
+    exceeds the on-package cache.  Protocol: args.warmup untimed steps, untimed
+    steps until args.spin_ms of wall time has passed, then args.runs timed
+    runs of exactly K steps, each between device synchronisations and timed
+    with HIP events on the launch stream; the median run is reported.  A
+    second pass times 64 single calls for the per-launch duration."""
     import torch
     from synth import inputs as SI
+    K = args.steps if steps is None else steps
     dense = w.mode == "dense"
     plan = None if dense else _plan(sq, w)
     desc = None if dense else sq.sq_plan_query(plan)
@@ -335,8 +476,9 @@ def measure(sq, w, args) -> dict:
         pool = torch.empty(sq.sq_pool_bytes(plan, w.n_slots), dtype=torch.uint8, device="cuda")
         sq.sq_pool_init(plan, dp, pool, w.n_slots)
         pools.append({"plan": plan, "dev_plan": dp, "pool": pool})
-    build_state(sq, w, pools, slots_dev,
-                w.warmup_steps if args.state_warmup is None else args.state_warmup)
+    contrast = build_state(sq, w, pools, slots_dev,
+                           w.warmup_steps if args.state_warmup is None else args.state_warmup,
+                           cache)
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -373,28 +515,44 @@ def measure(sq, w, args) -> dict:
     graph = None
     if not args.eager:
         # the K timed steps captured once as a HIP graph (the same launches,
-        # arguments and in-place pool updates); one untimed replay first
+        # arguments and in-place pool updates)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             cap = torch.cuda.current_stream()
-            for i in range(args.steps):
+            for i in range(K):
                 step(args.warmup + i, cap)
-        graph.replay()
+
+    def run():
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(K):
+                step(args.warmup + i)
+
+    # untimed runs until the clocks have settled
+    t0 = time.perf_counter()
+    spins = 0
+    while True:
+        run()
         torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(args.steps):
-            step(args.warmup + i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
+        spins += 1
+        if time.perf_counter() - t0 >= args.spin_ms * 1e-3:
+            break
+    runs = []
+    for _ in range(max(1, args.runs)):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        run()
+        end.record(stream)
+        torch.cuda.synchronize()
+        runs.append(start.elapsed_time(end) / K)
+    ms_per_step = float(np.median(runs))
+    graph_ok = graph is not None
     del graph
 
     # per-launch durations with events on the launch stream (second pass)
-    n_ev = min(args.steps, 64)
+    n_ev = min(K, 64)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_ev)]
     for i, (a, b) in enumerate(evs):
@@ -402,9 +560,17 @@ def measure(sq, w, args) -> dict:
         step(i)
         b.record(stream)
     torch.cuda.synchronize()
-    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    eager_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    # every decode step here is one kernel launch, so in the graph replay the
+    # launch duration is the timed region over K (back-to-back launches, no
+    # host gaps); eager launches each carry the host's launch gap
+    launch_ms = eager_ms if graph_ok is False else ms_per_step
+    timing = {"K": K, "runs_ms_per_step": runs, "median_ms_per_step": ms_per_step,
+              "spin_runs": spins, "spin_s": time.perf_counter() - t0,
+              "eager_launch_ms": eager_ms}
     return {"desc": desc, "pools": pools, "slots": slots, "ms_per_step": ms_per_step,
-            "launch_ms": launch_ms, "abytes": algorithmic_bytes(desc, w)}
+            "launch_ms": launch_ms, "abytes": algorithmic_bytes(desc, w), "timing": timing,
+            "contrast": contrast}
 
 
 VALU_PEAK = 256 * 4 * 16 * 2.4e9   # non-packed fp32 lane-ops/s: CUs x SIMDs x lanes x clock
@@ -457,23 +623,78 @@ def measure_prefill(sq, w, args) -> dict:
                          "ops_per_launch": ops}}
 
 
-def same_hardware(sq, args, value: float) -> dict:
+def _summary(w, m, kernel) -> dict:
+    """steps/s (median run), GB/s per step and per launch, % of the HBM peak."""
+    gbs = m["abytes"] / (m["ms_per_step"] * 1e-3) / 1e9
+    out = {"workload": w.name, "batch": w.batch, "heads": w.heads, "d_k": w.d_k, "d_v": w.d_v,
+           "mode": w.mode, "steps_per_s": 1e3 / m["ms_per_step"], "ms_per_step": m["ms_per_step"],
+           "launch_ms": m["launch_ms"], "algorithmic_bytes_per_step": m["abytes"],
+           "state_gbs": gbs, "pct_of_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+           "launch_gbs": m["abytes"] / (m["launch_ms"] * 1e-3) / 1e9,
+           "timing": m["timing"], "kernel": kernel}
+    if m["desc"] is not None and m["desc"]["unit_bits"] is not None:
+        out["unit_bits_histogram"] = {str(b): int(c) for b, c in
+                                      zip(*np.unique(m["desc"]["unit_bits"], return_counts=True))}
+    if w.mode == "window":
+        out["window"] = w.window
+        out["comp_rank"] = w.comp_rank
+    if m["contrast"] is not None and w.kind == "kda":
+        out["state_contrast"] = m["contrast"]
+    return out
+
+
+# the other workloads reported beside the headline, with the K each one times
+# (a multiple of layers x window for the window path, so that every timed run
+# holds exactly one rebuild per layer pool)
+CONFIGS = (("tiny_gdn_int8", 256, 1), ("gdn_mid_step6", 256, None), ("kda_step6", 64, None),
+           ("gdn_window16", 64, None), ("gdn_window16_r4", 64, None))
+
+
+def configs_block(sq, args, cache) -> dict:
+    """The tiny uniform INT8 case, the mid GDN plan, KDA and the per-window
+    path (without and with compensator tokens), each by the same protocol."""
+    import argparse as _ap
+    import torch
+    from synth import inputs as SI
+    res = {}
+    for name, K, layers in CONFIGS:
+        w = SI.workload(name)
+        a = _ap.Namespace(**vars(args))
+        if layers is not None:
+            a.layers = layers
+        K = max(K, args.steps) if w.mode != "window" else K * max(1, -(-args.steps // K))
+        m = measure(sq, w, a, steps=K, cache=cache)
+        kern = KERNEL["window"] if w.mode == "window" else KERNEL[
+            w.mode if w.kind == "gdn" else "kda"]
+        res[name] = _summary(w, m, kern)
+        if name == "tiny_gdn_int8":
+            res[name]["note"] = "one 64 x 64 tile per step: launch-latency bound, steps/s only"
+        del m
+        torch.cuda.empty_cache()
+    return res
+
+
+def same_hardware(sq, args, value: float, cache=None) -> dict:
     """The pool workload's shape (same batch, slots, heads, d, inputs and
     timing protocol) with the fp32 state kept dense, and with uniform rowwise
     INT4: the denominators of the packed path's speed-up on this GPU.  Then
     the 6-bit plan of the mid workload at batch 512 against the fp32 state of
-    that shape (the setting of the pages' 6-bit, batch-512 comparison)."""
+    that shape (the setting of the pages' 6-bit, batch-512 comparison), and the
+    fp32 state at the KDA and window shapes."""
     import torch
     from synth import inputs as SI
     res = {}
     for key, name in (("fp32_dense", "gdn_pool_fp32"), ("uniform_int4", "gdn_pool_int4"),
-                      ("step6_b512", "gdn_b512_step6"), ("fp32_dense_b512", "gdn_b512_fp32")):
+                      ("step6_b512", "gdn_b512_step6"), ("fp32_dense_b512", "gdn_b512_fp32"),
+                      ("fp32_dense_kda", "kda_fp32"), ("fp32_dense_window", "gdn_window_fp32")):
         w = SI.workload(name)
-        m = measure(sq, w, args)
+        m = measure(sq, w, args, cache=cache)
         res[key] = {"workload": name, "steps_per_s": 1e3 / m["ms_per_step"],
                     "ms_per_step": m["ms_per_step"], "launch_ms": m["launch_ms"],
                     "algorithmic_bytes_per_step": m["abytes"],
                     "achieved_gbs": m["abytes"] / (m["launch_ms"] * 1e-3) / 1e9,
+                    "pct_of_hbm_peak": 100.0 * m["abytes"] / (m["launch_ms"] * 1e-3) / 1e9
+                    / HBM_PEAK_GBS,
                     "kernel": KERNEL[w.mode]}
         del m
         torch.cuda.empty_cache()
@@ -489,14 +710,14 @@ DENSE_TWIN = {"kda_step6": "kda_fp32", "gdn_window16": "gdn_window_fp32",
               "gdn_window16_r4": "gdn_window_fp32"}
 
 
-def dense_twin(sq, args, value: float, name: str) -> dict:
+def dense_twin(sq, args, value: float, name: str, cache=None) -> dict:
     """The workload's shape (batch, slots, heads, d, inputs, gates, timing
     protocol) with the fp32 state kept dense: the denominator of the packed
     step's speed-up on this GPU."""
     import torch
     from synth import inputs as SI
     w = SI.workload(name)
-    m = measure(sq, w, args)
+    m = measure(sq, w, args, cache=cache)
     dense = {"workload": name, "steps_per_s": 1e3 / m["ms_per_step"], "ms_per_step": m["ms_per_step"],
              "launch_ms": m["launch_ms"], "algorithmic_bytes_per_step": m["abytes"],
              "achieved_gbs": m["abytes"] / (m["launch_ms"] * 1e-3) / 1e9, "kernel": KERNEL["dense"]}
