@@ -189,6 +189,21 @@ sq_status sq_calib_distortion(const sq_plan* plan, const void* dev_plan, int32_t
                               const float* S, void* packed, int32_t per_row, double* dist_sum,
                               hipStream_t stream);
 
+/* sq_calib_distortion for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops, harnesses that forbid hipMalloc):
+ * the packed heads go to a device array inside the library instead of a
+ * caller buffer.  The array holds 16 MiB on each GPU the library runs on,
+ * from the first call on that GPU until the process ends; calls needing more
+ * than that (n H sq_max_head_bytes > 16 MiB) fail with SQ_EINVAL before
+ * launching anything.  The call allocates nothing.  Every call on one GPU
+ * shares that GPU's array, so calls that overlap on one GPU (on different
+ * streams, or from several threads without ordering) race; calls ordered on
+ * one stream do not.  Arguments, results and the other errors as
+ * sq_calib_distortion. */
+sq_status sq_calib_distortion_noalloc(const sq_plan* plan, const void* dev_plan, int32_t n,
+                                      const float* S, int32_t per_row, double* dist_sum,
+                                      hipStream_t stream);
+
 /* ---------------------------------------------------------------- plans */
 
 /* Lifetime-aware bit allocation with sparse FP16 pivots ([SQ] Sec. 4, Eq. 8;

@@ -29,7 +29,7 @@ EXPORTED = (
     "sq_plan_upload", "sq_pool_bytes", "sq_pool_init", "sq_pool_pack", "sq_pool_unpack",
     "sq_decode_step", "sq_window_flush", "sq_quantize_tiles", "sq_max_head_bytes",
     "sq_dense_step", "sq_prefill_chunk", "sq_calib_gate_stats", "sq_impact_factors", "sq_calib_distortion",
-    "sq_last_error",
+    "sq_calib_distortion_noalloc", "sq_last_error",
 )
 
 
@@ -110,6 +110,7 @@ def lib() -> ctypes.CDLL:
             "sq_calib_gate_stats": [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P],
             "sq_impact_factors": [_I32, _I32, _P, ctypes.c_double, ctypes.c_double, _P],
             "sq_calib_distortion": [_P, _P, _I32, _P, _P, _I32, _P, _P],
+            "sq_calib_distortion_noalloc": [_P, _P, _I32, _P, _I32, _P, _P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -335,6 +336,13 @@ def sq_calib_distortion(plan, dev_plan, n, S, packed, per_row, dist_sum, stream=
     _check(lib().sq_calib_distortion(plan, _ptr(dev_plan), n, _ptr(S, _f32()), _ptr(packed),
                                      1 if per_row else 0, _ptr(dist_sum, torch.float64),
                                      _stream(stream)))
+
+
+def sq_calib_distortion_noalloc(plan, dev_plan, n, S, per_row, dist_sum, stream=None) -> None:
+    import torch
+    _check(lib().sq_calib_distortion_noalloc(plan, _ptr(dev_plan), n, _ptr(S, _f32()),
+                                             1 if per_row else 0, _ptr(dist_sum, torch.float64),
+                                             _stream(stream)))
 
 
 def device_plan(plan: Plan, device="cuda", stream=None):

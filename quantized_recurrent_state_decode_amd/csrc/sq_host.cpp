@@ -7,11 +7,18 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <numeric>
 #include <vector>
 
 #include "sq_internal.h"
+
+// Device scratch of sq_calib_distortion_noalloc: the packed heads of one
+// call.  Each GPU the library runs on holds its own copy until the process
+// ends; every call on that GPU reuses it.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -687,6 +694,50 @@ extern "C" sq_status sq_calib_distortion(const sq_plan* P, const void* dev_plan,
     e = launch_calib_dist(a.P, a.n_tiles, a.out, a.out_stride, S, per_row ? 1 : 0, dist_sum, st);
   if (e != hipSuccess) return hip_fail(e, "launching calibration distortion");
   return ok();
+}
+
+namespace {
+
+// Device address of `scratch` on the current GPU, looked up once per device
+// with that device current (the array's host-side name is not a device
+// address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+sq_status scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "querying the current device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SQ_EINVAL, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail(e, "looking up the device scratch address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+
+}  // namespace
+
+extern "C" sq_status sq_calib_distortion_noalloc(const sq_plan* P, const void* dev_plan,
+                                                 int32_t n, const float* S, int32_t per_row,
+                                                 double* dist_sum, hipStream_t st) {
+  if (!P || !dev_plan || !S || !dist_sum || n < 0)
+    return fail(SQ_EINVAL, "bad arguments to sq_calib_distortion_noalloc");
+  const size_t need = (size_t)n * (size_t)P->H * (size_t)P->max_head_bytes;
+  if (need > kNoAllocScratchBytes)
+    return fail(SQ_EINVAL,
+                "sq_calib_distortion_noalloc needs n H max_head_bytes = %zu bytes of scratch; "
+                "the limit is %zu (call it with fewer sequences)", need, kNoAllocScratchBytes);
+  if (n == 0) return ok();
+  void* ptr = nullptr;
+  sq_status s = scratch_ptr(&ptr);
+  if (s) return s;
+  return sq_calib_distortion(P, dev_plan, n, S, ptr, per_row, dist_sum, st);
 }
 
 extern "C" sq_status sq_prefill_chunk(int32_t kind, int32_t H, int32_t dk, int32_t dv,
