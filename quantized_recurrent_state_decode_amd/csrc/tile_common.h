@@ -254,12 +254,18 @@ __device__ __forceinline__ int piece_off(int rb, int p, int q) {
   return ((rb * (BITS / 2) + q) * NP + p) * 16;
 }
 
+// The packed state is streamed: each chunk is read once and written once per
+// step, so loads and stores are nontemporal (the caches keep the inputs and
+// tables instead; measured faster on every packed workload).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <int BITS, int NP>
 __device__ __forceinline__ void load_chunk(const unsigned char* region, int rb, int p,
                                            uint32_t (&w)[2 * BITS]) {
 #pragma unroll
   for (int q = 0; q < BITS / 2; ++q) {
-    const uint4 v = *reinterpret_cast<const uint4*>(region + piece_off<BITS, NP>(rb, p, q));
+    const u32x4 v =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(region + piece_off<BITS, NP>(rb, p, q)));
     w[4 * q + 0] = v.x;
     w[4 * q + 1] = v.y;
     w[4 * q + 2] = v.z;
@@ -271,9 +277,10 @@ template <int BITS, int NP>
 __device__ __forceinline__ void store_chunk(unsigned char* region, int rb, int p,
                                             const uint32_t (&w)[2 * BITS]) {
 #pragma unroll
-  for (int q = 0; q < BITS / 2; ++q)
-    *reinterpret_cast<uint4*>(region + piece_off<BITS, NP>(rb, p, q)) =
-        make_uint4(w[4 * q + 0], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+  for (int q = 0; q < BITS / 2; ++q) {
+    const u32x4 v = {w[4 * q + 0], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(region + piece_off<BITS, NP>(rb, p, q)));
+  }
 }
 
 // Lane geometry of a d_k x d_v tile: lane (rb, p) owns rows 32 rb .. 32 rb + 31
@@ -321,6 +328,31 @@ __device__ __forceinline__ uint32_t lds_ld32(int a) { return *(const lds_u32*)(u
 __device__ __forceinline__ float4 lds_ld4(int a) {
   const f32x4 v = *(const lds_f32x4*)(uintptr_t)a;
   return make_float4(v.x, v.y, v.z, v.w);
+}
+// Row transposes of 16 rows: lane p writes its partial of row m at
+// [m][p] and then reads 16 consecutive partials of one row with four 16-byte
+// reads.  A row stride of NP + 4 floats keeps the rows 16-byte aligned and
+// both the writes (consecutive lanes, consecutive words) and the reads (the
+// 16 lanes of a read group start 4 banks apart) free of bank conflicts.
+template <int NP>
+struct RowT {
+  static constexpr int S = NP + 4;
+};
+// combine of the 16 floats at f (16-byte aligned LDS): sum or max
+template <bool MAX>
+__device__ __forceinline__ float lds_fold16(const float* f) {
+  const f32x4* v = reinterpret_cast<const f32x4*>(f);
+  const f32x4 a = v[0], b = v[1], c = v[2], d = v[3];
+  if constexpr (MAX) {
+    const float m0 = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
+    const float m1 = fmaxf(fmaxf(b.x, b.y), fmaxf(b.z, b.w));
+    const float m2 = fmaxf(fmaxf(c.x, c.y), fmaxf(c.z, c.w));
+    const float m3 = fmaxf(fmaxf(d.x, d.y), fmaxf(d.z, d.w));
+    return fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+  } else {
+    return (((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w))) +
+           (((c.x + c.y) + (c.z + c.w)) + ((d.x + d.y) + (d.z + d.w)));
+  }
 }
 __device__ __forceinline__ void lds_st8(int a, uint32_t v) { *(lds_u8*)(uintptr_t)a = (unsigned char)v; }
 __device__ __forceinline__ void lds_st16(int a, uint32_t v) { *(lds_u16*)(uintptr_t)a = (unsigned short)v; }

@@ -34,7 +34,7 @@ struct SmemGdn {
   float2 colB[DK / 32][DV / 2];
   float2 colM[DK / 32][DV / 2];
   float4 colC[DK / 32][DV / 2];
-  float rowt[DK / 32][16][DV / 2 + 1];        // row partials of 16 rows, transposed
+  alignas(16) float rowt[DK / 32][16][RowT<DV / 2>::S];  // row partials of 16 rows, transposed
 };
 
 
@@ -284,12 +284,7 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
     }
     wave_sync();
     const int mm = p & 15, part = p >> 4;
-    float s = sm.rowt[rb][mm][part * 16];
-#pragma unroll
-    for (int pp = 1; pp < 16; ++pp) {
-      const float vv = sm.rowt[rb][mm][part * 16 + pp];
-      s = UNI ? fmaxf(s, vv) : s + vv;
-    }
+    float s = lds_fold16<UNI>(&sm.rowt[rb][mm][part * 16]);
     {  // combine the parts 16 (and 32) lanes apart
       float a0, b0;
       swap16(s, a0, b0);

@@ -64,7 +64,7 @@ extern __shared__ uint4 kda_dyn[];
 
 template <int DK, int DV>
 __host__ __device__ constexpr int dyn_bytes(int max_code_bytes) {
-  constexpr int transpose = (DK / 32) * 16 * (DV / 2 + 1) * 4;
+  constexpr int transpose = (DK / 32) * 16 * RowT<DV / 2>::S * 4;
   return ((max_code_bytes > transpose ? max_code_bytes : transpose) + 15) / 16 * 16 + 16;
 }
 
@@ -236,7 +236,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   constexpr bool WU = NP % 64 == 0;  // a wave's lanes share their rows
   __shared__ SmemKda<DK, DV> sm;
   unsigned char* codes = reinterpret_cast<unsigned char*>(kda_dyn);
-  float(*rowt)[16][NP + 1] = reinterpret_cast<float(*)[16][NP + 1]>(kda_dyn);
+  float(*rowt)[16][RowT<NP>::S] = reinterpret_cast<float(*)[16][RowT<NP>::S]>(kda_dyn);
   const int tile = blockIdx.x;
   const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p, r0 = 32 * rb;
   const long long tk = (long long)tile * DK, tv = (long long)tile * DV;
@@ -333,14 +333,13 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
     constexpr int CH = 4;
     const int nch = code_bytes >> 4;
     const int spare = dyn_bytes<DK, DV>(a.P.max_code_bytes) / 16 - 1;
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const u32x4* src = reinterpret_cast<const u32x4*>(base);
     u32x4* dst = reinterpret_cast<u32x4*>(codes);
     u32x4 v[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {  // first round, issued before the scale loads
       const int e = t + i * NT;
-      v[i] = src[e < nch ? e : 0];
+      v[i] = __builtin_nontemporal_load(src + (e < nch ? e : 0));
     }
     const float c0 = __half2float(c_ptr[j0]), c1 = __half2float(c_ptr[j0 + 1]);
     float rs = 0.f;
@@ -355,7 +354,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const int e = c + t + i * NT;
-        w[i] = src[e < nch ? e : 0];
+        w[i] = __builtin_nontemporal_load(src + (e < nch ? e : 0));
       }
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
@@ -493,9 +492,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
       rowt[rb][m][p] = fabsf(x[2 * (16 * hf + m)]) + fabsf(x[2 * (16 * hf + m) + 1]);
     wave_sync();
     const int mm = p & 15, part = p >> 4;
-    float s = rowt[rb][mm][part * 16];
-#pragma unroll
-    for (int pp = 1; pp < 16; ++pp) s += rowt[rb][mm][part * 16 + pp];
+    float s = lds_fold16<false>(&rowt[rb][mm][part * 16]);
     s = parts_sum<NP>(s);
     sh[hf] = s;
     wave_sync();
@@ -588,7 +585,8 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   sm.colC[rb][p] = make_float4(N0, N1, D0, D1);
   __syncthreads();
   for (int i = t * 16; i < code_bytes; i += NT * 16)
-    *reinterpret_cast<uint4*>(base + i) = *reinterpret_cast<const uint4*>(codes + i);
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(codes + i),
+                                reinterpret_cast<u32x4*>(base + i));
   if (rb == 0) {
     float n0 = 0.f, n1 = 0.f, dd0 = 0.f, dd1 = 0.f;
 #pragma unroll

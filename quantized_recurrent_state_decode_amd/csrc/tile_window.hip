@@ -62,7 +62,7 @@ struct SmemWin {
       float K[PM][DK];
       float U[PM][DV];
     } rec;                                   // records held, staged from the head
-    float rowt[DK / 32][16][DV / 2 + 1];     // re-encode row transpose (after the rebuild)
+    alignas(16) float rowt[DK / 32][16][RowT<DV / 2>::S];  // row transposes (after the staging)
   } u;
 };
 
@@ -105,7 +105,7 @@ struct Staged {
   static constexpr int NK = (PM * DK / 4 + NT - 1) / NT;  // float4 of K rows per thread
   static constexpr int NU = (PM * DV / 4 + NT - 1) / NT;  // float4 of U rows per thread
   static constexpr int NC = RMX > 0 ? (RMX * (DK + DV) / 2 + NT - 1) / NT : 1;  // half2 of pairs
-  float4 k[NK], u[NU];
+  f32x4 k[NK], u[NU];
   uint32_t c[NC];
   float al;
 
@@ -117,12 +117,12 @@ struct Staged {
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       const int e = t + i * NT;
-      k[i] = reinterpret_cast<const float4*>(wp.K)[e < n * DK / 4 ? e : 0];
+      k[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(wp.K) + (e < n * DK / 4 ? e : 0));
     }
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
       const int e = t + i * NT;
-      u[i] = reinterpret_cast<const float4*>(wp.U)[e < n * DV / 4 ? e : 0];
+      u[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(wp.U) + (e < n * DV / 4 ? e : 0));
     }
     if (RMX > 0) {
 #pragma unroll
@@ -142,9 +142,9 @@ struct Staged {
     static_assert(NK * NT == PM * DK / 4 && NU * NT == PM * DV / 4, "staging slots");
     const int t = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < NK; ++i) reinterpret_cast<float4*>(&sm.u.rec.K[0][0])[t + i * NT] = k[i];
+    for (int i = 0; i < NK; ++i) reinterpret_cast<f32x4*>(&sm.u.rec.K[0][0])[t + i * NT] = k[i];
 #pragma unroll
-    for (int i = 0; i < NU; ++i) reinterpret_cast<float4*>(&sm.u.rec.U[0][0])[t + i * NT] = u[i];
+    for (int i = 0; i < NU; ++i) reinterpret_cast<f32x4*>(&sm.u.rec.U[0][0])[t + i * NT] = u[i];
     if (RMX > 0) {
       // pair values 2e, 2e+1 of the head's [Kc (R d_k) | Uc (R d_v)] run
 #pragma unroll
@@ -195,9 +195,7 @@ __device__ __forceinline__ void fit_compensators(float (&x)[64], const WinPtrs& 
         }
         wave_sync();
         const int mm = p & 15, part = p >> 4;
-        float sv = sm.u.rowt[rb][mm][part * 16];
-#pragma unroll
-        for (int pp = 1; pp < 16; ++pp) sv += sm.u.rowt[rb][mm][part * 16 + pp];
+        float sv = lds_fold16<false>(&sm.u.rowt[rb][mm][part * 16]);
         sh[hf] = parts_sum<NP>(sv);
         wave_sync();
       }
@@ -296,9 +294,7 @@ __device__ __forceinline__ void encode_boundary(float (&x)[64], const WinPtrs& w
       sm.u.rowt[rb][m][p] = fabsf(x[2 * (16 * hf + m)]) + fabsf(x[2 * (16 * hf + m) + 1]);
     wave_sync();
     const int mm = p & 15, part = p >> 4;
-    float s = 0.f;
-#pragma unroll
-    for (int pp = 0; pp < 16; ++pp) s += sm.u.rowt[rb][mm][part * 16 + pp];
+    float s = lds_fold16<false>(&sm.u.rowt[rb][mm][part * 16]);
     s = parts_sum<NP>(s);
     if (part == 0) {
       const int a = r0 + 16 * hf + mm;
