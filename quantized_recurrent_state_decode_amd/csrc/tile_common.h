@@ -96,7 +96,8 @@ __device__ __forceinline__ void unpack_offset(const uint32_t (&w)[2 * BITS], flo
 #pragma unroll
     for (int d = 0; d < 8; ++d) {              // dword d: rows 4d..4d+3, both columns
       const uint32_t f = w[d] ^ 0x88888888u;
-      const uint32_t lo = f & 0x0f0f0f0fu, hi = (f >> 4) & 0x0f0f0f0fu;
+      // (the high nibbles shifted first: one shift and one three-input op)
+      const uint32_t lo = f & 0x0f0f0f0fu, hi = ((w[d] >> 4) ^ 0x08080808u) & 0x0f0f0f0fu;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         x[8 * d + 2 * k] = ubyte(lo, k);

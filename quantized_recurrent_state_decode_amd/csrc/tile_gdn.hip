@@ -252,15 +252,20 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
     const float2 vv = *reinterpret_cast<const float2*>(a.v + tv + j0);
     const float e0 = vv.x - c0 * d0, e1 = vv.y - c1 * d1;
     // pass 2: Xt = c_j (u - off) + gamma_i e_j, readout partials
-    const float o0 = -OFF * c0, o1 = -OFF * c1, cs0 = c0 * HS, cs1 = c1 * HS;
+    const float o0 = -OFF * c0, o1 = -OFF * c1;
+    // the column scales enter the update as fp32 registers: the empty asm
+    // keeps the compiler from folding their binary16-to-fp32 conversion into
+    // mixed-precision FMAs, which issue more slowly than plain ones
+    float cs0v = c0 * HS, cs1v = c1 * HS;
+    asm volatile("" : "+v"(cs0v), "+v"(cs1v));
 #pragma unroll
     for (int m = 0; m < 32; m += 4) {
       const float4 g4 = lds_ld4(rcb + 4 * (1 * DK + m)), t4 = lds_ld4(rcb + 4 * (2 * DK + m));
       const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, tv4[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float v0 = fmaf(cs0, code(2 * (m + u)), fmaf(gv[u], e0, o0));
-        const float v1 = fmaf(cs1, code(2 * (m + u) + 1), fmaf(gv[u], e1, o1));
+        const float v0 = fmaf(cs0v, code(2 * (m + u)), fmaf(gv[u], e0, o0));
+        const float v1 = fmaf(cs1v, code(2 * (m + u) + 1), fmaf(gv[u], e1, o1));
         x[2 * (m + u)] = v0;
         x[2 * (m + u) + 1] = v1;
         y0 = fmaf(tv4[u], v0, y0);
