@@ -9,11 +9,13 @@ the cumulative decay Gamma_{a:b} = alpha_b ... alpha_a (identity when a > b):
 
 For GDN the write vector is k~ = beta k and the read vector is alpha k (the
 notes' Table 4), so the corrected value of token i is
-u_i = v_i - S_{i-1}^T (alpha_i k_i); the token's output is o_i = S_i^T q_i
-(Sec. 2.1 Eq. 1).  The per-token loop of Sec. 2.6 computes u_i, appends the
-record, emits o_i and rebuilds the dense state when the window holds p
-records; the rebuilt state is re-encoded with the smoothed INT8 quantizer
-(Sec. 2.5, appendix B.3) and the window restarts.
+u_i = v_i - S_{i-1}^T (alpha_i k_i) and the token's output is o_i = S_i^T q_i
+(Sec. 2.1 Eq. 1).  The oracle forms the window's dense state from the
+expansion and reads u_i and o_i from it; once p records are held the dense
+state is re-encoded with the smoothed INT8 quantizer (Sec. 2.5, appendix
+B.3) as the next boundary.  The expansion's read form (Eq. 10,
+window_readout) is what the kernel evaluates; a pin checks it against the
+dense form.
 
 Compensator tokens (Sec. 2.4, Eqs. 5-7 and 10), rank r > 0: the boundary is
 S_hat_0 = C dequant(R_hat) + K~c U~c^T with r FP16 factor pairs (k~c_h, u~c_h).
@@ -175,50 +177,55 @@ def window_dense(S0: np.ndarray, alphas, kt, u, n: int, Kc=None, Uc=None) -> np.
     return S
 
 
+def close_window(st: dict, iters: int = 4, exact: bool = False, adopt=None):
+    """Rebuild and re-encode: the window's records are folded into its dense
+    state S_l (Eq. 7, window_state_dense), which becomes the next boundary
+    (compensator fit from the current pairs u~c, then the smoothed INT8
+    encoding of the residual, Sec. 2.4-2.5); the window restarts empty.
+    Returns (new state, the encoding with its residual "R")."""
+    Kc = st.get("Kc")
+    rank = 0 if Kc is None else len(Kc)
+    enc = encode_boundary(window_state_dense(st), rank, iters, st.get("Uc"), exact, adopt)
+    new = dict(st, ell=0)
+    new.update({kk: vv for kk, vv in enc.items() if kk != "R"})
+    return new, enc
+
+
 def window_step(st: dict, q, k, v, beta: float, alpha: float, p: int, iters: int = 4,
                 exact: bool = False, adopt=None) -> dict:
-    """One token on one (slot, head) window state.  Returns the output o_i,
-    the record written and the new state (a fresh dict).  The compensator
-    rank is that of st["Kc"] (absent or empty: none).  `exact` keeps records
-    and factors unrounded and the boundary unquantized."""
+    """One token on one (slot, head) window state.
+
+    The window holds l records and its dense state is S_l (Eq. 7).  Token
+    i = l + 1 follows the gated delta rule (Sec. 2.1, Eq. 1) with the GDN
+    read vector alpha_i k_i and write vector beta_i k_i (Table 4):
+      u_i = v_i - S_l^T (alpha_i k_i)           the corrected value,
+      S_i = alpha_i S_l + (beta_i k_i) u_i^T    one more record in Eq. 4,
+      o_i = S_i^T q_i                           the token's output,
+    and the record (alpha_i, beta_i k_i, u_i) is kept (float32 unless
+    `exact`).  When the window holds p records it is closed (close_window).
+    The compensator rank is that of st["Kc"] (absent or empty: none).
+    Returns the output, the record and the new state (a fresh dict)."""
     ell = int(st["ell"])
     i = ell + 1
-    S0 = boundary_residual(st)
-    Kc, Uc = st.get("Kc"), st.get("Uc")
-    rank = 0 if Kc is None else len(Kc)
     rnd = (lambda x: np.asarray(x, dtype=np.float64)) if exact else fp32
-    alphas = st["alpha"].copy()
-    kt = st["kt"].copy()
-    u = st["u"].copy()
-    alphas[i - 1] = alpha
-    prev = window_readout(S0, alphas, kt, u, i - 1, alpha * k, Kc, Uc)
-    u_i = rnd(v - prev)
-    kt[i - 1] = rnd(beta * k)
-    u[i - 1] = u_i
-    o = window_readout(S0, alphas, kt, u, i, q, Kc, Uc)
+    u_i = rnd(v - window_state_dense(st).T @ (alpha * k))
+    kt_i = rnd(beta * k)
+    alphas, kt, u = st["alpha"].copy(), st["kt"].copy(), st["u"].copy()
+    alphas[i - 1], kt[i - 1], u[i - 1] = alpha, kt_i, u_i
     new = dict(st, alpha=alphas, kt=kt, u=u, ell=i)
+    o = window_state_dense(new).T @ q
     flushed = None
     if i == p:
-        flushed = encode_boundary(window_dense(S0, alphas, kt, u, p, Kc, Uc), rank, iters,
-                                  Uc, exact, adopt)
-        new.update({kk: vv for kk, vv in flushed.items() if kk not in ("R",)})
-        new["ell"] = 0
-    return {"o": o, "u": u_i, "kt": kt[i - 1], "state": new, "flushed": flushed,
-            "S0": S0}
+        new, flushed = close_window(new, iters, exact, adopt)
+    return {"o": o, "u": u_i, "kt": kt_i, "state": new, "flushed": flushed,
+            "S0": boundary_residual(st)}
 
 
 def window_flush(st: dict, p: int, iters: int = 4, exact: bool = False, adopt=None) -> dict:
-    """Rebuild and re-encode a window holding 0 < l < p records (no-op at l = 0)."""
-    ell = int(st["ell"])
-    if ell == 0:
+    """Close a window holding 0 < l < p records early (no-op at l = 0)."""
+    if int(st["ell"]) == 0:
         return dict(st)
-    Kc, Uc = st.get("Kc"), st.get("Uc")
-    rank = 0 if Kc is None else len(Kc)
-    enc = encode_boundary(window_dense(boundary_residual(st), st["alpha"], st["kt"], st["u"],
-                                       ell, Kc, Uc), rank, iters, Uc, exact, adopt)
-    new = dict(st, ell=0)
-    new.update({kk: vv for kk, vv in enc.items() if kk != "R"})
-    return new
+    return close_window(st, iters, exact, adopt)[0]
 
 
 def window_state_dense(st: dict) -> np.ndarray:

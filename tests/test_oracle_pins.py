@@ -511,6 +511,34 @@ def test_compensated_window_exact_with_identity_quantizer(rng):
     assert st["ell"] == 0
 
 
+@pytest.mark.parametrize("rank", [0, 2])
+def test_window_flush_keeps_the_state_and_restarts(rng, rank):
+    """LeapQuant notes Sec. 2.6: closing a window early folds its records into
+    the boundary.  With an identity quantizer the dense state is unchanged
+    (Eq. 7 before, boundary plus pairs after) and the window is empty; at
+    l = 0 the flush is a no-op; the next tokens still follow the step
+    recurrence."""
+    d_k, d_v, p = 9, 6, 8
+    S = rng.standard_normal((d_k, d_v))
+    st = W.new_window_state(S, p, rank, 3, exact=True)
+    assert W.window_flush(st, p, 3, exact=True)["ell"] == 0
+    for t in range(3):
+        inp, dvec = draw(rng, d_k, d_v, "gdn")
+        st = W.window_step(st, inp["q"], inp["k"], inp["v"], inp["beta"], dvec[0], p, 3,
+                           exact=True)["state"]
+        S, _ = R.dense_step(S, inp["q"], inp["k"], inp["v"], inp["beta"], dvec)
+    assert st["ell"] == 3
+    fl = W.window_flush(st, p, 3, exact=True)
+    assert fl["ell"] == 0
+    np.testing.assert_allclose(W.window_state_dense(fl), S, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(W.boundary_residual(fl) + (fl["Kc"].T @ fl["Uc"] if rank else 0.0),
+                               S, rtol=0, atol=1e-12)
+    inp, dvec = draw(rng, d_k, d_v, "gdn")
+    res = W.window_step(fl, inp["q"], inp["k"], inp["v"], inp["beta"], dvec[0], p, 3, exact=True)
+    S, y = R.dense_step(S, inp["q"], inp["k"], inp["v"], inp["beta"], dvec)
+    np.testing.assert_allclose(res["o"], y, rtol=0, atol=1e-11)
+
+
 def test_compensated_readout_matches_dense(rng):
     """Eq. 10 term by term: boundary residual, compensators decaying with the
     boundary, records with their own decay, equals (S_l)^T x of Eq. 7."""
