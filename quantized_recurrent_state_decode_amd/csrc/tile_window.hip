@@ -46,7 +46,6 @@ struct SmemWin {
   float x1[DK], qv[DK], ktn[DK];  // alpha_i k_i, q_i, beta_i k_i (float32)
   float cx1[DK], cq[DK];          // C_a x1_a, C_a q_a
   float rowf[DK];                 // rebuild row factor, then 1 / C_a
-  float csum[DK / 32][2];         // per row block: sum_a C_a x1_a, sum_a C_a q_a
   float al[PM + 1];               // record decays (+ a spare word)
   float g1[PM + 1], g2[PM + 1];   // suffix products of the decays
   float2 dots[DK / 32][PM + RMX];  // per row block: kt_j . x1, kt_j . q; then kc_h . x1, kc_h . q
@@ -94,6 +93,16 @@ __device__ __forceinline__ __half half_sat(float v) {
   return __float2half_rn(fminf(fmaxf(v, -kFp16Max), kFp16Max));
 }
 
+
+// The 64 INT8 boundary codes of a lane chunk (two's-complement bytes, value
+// n = 2m + c) as floats: one sign-extending byte conversion each.
+__device__ __forceinline__ void unpack_signed8(const uint32_t (&w)[16], float (&x)[64]) {
+#pragma unroll
+  for (int d = 0; d < 16; ++d) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[4 * d + k] = (float)(int)(signed char)(w[d] >> (8 * k));
+  }
+}
 
 // The records and compensator pairs held by a head, staged through
 // registers: `issue` starts every load (a fixed number per thread,
@@ -244,12 +253,14 @@ __device__ __forceinline__ void fit_compensators(float (&x)[64], const WinPtrs& 
     const float s2 = wave_sum(rb == 0 ? fmaf(b0, b0, b1 * b1) : 0.f);
     if (t == 0) sm.red[0][NRB] = s2;
     __syncthreads();
-    const float sigma = sqrtf(sm.red[0][NRB]);
+    // hardware square roots (1 ulp): they only scale the pair before its FP16
+    // rounding
+    const float sigma = __builtin_amdgcn_sqrtf(sm.red[0][NRB]);
     const bool zero = !(inv > 0.f) || !(sigma > 0.f);
-    const float sq = zero ? 0.f : sqrtf(sigma);
+    const float sq = zero ? 0.f : __builtin_amdgcn_sqrtf(sigma);
     const float isq = zero ? 0.f : frcp(sq);
-    const float u0 = __half2float(half_sat(b0 * isq));
-    const float u1 = __half2float(half_sat(b1 * isq));
+    float u0 = __half2float(half_sat(b0 * isq));
+    float u1 = __half2float(half_sat(b1 * isq));
     if (p < 32) {
       const int i = r0 + p;
       const __half kh = half_sat(zero ? 0.f : sq * (sm.va[i] * inv));
@@ -261,7 +272,10 @@ __device__ __forceinline__ void fit_compensators(float (&x)[64], const WinPtrs& 
       wp.Uc[h * DV + j0 + 1] = __float2half_rn(u1);
     }
     wave_sync();
-    // take the stored pair out of the state
+    // take the stored pair out of the state (the pair as fp32 registers: the
+    // compiler would otherwise fold the FP16 value into mixed-precision FMAs,
+    // which issue more slowly)
+    asm volatile("" : "+v"(u0), "+v"(u1));
 #pragma unroll
     for (int m = 0; m < 32; m += 4) {
       const float4 k4 = *reinterpret_cast<const float4*>(&sm.va[r0 + m]);
@@ -306,12 +320,14 @@ __device__ __forceinline__ void encode_boundary(float (&x)[64], const WinPtrs& w
   }
   float m0 = 0.f, m1 = 0.f;
 #pragma unroll
-  for (int m = 0; m < 32; ++m) {
-    const float ic = sm.rowf[r0 + m];
+  for (int m = 0; m < 32; m += 2) {
+    const float ic = sm.rowf[r0 + m], ic1 = sm.rowf[r0 + m + 1];
     x[2 * m] *= ic;
     x[2 * m + 1] *= ic;
-    m0 = fmaxf(m0, fabsf(x[2 * m]));
-    m1 = fmaxf(m1, fabsf(x[2 * m + 1]));
+    x[2 * m + 2] *= ic1;
+    x[2 * m + 3] *= ic1;
+    m0 = fmaxf(m0, fmaxf(fabsf(x[2 * m]), fabsf(x[2 * m + 2])));
+    m1 = fmaxf(m1, fmaxf(fabsf(x[2 * m + 1]), fabsf(x[2 * m + 3])));
   }
   sm.colA[rb][p] = make_float2(m0, m1);
   __syncthreads();
@@ -321,14 +337,17 @@ __device__ __forceinline__ void encode_boundary(float (&x)[64], const WinPtrs& w
     b0 = fmaxf(b0, sm.colA[r][p].x);
     b1 = fmaxf(b1, sm.colA[r][p].y);
   }
+  // codes by magic rounding: |x| <= B_j and s = fl(127 / B_j) keep the exact
+  // product within 127 (1 + 2^-24), so the rounded code never leaves +-127 and
+  // its two's-complement byte is the low byte of m
   const float s0 = b0 > 0.f ? 127.0f / b0 : 0.f, s1 = b1 > 0.f ? 127.0f / b1 : 0.f;
 #pragma unroll
   for (int m = 0; m < 32; ++m) {
-    x[2 * m] = fminf(fmaxf(rintf(x[2 * m] * s0), -127.f), 127.f) + 128.f;
-    x[2 * m + 1] = fminf(fmaxf(rintf(x[2 * m + 1] * s1), -127.f), 127.f) + 128.f;
+    x[2 * m] = fmaf(x[2 * m], s0, kMagic);
+    x[2 * m + 1] = fmaf(x[2 * m + 1], s1, kMagic);
   }
   uint32_t wd[16];
-  pack_codes<8>(x, wd);
+  pack_magic<8>(x, wd);
   store_chunk<8, NP>(wp.Z, rb, p, wd);
   if (rb == 0) *reinterpret_cast<float2*>(wp.B + j0) = make_float2(b0, b1);
   if (t == 0) wp.ell[0] = 0;
@@ -341,7 +360,7 @@ __device__ __forceinline__ void encode_boundary(float (&x)[64], const WinPtrs& w
 
 // Rebuild the dense state of L records (staged in LDS; record L-1 replaced by
 // the current token's when `last_new`) and R compensator pairs (staged) into
-// x, which holds Z + 128 on entry.
+// x, which holds the boundary codes Z on entry.
 template <int DK, int DV, int PM, int RMX>
 __device__ __forceinline__ void rebuild(float (&x)[64], const WinPtrs& wp, int L, int R,
                                         bool last_new, SmemWin<DK, DV, PM, RMX>& sm) {
@@ -371,17 +390,17 @@ __device__ __forceinline__ void rebuild(float (&x)[64], const WinPtrs& wp, int L
 #pragma unroll
   for (int m = 0; m < 32; ++m) {
     const float f = sm.rowf[r0 + m];
-    x[2 * m] = f * bb.x * (x[2 * m] - 128.f);
-    x[2 * m + 1] = f * bb.y * (x[2 * m + 1] - 128.f);
+    x[2 * m] = (x[2 * m] * f) * bb.x;
+    x[2 * m + 1] = (x[2 * m + 1] * f) * bb.y;
   }
   // compensator pairs decay with the boundary: Gamma_{1:L} kc_h uc_h^T
   const float gb = sm.g1[PM];
   for (int h = 0; h < R; ++h) {
-    const float u0 = sm.uc[h][j0], u1 = sm.uc[h][j0 + 1];
+    const float u0 = gb * sm.uc[h][j0], u1 = gb * sm.uc[h][j0 + 1];
 #pragma unroll
     for (int m = 0; m < 32; m += 4) {
       const float4 k4 = *reinterpret_cast<const float4*>(&sm.kc[h][r0 + m]);
-      const float kv[4] = {gb * k4.x, gb * k4.y, gb * k4.z, gb * k4.w};
+      const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         x[2 * (m + q)] = fmaf(kv[q], u0, x[2 * (m + q)]);
@@ -460,7 +479,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     stg.issue(wp, ell, R);
     stg.commit(ell, R, sm);
   }
-  unpack_offset<8>(wd, x);  // Z + 128
+  unpack_signed8(wd, x);  // Z
   if constexpr (op == OP_UNPACK || op == OP_FLUSH) {
     if (op == OP_FLUSH && ell == 0) return;
     __syncthreads();
@@ -484,17 +503,9 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     sm.x1[r] = x1;
     sm.qv[r] = qq;
     sm.ktn[r] = kn;
-    float c1 = ca * x1, c2 = ca * qq;
-    sm.cx1[r] = c1;
-    sm.cq[r] = c2;
+    sm.cx1[r] = ca * x1;
+    sm.cq[r] = ca * qq;
     wp.K[ell * DK + r] = kn;  // the new record's key (record slot ell is free)
-    // sums over the block's 32 rows, valid at p = 16 .. 31
-    c1 = half32_sum_hi(c1);
-    c2 = half32_sum_hi(c2);
-    if (p == 16) {
-      sm.csum[rb][0] = c1;
-      sm.csum[rb][1] = c2;
-    }
   }
   __syncthreads();
   if (t == 0) {
@@ -527,7 +538,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     }
     sm.dots[rb][p] = make_float2(d1, d2);
   }
-  // boundary readouts: sum_a Z_aj (C_a x_a) = sum_a (u_aj - 128) C_a x_a
+  // boundary readouts: sum_a Z_aj (C_a x_a)
   float s10 = 0.f, s11 = 0.f, s20 = 0.f, s21 = 0.f;
 #pragma unroll
   for (int m = 0; m < 32; m += 4) {
@@ -542,9 +553,8 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
       s21 = fmaf(v2[q], x[2 * (m + q) + 1], s21);
     }
   }
-  const float o1 = -128.f * sm.csum[rb][0], o2 = -128.f * sm.csum[rb][1];
-  sm.colA[rb][p] = make_float2(s10 + o1, s11 + o1);
-  sm.colB[rb][p] = make_float2(s20 + o2, s21 + o2);
+  sm.colA[rb][p] = make_float2(s10, s11);
+  sm.colB[rb][p] = make_float2(s20, s21);
   __syncthreads();
   if (rb == 0) {
     float r10 = 0.f, r11 = 0.f, r20 = 0.f, r21 = 0.f;
