@@ -27,13 +27,14 @@ namespace {
 template <int DK, int DV>
 struct SmemGdn {
   // per-row constants: 0 kappa, 1 gamma, 2 theta, 3 rho (row factor of Xt),
-  // 4 pi (X / r = Xt pi) or sigma (uniform), 5 lambda (refit weight)
+  // 4 1 / w (STEP, until the row-scale pass), then pi (X / r = Xt pi) or
+  // sigma (uniform), 5 the impact factor w (STEP), then lambda (refit weight)
   float rowc[6][DK];
   float ksum[DK / 32];                        // sum of kappa per row block
   float2 colA[DK / 32][DV / 2];               // column partials per row block
   float2 colB[DK / 32][DV / 2];
   float2 colM[DK / 32][DV / 2];
-  float4 colC[DK / 32][DV / 2];
+  float4 colC[DK / 32][DV / 2];               // (row block 0's part holds the token's v until pass 4)
   alignas(16) float rowt[DK / 32][16][RowT<DV / 2>::S];  // row partials of 16 rows, transposed
 };
 
@@ -140,8 +141,9 @@ __device__ __forceinline__ void codes_rowwise(float (&x)[64], int sig, uint32_t 
   if constexpr (BITS == 6) pack_magic<6>(x, w);
 }
 
-// Quantized (b in {2,4,6,8}) head: uniform (UNI) or STEP dual-axis.
-template <int DK, int DV, int BITS, bool UNI, int OP>
+// Quantized (b in {2,4,6,8}) head: uniform (UNI) or STEP dual-axis.  LATE:
+// the launch is one round of resident workgroups (see EARLY below).
+template <int DK, int DV, int BITS, bool UNI, int OP, bool LATE = false>
 __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, const int h,
                                            unsigned char* base, SmemGdn<DK, DV>& sm) {
   using G = Geo<DK, DV>;
@@ -156,6 +158,14 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
   __half* rs_ptr = reinterpret_cast<__half*>(base + wuni(a.P.r_off[h]));
   __half* c_ptr = UNI ? nullptr : reinterpret_cast<__half*>(base + wuni(a.P.c_off[h]));
   const long long tk = (long long)tile * DK, tv = (long long)tile * DV;
+  // The token's v (needed after the first block barrier) and the impact
+  // factors (needed by the row-scale pass) go out with the codes and wait in
+  // LDS, so no memory round trip is left on the path after a barrier.  On
+  // the other tile shapes the extra live ranges spill, and in a launch that
+  // the chip holds in one round of workgroups staging measured slower (all
+  // tiles start together, and the start-up burst is the path): both are read
+  // where they are used there.
+  constexpr bool EARLY = DK == 128 && DV == 128 && !LATE;
 
   float x[64];
   float y0 = 0.f, y1 = 0.f;
@@ -167,7 +177,14 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
       x[2 * m] = v2.x;
       x[2 * m + 1] = v2.y;
     }
-    if (p < 32) sm.rowc[3][r0 + p] = 1.0f;
+    if (p < 32) {
+      const int i = r0 + p;
+      sm.rowc[3][i] = 1.0f;
+      if (!UNI && EARLY) {
+        sm.rowc[5][i] = a.P.w[h * DK + i];
+        sm.rowc[4][i] = a.P.winv[h * DK + i];
+      }
+    }
     wave_sync();
   } else {
     // uniform decode reads the codes as binary16 subnormals (u 2^-24): the
@@ -180,6 +197,9 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
     constexpr float HS = HC ? 0x1p24f : 1.0f;
     uint32_t wd[2 * BITS];
     load_chunk<BITS, NP>(base, rb, p, wd);
+    // row block 0 loads the token's v behind the codes
+    float2 vin = make_float2(0.f, 0.f);
+    if (EARLY && op == OP_DECODE && rb == 0) vin = *reinterpret_cast<const float2*>(a.v + tv + j0);
     float c0 = 1.0f, c1 = 1.0f;
     if (!UNI) {
       c0 = __half2float(c_ptr[j0]);
@@ -203,11 +223,18 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
         sm.rowc[1][i] = bk * frcp(rp);     // gamma
         sm.rowc[2][i] = qq * rp;           // theta: readout weight on Xt
         sm.rowc[3][i] = rp;
+        if (!UNI && EARLY) {  // the impact factors wait in LDS for the row-scale pass
+          sm.rowc[5][i] = a.P.w[h * DK + i];
+          sm.rowc[4][i] = a.P.winv[h * DK + i];
+        }
         // sum of kappa over the block's 32 rows (offset of the unpacked codes)
         const float ksum = half32_sum_hi(kap);
         if (p == 16) sm.ksum[rb] = ksum;
       }
     }
+    // (staged before the unpack: it arrives right behind the codes, and no
+    // register stays live across pass 1)
+    if (EARLY && op == OP_DECODE && rb == 0) sm.colC[0][p] = make_float4(vin.x, vin.y, 0.f, 0.f);
     uint32_t hc[32];
     if constexpr (HC) unpack_half<BITS>(wd, hc);
     else unpack_offset<BITS>(wd, x);
@@ -249,7 +276,8 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
       d0 += c.x;
       d1 += c.y;
     }
-    const float2 vv = *reinterpret_cast<const float2*>(a.v + tv + j0);
+    const float2 vv = EARLY ? make_float2(sm.colC[0][p].x, sm.colC[0][p].y)
+                              : *reinterpret_cast<const float2*>(a.v + tv + j0);
     const float e0 = vv.x - c0 * d0, e1 = vv.y - c1 * d1;
     // pass 2: Xt = c_j (u - off) + gamma_i e_j, readout partials
     const float o0 = -OFF * c0, o1 = -OFF * c1;
@@ -311,10 +339,10 @@ __device__ __forceinline__ void quant_tile(const TileArgs& a, const int tile, co
       rs_ptr[i] = __float2half_rn(si);
       sm.rowc[4][i] = rp * frcp(si);  // code pre-value = Xt * sigma_i
     } else {
-      const float wi = a.P.w[h * DK + i];
+      const float wi = EARLY ? sm.rowc[5][i] : a.P.w[h * DK + i];
+      const float wiv = EARLY ? sm.rowc[4][i] : a.P.winv[h * DK + i];
       // the hardware square root (1 ulp) only feeds an FP16 rounding
-      const float ri =
-          fp16_scale(__builtin_amdgcn_sqrtf(rp * s * (1.0f / (float)DV) * a.P.winv[h * DK + i]));
+      const float ri = fp16_scale(__builtin_amdgcn_sqrtf(rp * s * (1.0f / (float)DV) * wiv));
       rs_ptr[i] = __float2half_rn(ri);
       sm.rowc[4][i] = rp * frcp(ri);                  // pi: X / r_i = Xt * pi_i
       sm.rowc[5][i] = wi * wi * ri * ri * (1.0f / QB);  // lambda: refit weight
@@ -442,6 +470,10 @@ __device__ __forceinline__ void pivot_tile(const TileArgs& a, const int tile, co
       sm.rowc[1][t] = wuni(a.beta[tile]) * kk;
       sm.rowc[2][t] = a.q[tk + t];
     }
+    if (rb == 0) {
+      const float2 v2 = *reinterpret_cast<const float2*>(a.v + tv + j0);
+      sm.colC[0][p] = make_float4(v2.x, v2.y, 0.f, 0.f);
+    }
     __syncthreads();
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -459,7 +491,7 @@ __device__ __forceinline__ void pivot_tile(const TileArgs& a, const int tile, co
       d0 += c.x;
       d1 += c.y;
     }
-    const float2 vv = *reinterpret_cast<const float2*>(a.v + tv + j0);
+    const float2 vv = make_float2(sm.colC[0][p].x, sm.colC[0][p].y);
     const float e0 = vv.x - d0, e1 = vv.y - d1;
     float y0 = 0.f, y1 = 0.f;
 #pragma unroll
@@ -549,7 +581,7 @@ __device__ __forceinline__ int pick5(const int (&v)[5], int i) {
 // workgroup runs exactly one of the width-specialised bodies; the kernel's
 // register budget is the largest of them.
 // Tile t of the class list: class c holds t in [cls_end[c-1], cls_end[c]).
-template <int DK, int DV, bool UNI>
+template <int DK, int DV, bool UNI, bool LATE = false>
 __device__ __forceinline__ void merged_tile(const TileArgs& a, int t, SmemGdn<DK, DV>& sm) {
   int c = 0;
 #pragma unroll
@@ -567,10 +599,10 @@ __device__ __forceinline__ void merged_tile(const TileArgs& a, int t, SmemGdn<DK
   }
   unsigned char* base = a.pool + (long long)slot * a.P.slot_bytes + wuni(a.P.head_off[h]);
   switch (bits) {
-    case 2: quant_tile<DK, DV, 2, UNI, OP_DECODE>(a, tile, h, base, sm); break;
-    case 4: quant_tile<DK, DV, 4, UNI, OP_DECODE>(a, tile, h, base, sm); break;
-    case 6: quant_tile<DK, DV, 6, UNI, OP_DECODE>(a, tile, h, base, sm); break;
-    case 8: quant_tile<DK, DV, 8, UNI, OP_DECODE>(a, tile, h, base, sm); break;
+    case 2: quant_tile<DK, DV, 2, UNI, OP_DECODE, LATE>(a, tile, h, base, sm); break;
+    case 4: quant_tile<DK, DV, 4, UNI, OP_DECODE, LATE>(a, tile, h, base, sm); break;
+    case 6: quant_tile<DK, DV, 6, UNI, OP_DECODE, LATE>(a, tile, h, base, sm); break;
+    case 8: quant_tile<DK, DV, 8, UNI, OP_DECODE, LATE>(a, tile, h, base, sm); break;
     case 16:
       if constexpr (!UNI) pivot_tile<DK, DV, OP_DECODE>(a, tile, h, base, sm);
       break;
@@ -598,11 +630,11 @@ __device__ __forceinline__ void class0_tile(const TileArgs& a, int bi, int j, Sm
 // class head t % cls_n).  The width is uniform over a workgroup, so each
 // workgroup runs exactly one of the width-specialised bodies; the kernel's
 // register budget is the largest of them.
-template <int DK, int DV, bool UNI>
+template <int DK, int DV, bool UNI, bool LATE>
 __global__ __launch_bounds__((DK / 32) * (DV / 2))
 __attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_decode_kernel(TileArgs a) {
   __shared__ SmemGdn<DK, DV> sm;
-  merged_tile<DK, DV, UNI>(a, blockIdx.x, sm);
+  merged_tile<DK, DV, UNI, LATE>(a, blockIdx.x, sm);
 }
 
 // STEP decode of class 0 in its width-specialised body plus the other classes
@@ -633,6 +665,9 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void gdn_class_kernel(TileArgs a) {
   class0_tile<DK, DV, BITS, UNI>(a, blockIdx.y, blockIdx.x, sm);
 }
 
+// 256 CUs x 4 resident 256-lane workgroups: the tiles of one round
+constexpr int kRoundTiles = 1024;
+
 template <int DK, int DV, int BITS>
 hipError_t launch_solo(const TileArgs& a, const dim3 grid, const dim3 block, hipStream_t s) {
   if (a.P.mode == SQ_MODE_UNIFORM) {
@@ -661,10 +696,14 @@ hipError_t launch_decode(const TileArgs& a, bool solo, hipStream_t s) {
       default: return hipErrorInvalidValue;
     }
   }
-  if (a.P.mode == SQ_MODE_UNIFORM)
-    hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, true>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, false>), grid, block, 0, s, a);
+  if (a.P.mode == SQ_MODE_UNIFORM) {
+    hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, true, false>), grid, block, 0, s, a);
+  } else {
+    bool late = false;
+    if constexpr (DK == 128 && DV == 128) late = a.n_tiles <= kRoundTiles;
+    if (late) hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, false, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

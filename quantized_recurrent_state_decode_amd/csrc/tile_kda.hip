@@ -40,6 +40,7 @@ struct SmemKdaCore {
   float2 colB[DK / 32][DV / 2];
   float2 colM[DK / 32][DV / 2];
   float4 colC[DK / 32][DV / 2];
+  float2 vin[DV / 2];  // the token's v, staged by row block 0
 };
 // Row m of a width class is addressed as (class base - lo * row bytes) + m *
 // row bytes, the last term an instruction offset.  The first term may fall
@@ -278,6 +279,12 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
     }
     beta = a.beta[tile];
   }
+  // the token's v is needed after the first block barrier of pass 1; row
+  // block 0 loads it with the other inputs and stages it in LDS (on the
+  // other tile shapes the extra live range spills: v is read late there)
+  constexpr bool EARLY_V = DK == 128 && DV == 128;
+  float2 vin = make_float2(0.f, 0.f);
+  if (EARLY_V && OP == OP_DECODE && ok && rb == 0) vin = *reinterpret_cast<const float2*>(a.v + tv + j0);
   if (!a.out) {
     ok = slot >= 0 && (long long)slot < a.n_slots;
     base = a.pool + (long long)(ok ? slot : 0) * a.P.slot_bytes + wuni(a.P.head_off[h]);
@@ -396,6 +403,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
         }
       }
     }
+    if (EARLY_V && OP == OP_DECODE && rb == 0) sm.vin[p] = vin;
     __syncthreads();  // codes staged, per-row constants ready
     fresh_masks<WU>(R);
     int rda[5];
@@ -460,7 +468,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
       d0 += sm.colA[r][p].x;
       d1 += sm.colA[r][p].y;
     }
-    const float2 vv = *reinterpret_cast<const float2*>(a.v + tv + j0);
+    const float2 vv = EARLY_V ? sm.vin[p] : *reinterpret_cast<const float2*>(a.v + tv + j0);
     const float e0 = vv.x - d0, e1 = vv.y - d1;
     // pass 2: Xt = x + gamma_s e_j, readout partials
 #pragma unroll

@@ -54,6 +54,9 @@ struct SmemWin {
   float va[RMX > 0 ? DK : 1];       // compensator fit: a = M b, then the rounded kc
   float red[2][DK / 32 + 1];        // compensator fit: block sums (two buffers)
   float unew[DV];
+  float crow[DK];                   // the boundary's row scales C, staged
+  float2 bcol[DV / 2];              // its column scales B, staged
+  float2 vin[DV / 2];               // the token's v, staged
   float2 colA[DK / 32][DV / 2];
   float2 colB[DK / 32][DV / 2];
   union {
@@ -384,9 +387,9 @@ __device__ __forceinline__ void rebuild(float (&x)[64], const WinPtrs& wp, int L
   }
   if (last_new)
     for (int i = t; i < DV; i += NT) sm.u.rec.U[L - 1][i] = sm.unew[i];
-  if (t < DK) sm.rowf[t] = sm.g1[PM] * wp.C[t] * (1.0f / 127.0f);
+  if (t < DK) sm.rowf[t] = sm.g1[PM] * sm.crow[t] * (1.0f / 127.0f);
   __syncthreads();
-  const float2 bb = *reinterpret_cast<const float2*>(wp.B + j0);
+  const float2 bb = sm.bcol[p];
 #pragma unroll
   for (int m = 0; m < 32; ++m) {
     const float f = sm.rowf[r0 + m];
@@ -462,7 +465,12 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
   uint32_t wd[16];
   load_chunk<8, NP>(wp.Z, rb, p, wd);
   const long long tk = (long long)tile * DK, tv = (long long)tile * DV;
-  float kk = 0.f, qq = 0.f, ca = 0.f, alpha = 0.f, beta = 0.f;
+  float kk = 0.f, qq = 0.f, alpha = 0.f, beta = 0.f;
+  // the boundary's scales and the token's v are used after block barriers
+  // (readout tail, rebuild): they go out with the codes and wait in LDS
+  const float ca = p < 32 ? wp.C[r0 + p] : 0.f;
+  float2 bcol = make_float2(0.f, 0.f), vin = make_float2(0.f, 0.f);
+  if (rb == 0) bcol = *reinterpret_cast<const float2*>(wp.B + j0);
   if constexpr (op == OP_DECODE) {
     alpha = a.gate[tile];
     beta = a.beta[tile];
@@ -470,14 +478,19 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
       const int r = r0 + p;
       kk = a.k[tk + r];
       qq = a.q[tk + r];
-      ca = wp.C[r];
     }
+    if (rb == 0) vin = *reinterpret_cast<const float2*>(a.v + tv + j0);
   }
   const int ell = min(max(ell0, 0), P - 1);
   {
     Staged<DK, DV, PM, RMX> stg;
     stg.issue(wp, ell, R);
     stg.commit(ell, R, sm);
+    if (p < 32) sm.crow[r0 + p] = ca;
+    if (rb == 0) {
+      sm.bcol[p] = bcol;
+      sm.vin[p] = vin;
+    }
   }
   unpack_signed8(wd, x);  // Z
   if constexpr (op == OP_UNPACK || op == OP_FLUSH) {
@@ -565,7 +578,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
       r20 += sm.colB[r][p].x;
       r21 += sm.colB[r][p].y;
     }
-    const float2 bb = *reinterpret_cast<const float2*>(wp.B + j0);
+    const float2 bb = sm.bcol[p];
     const float f0 = bb.x * (1.0f / 127.0f), f1 = bb.y * (1.0f / 127.0f);
     float pv0 = sm.g1[PM] * f0 * r10, pv1 = sm.g1[PM] * f1 * r11;
     float w0 = sm.g2[PM] * f0 * r20, w1 = sm.g2[PM] * f1 * r21;
@@ -600,7 +613,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     float dn = 0.f;  // kt_i . q
 #pragma unroll
     for (int r = 0; r < NRB; ++r) dn += sm.dots[r][ell].y;
-    const float2 vv = *reinterpret_cast<const float2*>(a.v + tv + j0);
+    const float2 vv = sm.vin[p];
     const float u0 = vv.x - pv0, u1 = vv.y - pv1;
     w0 = fmaf(u0, dn, w0);
     w1 = fmaf(u1, dn, w1);
