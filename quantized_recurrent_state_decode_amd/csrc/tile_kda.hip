@@ -41,6 +41,7 @@ struct SmemKdaCore {
   float2 colM[DK / 32][DV / 2];
   float4 colC[DK / 32][DV / 2];
   float2 vin[DV / 2];  // the token's v, staged by row block 0
+  int2 rowab[DK];      // storage row s: LDS byte address of its codes, its width
 };
 // Row m of a width class is addressed as (class base - lo * row bytes) + m *
 // row bytes, the last term an instruction offset.  The first term may fall
@@ -404,40 +405,80 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
       }
     }
     if (EARLY_V && OP == OP_DECODE && rb == 0) sm.vin[p] = vin;
+    if (WU && p < 32) sm.rowab[r0 + p] = make_int2(lds_addr(codes) + roff, rbits);
     __syncthreads();  // codes staged, per-row constants ready
-    fresh_masks<WU>(R);
-    int rda[5];
-    lane_addrs<false>(R, p, rda);
-    // all rows' fields are read before any is decoded, so the LDS reads of
-    // the 32 rows overlap: the width only selects the address, and one
-    // two-dword read (outside the branches) serves every width; x holds the
-    // raw dwords in between
+    if constexpr (WU) {
+      // The rows' widths come from the row table, not from branches: lane p's
+      // two fields of a row of width B start at bit 2 B p, so the read address
+      // and the decode are arithmetic on B.  All rows' fields are read before
+      // any is decoded (the LDS reads overlap; x holds the raw dwords in
+      // between).  FP16 rows decode as 16-bit integers here and are redone
+      // below.
+      const uint32_t p2 = 2u * p;
 #pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      int ad = 0;
-      by_class(R, m, [&](auto w) {
-        constexpr int C = decltype(w)::idx;
-        ad = rda[C] + m * row_bytes<DV, C>();
-      });
-      x[2 * m] = __uint_as_float(lds_ld32(ad));
-      x[2 * m + 1] = __uint_as_float(lds_ld32(ad + 4));
-    }
-    fresh_masks<WU>(R);
+      for (int m = 0; m < 32; ++m) {
+        const int2 ab = sm.rowab[r0 + m];
+        const uint32_t bp = __umul24((uint32_t)ab.y, p2);
+        const int ad = ab.x + (int)((bp >> 5) << 2);
+        x[2 * m] = __uint_as_float(lds_ld32(ad));
+        x[2 * m + 1] = __uint_as_float(lds_ld32(ad + 4));
+      }
 #pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      by_class(R, m, [&](auto w) {
-        constexpr int B = decltype(w)::bits;
-        float z0, z1;
-        decode_pair<B>(__float_as_uint(x[2 * m]), __float_as_uint(x[2 * m + 1]), p, z0, z1);
-        if constexpr (B == 16) {
-          const float f = sm.rowc[4][r0 + m];
-          x[2 * m] = f * z0;
-          x[2 * m + 1] = f * z1;
-        } else {
-          x[2 * m] = c0 * z0;
-          x[2 * m + 1] = c1 * z1;
+      for (int m = 0; m < 32; ++m) {
+        const int2 ab = sm.rowab[r0 + m];
+        const uint32_t bp = __umul24((uint32_t)ab.y, p2);
+        const uint32_t f = __builtin_amdgcn_alignbit(__float_as_uint(x[2 * m + 1]),
+                                                     __float_as_uint(x[2 * m]), bp);
+        // (the builtin returns an unsigned type: reinterpret as signed first)
+        x[2 * m] = c0 * (float)(int)__builtin_amdgcn_sbfe((int)f, 0, ab.y);
+        x[2 * m + 1] = c1 * (float)(int)__builtin_amdgcn_sbfe((int)f, ab.y, ab.y);
+      }
+      if (R.msk[4]) {  // FP16 rows of the block: their values, times rho
+#pragma unroll
+        for (int m = 0; m < 32; ++m) {
+          if (R.msk[4] & (1u << m)) {
+            const uint32_t h2 = lds_ld32(sm.rowab[r0 + m].x + 4 * p);
+            const float f = sm.rowc[4][r0 + m];
+            x[2 * m] = f * half_from_bits(h2);
+            x[2 * m + 1] = f * half_from_bits(h2 >> 16);
+          }
         }
-      });
+      }
+    } else {
+      fresh_masks<WU>(R);
+      int rda[5];
+      lane_addrs<false>(R, p, rda);
+      // all rows' fields are read before any is decoded, so the LDS reads of
+      // the 32 rows overlap: the width only selects the address, and one
+      // two-dword read (outside the branches) serves every width; x holds the
+      // raw dwords in between
+#pragma unroll
+      for (int m = 0; m < 32; ++m) {
+        int ad = 0;
+        by_class(R, m, [&](auto w) {
+          constexpr int C = decltype(w)::idx;
+          ad = rda[C] + m * row_bytes<DV, C>();
+        });
+        x[2 * m] = __uint_as_float(lds_ld32(ad));
+        x[2 * m + 1] = __uint_as_float(lds_ld32(ad + 4));
+      }
+      fresh_masks<WU>(R);
+#pragma unroll
+      for (int m = 0; m < 32; ++m) {
+        by_class(R, m, [&](auto w) {
+          constexpr int B = decltype(w)::bits;
+          float z0, z1;
+          decode_pair<B>(__float_as_uint(x[2 * m]), __float_as_uint(x[2 * m + 1]), p, z0, z1);
+          if constexpr (B == 16) {
+            const float f = sm.rowc[4][r0 + m];
+            x[2 * m] = f * z0;
+            x[2 * m + 1] = f * z1;
+          } else {
+            x[2 * m] = c0 * z0;
+            x[2 * m + 1] = c1 * z1;
+          }
+        });
+      }
     }
     if constexpr (OP == OP_UNPACK) {
       float* S = a.S_out + (long long)tile * DK * DV;
