@@ -537,19 +537,52 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     }
     sm.g2[PM] = g;
   }
-  // dot products over this wave's rows: lane j < PM handles record j, lane
-  // PM + h compensator pair h
-  const bool comp_lane = p >= PM && p < PM + R;
-  if ((p <= ell && p < PM) || comp_lane) {
-    const float* src = comp_lane ? sm.kc[p - PM] : (p == ell ? sm.ktn : sm.u.rec.K[p]);
+  // dot products over this wave's rows.  Unit u < PM is record u (the
+  // token's own key at u = ell), unit PM + h compensator pair h; the units
+  // take NU lanes (a power of two), and the wave's 32 rows are split into
+  // SEG segments over the remaining lanes (lane p: unit p % NU, segment
+  // p / NU), whose partial sums combine across lanes NU apart.  Each unit
+  // walks its segment's rows in a rotated order, so the lanes of one
+  // instruction read different rows of their key vectors rather than one
+  // LDS bank.
+  {
+    constexpr int NU = PM + RMX <= 16 ? 16 : PM + RMX <= 32 ? 32 : 64;
+    constexpr int SEG = NP / NU >= 4 ? 4 : NP / NU >= 2 ? 2 : 1;
+    constexpr int L = 32 / SEG;
+    const int u = p % NU, sg = p / NU;
+    const bool rec = u < PM && u <= ell, cmp = u >= PM && u < PM + R;
     float d1 = 0.f, d2 = 0.f;
-#pragma unroll 8
-    for (int m = 0; m < 32; ++m) {
-      const float kt = src[r0 + m];
-      d1 = fmaf(kt, sm.x1[r0 + m], d1);
-      d2 = fmaf(kt, sm.qv[r0 + m], d2);
+    if (sg < SEG && (rec || cmp)) {
+      const float* src = cmp ? sm.kc[u - PM] : (u == ell ? sm.ktn : sm.u.rec.K[u]);
+      const int rs = r0 + sg * L;
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        const int rr = rs + ((i + u) & (L - 1));
+        const float kt = src[rr];
+        d1 = fmaf(kt, sm.x1[rr], d1);
+        d2 = fmaf(kt, sm.qv[rr], d2);
+      }
     }
-    sm.dots[rb][p] = make_float2(d1, d2);
+    if constexpr (SEG >= 2) {  // partner lanes NU apart (16 or 32)
+      float a0, b0, a1, b1;
+      if constexpr (NU == 16) {
+        swap16(d1, a0, b0);
+        swap16(d2, a1, b1);
+      } else {
+        swap32(d1, a0, b0);
+        swap32(d2, a1, b1);
+      }
+      d1 = a0 + b0;
+      d2 = a1 + b1;
+    }
+    if constexpr (SEG == 4) {  // and 32 apart
+      float a0, b0, a1, b1;
+      swap32(d1, a0, b0);
+      swap32(d2, a1, b1);
+      d1 = a0 + b0;
+      d2 = a1 + b1;
+    }
+    if (sg == 0 && (rec || cmp)) sm.dots[rb][u] = make_float2(d1, d2);
   }
   // boundary readouts: sum_a Z_aj (C_a x_a)
   float s10 = 0.f, s11 = 0.f, s20 = 0.f, s21 = 0.f;
