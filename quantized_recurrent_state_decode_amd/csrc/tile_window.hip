@@ -107,6 +107,20 @@ __device__ __forceinline__ void unpack_signed8(const uint32_t (&w)[16], float (&
   }
 }
 
+// Suffix products of the decays of records 0 .. n-1 (n <= PM), computed by
+// the 64 lanes of the first wave together (a log-step product scan):
+// g[j] = prod_{m=j+1}^{n-1} al[m] for j < PM, and g[PM] = the product of all.
+template <int PM>
+__device__ __forceinline__ void decay_suffix(const float* al, int n, float* g) {
+  const int j = threadIdx.x;
+  float a = j < n ? al[j] : 1.f;  // lanes past the records hold 1
+#pragma unroll
+  for (int off = 1; off < PM; off <<= 1) a *= __shfl_down(a, off, 64);
+  const float e = __shfl_down(a, 1, 64);  // lane j + 1's inclusive product
+  if (j < PM) g[j] = e;
+  if (j == 0) g[PM] = a;
+}
+
 // The records and compensator pairs held by a head, staged through
 // registers: `issue` starts every load (a fixed number per thread,
 // predicated on what the head holds), `commit` stores them to LDS, so the
@@ -371,14 +385,7 @@ __device__ __forceinline__ void rebuild(float (&x)[64], const WinPtrs& wp, int L
   constexpr int NP = G::NP, NT = G::NT;
   const int t = threadIdx.x, rb = t / NP, p = t - rb * NP, j0 = 2 * p, r0 = 32 * rb;
   // factor of record j: prod_{m=j+1}^{L-1} al[m]; Gamma over all L records
-  if (t == 0) {
-    float g = 1.f;
-    for (int j = L - 1; j >= 0; --j) {
-      sm.g1[j] = g;
-      g *= sm.al[j];
-    }
-    sm.g1[PM] = g;
-  }
+  if (t < 64) decay_suffix<PM>(sm.al, L, sm.g1);
   __syncthreads();
   for (int i = t; i < L * DK; i += NT) {
     const int j = i / DK, a = i - j * DK;
@@ -521,21 +528,11 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     wp.K[ell * DK + r] = kn;  // the new record's key (record slot ell is free)
   }
   __syncthreads();
-  if (t == 0) {
-    // g1[j] = prod_{m=j+1}^{ell-1} al[m] (for u_i), g2[j] = prod_{m=j+1}^{ell} al[m]
-    // (for o_i); index PM holds the products over all records
-    float g = 1.f;
-    for (int j = ell - 1; j >= 0; --j) {
-      sm.g1[j] = g;
-      g *= sm.al[j];
-    }
-    sm.g1[PM] = g;
-    g = 1.f;
-    for (int j = ell; j >= 0; --j) {
-      sm.g2[j] = g;
-      g *= sm.al[j];
-    }
-    sm.g2[PM] = g;
+  // g1[j] = prod_{m=j+1}^{ell-1} al[m] (for u_i), g2[j] = prod_{m=j+1}^{ell} al[m]
+  // (for o_i); index PM holds the products over all records
+  if (t < 64) {
+    decay_suffix<PM>(sm.al, ell, sm.g1);
+    decay_suffix<PM>(sm.al, ell + 1, sm.g2);
   }
   // dot products over this wave's rows.  Unit u < PM is record u (the
   // token's own key at u = ell), unit PM + h compensator pair h; the units
