@@ -49,6 +49,7 @@ struct SmemWin {
   float al[PM + 1];               // record decays (+ a spare word)
   float g1[PM + 1], g2[PM + 1];   // suffix products of the decays
   float2 dots[DK / 32][PM + RMX];  // per row block: kt_j . x1, kt_j . q; then kc_h . x1, kc_h . q
+  float2 esum[PM + RMX];           // the same summed over row blocks, decay-scaled
   float kc[RMX > 0 ? RMX : 1][DK];  // compensator pairs of the head (float)
   float uc[RMX > 0 ? RMX : 1][DV];
   float va[RMX > 0 ? DK : 1];       // compensator fit: a = M b, then the rounded kc
@@ -612,37 +613,40 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void window_tile_kernel(TileArgs a) {
     const float f0 = bb.x * (1.0f / 127.0f), f1 = bb.y * (1.0f / 127.0f);
     float pv0 = sm.g1[PM] * f0 * r10, pv1 = sm.g1[PM] * f1 * r11;
     float w0 = sm.g2[PM] * f0 * r20, w1 = sm.g2[PM] * f1 * r21;
-    for (int hh = 0; hh < R; ++hh) {  // compensators decay with the boundary
-      float d1 = 0.f, d2 = 0.f;
+    // each unit's dot products summed over the row blocks and scaled by its
+    // decay, one lane per unit (records 0 .. ell, then the pairs), so the
+    // serial loops below read one value per unit
+    {
+      const int u = p;
+      if (u < PM + R && (u <= ell || u >= PM)) {
+        float d1 = 0.f, d2 = 0.f;
 #pragma unroll
-      for (int r = 0; r < NRB; ++r) {
-        d1 += sm.dots[r][PM + hh].x;
-        d2 += sm.dots[r][PM + hh].y;
+        for (int r = 0; r < NRB; ++r) {
+          d1 += sm.dots[r][u].x;
+          d2 += sm.dots[r][u].y;
+        }
+        const int gi = u >= PM ? PM : u;  // compensators decay with the boundary
+        sm.esum[u] = u == ell ? make_float2(0.f, d2) : make_float2(sm.g1[gi] * d1, sm.g2[gi] * d2);
       }
-      const float e1 = sm.g1[PM] * d1, e2 = sm.g2[PM] * d2;
+      wave_sync();
+    }
+    for (int hh = 0; hh < R; ++hh) {
+      const float2 e = sm.esum[PM + hh];
       const float uc0 = sm.uc[hh][j0], uc1 = sm.uc[hh][j0 + 1];
-      pv0 = fmaf(uc0, e1, pv0);
-      pv1 = fmaf(uc1, e1, pv1);
-      w0 = fmaf(uc0, e2, w0);
-      w1 = fmaf(uc1, e2, w1);
+      pv0 = fmaf(uc0, e.x, pv0);
+      pv1 = fmaf(uc1, e.x, pv1);
+      w0 = fmaf(uc0, e.y, w0);
+      w1 = fmaf(uc1, e.y, w1);
     }
     for (int j = 0; j < ell; ++j) {
-      float d1 = 0.f, d2 = 0.f;
-#pragma unroll
-      for (int r = 0; r < NRB; ++r) {
-        d1 += sm.dots[r][j].x;
-        d2 += sm.dots[r][j].y;
-      }
+      const float2 e = sm.esum[j];
       const float2 u = *reinterpret_cast<const float2*>(&sm.u.rec.U[j][j0]);
-      const float e1 = sm.g1[j] * d1, e2 = sm.g2[j] * d2;
-      pv0 = fmaf(u.x, e1, pv0);
-      pv1 = fmaf(u.y, e1, pv1);
-      w0 = fmaf(u.x, e2, w0);
-      w1 = fmaf(u.y, e2, w1);
+      pv0 = fmaf(u.x, e.x, pv0);
+      pv1 = fmaf(u.y, e.x, pv1);
+      w0 = fmaf(u.x, e.y, w0);
+      w1 = fmaf(u.y, e.y, w1);
     }
-    float dn = 0.f;  // kt_i . q
-#pragma unroll
-    for (int r = 0; r < NRB; ++r) dn += sm.dots[r][ell].y;
+    const float dn = sm.esum[ell].y;  // kt_i . q
     const float2 vv = sm.vin[p];
     const float u0 = vv.x - pv0, u1 = vv.y - pv1;
     w0 = fmaf(u0, dn, w0);
