@@ -230,6 +230,67 @@ __device__ __forceinline__ void codes_refit(float (&x)[64], const RowCls& R, con
   }
 }
 
+// Pass 4 for blocks whose row masks are wave-uniform (64 lanes per block):
+// the arithmetic runs inside the branch for the row's width, so the rounding
+// scale q_b / c0_j of each width is a register formed once, and the
+// denominator is summed per width, D = sum_B (sum_{rows of width B}
+// lambda_s z^2) / q_b(B) (lambda_s carries one factor 1 / q_b, the other is
+// applied per width at the end).  FP16 rows only store their values.
+template <int DK, int DV, bool SAT>
+__device__ __forceinline__ void codes_refit_wu(float (&x)[64], const RowCls& R, const float* lam,
+                                               float ic0, float ic1, float mgc, int p, float& N0,
+                                               float& N1, float& D0, float& D1) {
+  constexpr float QB[4] = {1.f, 7.f, 31.f, 127.f};
+  int wra[5];
+  lane_addrs<true>(R, p, wra);
+  float tau[4][2], dc[4][2];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    tau[c][0] = QB[c] * ic0;
+    tau[c][1] = QB[c] * ic1;
+    dc[c][0] = 0.f;
+    dc[c][1] = 0.f;
+  }
+#pragma unroll
+  for (int m4 = 0; m4 < 32; m4 += 2) {
+    const float2 l4 = *reinterpret_cast<const float2*>(lam + m4);
+    const float lv[2] = {l4.x, l4.y};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int m = m4 + u;
+      const float pv0 = x[2 * m], pv1 = x[2 * m + 1];
+      by_class(R, m, [&](auto w) {
+        constexpr int B = decltype(w)::bits, C = decltype(w)::idx;
+        const int a = wra[C] + m * row_bytes<DV, C>();
+        if constexpr (B == 16) {
+          lds_st32(a, half_bits(pv0) | (half_bits(pv1) << 16));
+        } else {
+          float mg0 = fmaf(pv0, tau[C][0], mgc), mg1 = fmaf(pv1, tau[C][1], mgc);
+          if constexpr (SAT) {  // a column scale saturated at the FP16 maximum
+            mg0 = __builtin_amdgcn_fmed3f(mg0, mgc - QB[C], mgc + QB[C]);
+            mg1 = __builtin_amdgcn_fmed3f(mg1, mgc - QB[C], mgc + QB[C]);
+          }
+          const float z0 = mg0 - mgc, z1 = mg1 - mgc;
+          const float t0 = lv[u] * z0, t1 = lv[u] * z1;
+          N0 = fmaf(t0, pv0, N0);
+          N1 = fmaf(t1, pv1, N1);
+          dc[C][0] = fmaf(t0, z0, dc[C][0]);
+          dc[C][1] = fmaf(t1, z1, dc[C][1]);
+          asm volatile("" : "+v"(N0), "+v"(N1), "+v"(dc[C][0]), "+v"(dc[C][1]));
+          write_pair<B>(a, p, mg0, mg1);
+        }
+      });
+    }
+  }
+  D0 = 0.f;
+  D1 = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    D0 = fmaf(dc[c][0], 1.f / QB[c], D0);
+    D1 = fmaf(dc[c][1], 1.f / QB[c], D1);
+  }
+}
+
 template <int DK, int DV, int OP>
 __global__ __launch_bounds__((DK / 32) * (DV / 2))
 __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
@@ -625,12 +686,19 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   float mgc = kMagic;
   asm volatile("" : "+s"(mgc));
   fresh_masks<WU>(R);
-  if (sat)
-    codes_refit<DK, DV, true>(x, R, &sm.rowc[5][r0], &sm.rowc[6][r0], &sm.rowc[7][r0], ic0, ic1,
-                              mgc, p, N0, N1, D0, D1);
-  else
-    codes_refit<DK, DV, false>(x, R, &sm.rowc[5][r0], &sm.rowc[6][r0], &sm.rowc[7][r0], ic0, ic1,
-                               mgc, p, N0, N1, D0, D1);
+  if constexpr (WU) {
+    if (sat)
+      codes_refit_wu<DK, DV, true>(x, R, &sm.rowc[5][r0], ic0, ic1, mgc, p, N0, N1, D0, D1);
+    else
+      codes_refit_wu<DK, DV, false>(x, R, &sm.rowc[5][r0], ic0, ic1, mgc, p, N0, N1, D0, D1);
+  } else {
+    if (sat)
+      codes_refit<DK, DV, true>(x, R, &sm.rowc[5][r0], &sm.rowc[6][r0], &sm.rowc[7][r0], ic0, ic1,
+                                mgc, p, N0, N1, D0, D1);
+    else
+      codes_refit<DK, DV, false>(x, R, &sm.rowc[5][r0], &sm.rowc[6][r0], &sm.rowc[7][r0], ic0,
+                                 ic1, mgc, p, N0, N1, D0, D1);
+  }
   sm.colC[rb][p] = make_float4(N0, N1, D0, D1);
   __syncthreads();
   for (int i = t * 16; i < code_bytes; i += NT * 16)
