@@ -326,6 +326,25 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 __device__ __forceinline__ int lds_addr(const void* ptr) { return (int)(uintptr_t)(const lds_u8*)ptr; }
 __device__ __forceinline__ uint32_t lds_ld32(int a) { return *(const lds_u32*)(uintptr_t)a; }
+typedef __attribute__((address_space(3))) signed char lds_s8;
+// byte k (0 or 1) of w, sign-extended, as a float: one v_cvt_f32_i32 with an
+// SDWA byte select (written out: the compiler otherwise emits a bit-field
+// extract and a conversion)
+template <int K>
+__device__ __forceinline__ float sbyte_f(uint32_t w) {
+  static_assert(K == 0 || K == 1, "byte 0 or 1");
+  float r;
+  if constexpr (K == 0)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0"
+        : "=v"(r) : "v"(w));
+  else
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1"
+        : "=v"(r) : "v"(w));
+  return r;
+}
+// a byte, sign-extended (ds_read_i8), and a 16-bit word (ds_read_u16)
+__device__ __forceinline__ int lds_ld8s(int a) { return *(const lds_s8*)(uintptr_t)a; }
+__device__ __forceinline__ uint32_t lds_ld16(int a) { return *(const lds_u16*)(uintptr_t)a; }
 __device__ __forceinline__ float4 lds_ld4(int a) {
   const f32x4 v = *(const lds_f32x4*)(uintptr_t)a;
   return make_float4(v.x, v.y, v.z, v.w);

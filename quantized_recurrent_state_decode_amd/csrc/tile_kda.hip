@@ -291,6 +291,41 @@ __device__ __forceinline__ void codes_refit_wu(float (&x)[64], const RowCls& R, 
   }
 }
 
+// Pass 4 for a 64-lane row block whose rows all have width B (4 or 8 bits;
+// no FP16 rows): no per-row dispatch, one rounding scale and one denominator.
+template <int DK, int DV, int B>
+__device__ __forceinline__ void codes_refit_one(float (&x)[64], const RowCls& R, const float* lam,
+                                                float ic0, float ic1, float mgc, int p, float& N0,
+                                                float& N1, float& D0, float& D1) {
+  constexpr int C = Wc<B>::idx;
+  constexpr float QB = (float)((1 << (B - 1)) - 1);
+  int wra[5];
+  lane_addrs<true>(R, p, wra);
+  const float tau0 = QB * ic0, tau1 = QB * ic1;
+  float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+  for (int m4 = 0; m4 < 32; m4 += 2) {
+    const float2 l4 = *reinterpret_cast<const float2*>(lam + m4);
+    const float lv[2] = {l4.x, l4.y};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int m = m4 + u;
+      const float pv0 = x[2 * m], pv1 = x[2 * m + 1];
+      const float mg0 = fmaf(pv0, tau0, mgc), mg1 = fmaf(pv1, tau1, mgc);
+      const float z0 = mg0 - mgc, z1 = mg1 - mgc;
+      const float t0 = lv[u] * z0, t1 = lv[u] * z1;
+      N0 = fmaf(t0, pv0, N0);
+      N1 = fmaf(t1, pv1, N1);
+      d0 = fmaf(t0, z0, d0);
+      d1 = fmaf(t1, z1, d1);
+      asm volatile("" : "+v"(N0), "+v"(N1), "+v"(d0), "+v"(d1));
+      write_pair<B>(wra[C] + m * row_bytes<DV, C>(), p, mg0, mg1);
+    }
+  }
+  D0 = d0 * (1.f / QB);
+  D1 = d1 * (1.f / QB);
+}
+
 template <int DK, int DV, int OP>
 __global__ __launch_bounds__((DK / 32) * (DV / 2))
 __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
@@ -374,6 +409,10 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
       R.b0[c] = lds_addr(codes) + first - lo * (DV * W[c] / 8);
     }
   }
+  // a 64-lane block whose rows all have 4 (one = 1) or 8 bits (one = 3) takes
+  // width-specialised read and code passes (about half the blocks of a
+  // calibrated plan: rows sorted by width fill whole blocks of one width)
+  const int one = !WU ? -1 : R.msk[1] == ~0u ? 1 : R.msk[3] == ~0u ? 3 : -1;
   float x[64];
   float y0 = 0.f, y1 = 0.f;
   if constexpr (OP == OP_PACK) {
@@ -475,6 +514,26 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
       // any is decoded (the LDS reads overlap; x holds the raw dwords in
       // between).  FP16 rows decode as 16-bit integers here and are redone
       // below.
+      if (one == 1) {
+        // every row 4 bits: lane p's two fields are byte p of the row, read
+        // sign-extended (the high field is then an arithmetic shift)
+        const int a0 = R.b0[1] + p;
+#pragma unroll
+        for (int m = 0; m < 32; ++m) {
+          const int v = lds_ld8s(a0 + m * row_bytes<DV, 1>());
+          x[2 * m] = c0 * (float)(int)__builtin_amdgcn_sbfe(v, 0, 4);
+          x[2 * m + 1] = c1 * (float)(v >> 4);
+        }
+      } else if (one == 3) {
+        // every row 8 bits: lane p's two fields are the 16-bit word p
+        const int a0 = R.b0[3] + 2 * p;
+#pragma unroll
+        for (int m = 0; m < 32; ++m) {
+          const uint32_t v = lds_ld16(a0 + m * row_bytes<DV, 3>());
+          x[2 * m] = c0 * sbyte_f<0>(v);
+          x[2 * m + 1] = c1 * sbyte_f<1>(v);
+        }
+      } else {
       const uint32_t p2 = 2u * p;
 #pragma unroll
       for (int m = 0; m < 32; ++m) {
@@ -493,6 +552,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
         // (the builtin returns an unsigned type: reinterpret as signed first)
         x[2 * m] = c0 * (float)(int)__builtin_amdgcn_sbfe((int)f, 0, ab.y);
         x[2 * m + 1] = c1 * (float)(int)__builtin_amdgcn_sbfe((int)f, ab.y, ab.y);
+      }
       }
       if (R.msk[4]) {  // FP16 rows of the block: their values, times rho
 #pragma unroll
@@ -689,6 +749,10 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void kda_tile_kernel(TileArgs a) {
   if constexpr (WU) {
     if (sat)
       codes_refit_wu<DK, DV, true>(x, R, &sm.rowc[5][r0], ic0, ic1, mgc, p, N0, N1, D0, D1);
+    else if (one == 1)
+      codes_refit_one<DK, DV, 4>(x, R, &sm.rowc[5][r0], ic0, ic1, mgc, p, N0, N1, D0, D1);
+    else if (one == 3)
+      codes_refit_one<DK, DV, 8>(x, R, &sm.rowc[5][r0], ic0, ic1, mgc, p, N0, N1, D0, D1);
     else
       codes_refit_wu<DK, DV, false>(x, R, &sm.rowc[5][r0], ic0, ic1, mgc, p, N0, N1, D0, D1);
   } else {
