@@ -15,7 +15,9 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libstepq.so")
+# SQ_LIBRARY names another build of the library to load instead (the tests'
+# checked host build); by default the in-tree libstepq.so
+LIB_PATH = os.environ.get("SQ_LIBRARY") or os.path.join(_HERE, "libstepq.so")
 
 SQ_OK, SQ_EINVAL, SQ_EUNSUPPORTED, SQ_ESLOT_RANGE, SQ_EDUP_SLOT = 0, 1, 2, 3, 4
 SQ_EPLAN_MISMATCH, SQ_EBUDGET, SQ_EHIP, SQ_ENOMEM, SQ_ENONFINITE = 5, 6, 7, 8, 9

@@ -20,6 +20,14 @@
 constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
+#ifdef SQ_HOSTCHECK
+void sq_check_failed(const char* cond, const char* file, int line) {
+  std::fprintf(stderr, "SQ_CHECK failed: %s (%s:%d)\n", cond, file, line);
+  std::fflush(stderr);
+  std::abort();
+}
+#endif
+
 namespace {
 
 thread_local std::string g_err;
@@ -103,11 +111,20 @@ void finish_plan(sq_plan* P) {
       analytic += used;
     }
     const long long padded = round_up(used, 256);
+    // the head's arrays lie inside its bytes, its bytes inside the slot
+    SQ_CHECK(used > 0 && used <= padded && padded % 256 == 0);
+    SQ_CHECK(P->r_off[h] >= 0 && P->r_off[h] <= used && P->c_off[h] >= 0 && P->c_off[h] <= used);
+    if (P->mode == SQ_MODE_STEP && P->kind == SQ_KIND_KDA) {
+      for (int s = 0; s < dk; ++s)
+        SQ_CHECK(P->row_off[h * dk + s] + row_bytes(dv, P->row_bits[h * dk + s]) <= P->r_off[h]);
+      SQ_CHECK(P->c_off[h] + 2LL * dv == used);
+    }
     P->head_off[h] = off;
     off += padded;
     payload += used;
     maxh = std::max<int>(maxh, (int)padded);
   }
+  SQ_CHECK(off % 256 == 0 && maxh % 256 == 0);  // 16-byte accesses stay aligned in every slot
   P->slot_bytes = off;
   P->payload_bytes = payload;
   P->analytic_bytes = analytic;
@@ -137,6 +154,17 @@ void finish_plan(sq_plan* P) {
   P->o_c_off = put(img, P->c_off);
   P->o_cls = put(img, P->cls_heads);
   img.resize(round_up((long long)img.size(), 256), 0);
+  // every table the kernels index lies inside the image, at its full length
+  SQ_CHECK(P->o_head_off + H * sizeof(long long) <= img.size());
+  SQ_CHECK(P->o_head_bits + H * sizeof(int) <= img.size());
+  SQ_CHECK(P->o_w + P->w.size() * sizeof(float) <= img.size());
+  SQ_CHECK(P->o_winv + P->winv.size() * sizeof(float) <= img.size());
+  SQ_CHECK(P->o_row_key + P->row_key.size() * sizeof(int) <= img.size());
+  SQ_CHECK(P->o_row_bits + P->row_bits.size() * sizeof(int) <= img.size());
+  SQ_CHECK(P->o_row_off + P->row_off.size() * sizeof(int) <= img.size());
+  SQ_CHECK(P->o_r_off + H * sizeof(int) <= img.size() && P->o_c_off + H * sizeof(int) <= img.size());
+  SQ_CHECK(P->o_cls + P->cls_heads.size() * sizeof(int) <= img.size());
+  SQ_CHECK(P->mode != SQ_MODE_STEP || P->kind != SQ_KIND_GDN || (int)P->cls_heads.size() == H);
 }
 
 DevPlan dev_view(const sq_plan* P, const void* dev) {
@@ -217,6 +245,14 @@ TileArgs class_args(const sq_plan* P, const TileArgs& a, const int* order, int l
     b.cls_end[i] = end;
   }
   b.n_tiles = end;
+  // each class's heads are a range of the class table, and its tiles the
+  // grid range [cls_end[i-1], cls_end[i]) of B rows per head
+  SQ_CHECK(b.n_cls >= 1 && b.n_cls <= 5);
+  for (int i = 0; i < b.n_cls; ++i) {
+    SQ_CHECK(b.cls_n[i] > 0 && b.cls_first[i] >= 0);
+    SQ_CHECK(b.cls_first[i] + b.cls_n[i] <= (int)P->cls_heads.size());
+    SQ_CHECK(b.cls_end[i] - (i ? b.cls_end[i - 1] : 0) == a.B * b.cls_n[i]);
+  }
   return b;
 }
 
@@ -254,6 +290,7 @@ hipError_t dispatch(const sq_plan* P, const TileArgs& a, hipStream_t st) {
   std::stable_sort(order, order + 5, [&](int x, int y) { return P->cls_count[x] > P->cls_count[y]; });
   int n = 0;
   while (n < 5 && P->cls_count[order[n]]) ++n;
+  SQ_CHECK(a.n_tiles == a.B * P->H);
   if (n == 1) return launch_decode_gdn(class_args(P, a, order, 0, 1), true, st);
   if ((long long)a.B * P->cls_count[order[0]] < kSoloTiles)
     return launch_decode_gdn(class_args(P, a, order, 0, n), false, st);
@@ -263,6 +300,10 @@ hipError_t dispatch(const sq_plan* P, const TileArgs& a, hipStream_t st) {
     TileArgs b = class_args(P, a, order, 0, n);
     const int n0 = b.cls_n[0];
     b.pre_rows = (b.n_tiles - b.cls_end[0] + n0 - 1) / n0;
+    // the leading rows hold every tile of the smaller classes, and every
+    // class together is the whole batch
+    SQ_CHECK((long long)b.pre_rows * n0 >= b.n_tiles - b.cls_end[0]);
+    SQ_CHECK(b.n_tiles == a.n_tiles);
     if ((long long)b.B + b.pre_rows <= 65535) return launch_split_gdn(b, st);
   }
   hipError_t e = launch_decode_gdn(class_args(P, a, order, 0, 1), true, st);

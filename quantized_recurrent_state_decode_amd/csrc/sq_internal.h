@@ -9,6 +9,17 @@
 
 #include "stepq.h"
 
+// Host-side bounds asserts of the checked build (-DSQ_HOSTCHECK): the plan's
+// byte layout, the device-table image and the launch arguments each kernel
+// grid relies on.  A failed check prints the condition and aborts; in the
+// normal build the checks compile to nothing.
+#ifdef SQ_HOSTCHECK
+[[noreturn]] void sq_check_failed(const char* cond, const char* file, int line);
+#define SQ_CHECK(c) ((c) ? (void)0 : sq_check_failed(#c, __FILE__, __LINE__))
+#else
+#define SQ_CHECK(c) ((void)0)
+#endif
+
 // Device view of a plan: pointers into the caller-owned device table buffer.
 struct DevPlan {
   int mode, kind, H, dk, dv, ubits, p;
