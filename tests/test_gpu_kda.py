@@ -130,3 +130,49 @@ def test_full_size_kda_sampled():
     rep = _compare_steps(pool, w2, slots, 1, sample)
     print("adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
     rep.assert_ok()
+
+
+@pytest.mark.parametrize("shape", [(128, 128), (64, 128)])
+def test_kda_single_width_blocks(shape):
+    """Heads whose sorted rows fill whole 32-row blocks of one width (4 or 8
+    bits, the blocks with their own read and code passes) beside mixed blocks,
+    a 6-bit-only block and FP16 rows; all tiles teacher-forced on four steps,
+    the last with a saturated value column (those blocks then take the
+    clamping code pass after their own read)."""
+    import torch
+    dk, dv = shape
+    rng = np.random.default_rng(90 + dk)
+    runs = {128: [[(4, 64), (8, 64)], [(4, 40), (6, 56), (8, 32)], [(2, 8), (4, 24), (8, 93), (16, 3)]],
+            64: [[(4, 32), (8, 32)], [(8, 32), (6, 32)], [(4, 30), (16, 2), (8, 32)]]}[dk]
+    H = len(runs)
+    bits = np.concatenate([rng.permutation(np.concatenate([np.full(n, b) for b, n in head]))
+                           for head in runs]).astype(np.int32)
+    assert bits.size == H * dk
+    w8 = C.impact_factors(rng.lognormal(0.0, 1.5, (H, dk))).astype(np.float32)
+    plan = sq.sq_plan_create_step(sq.SQ_KIND_KDA, H, dk, dv, bits, w8)
+    w = SI.workload("kda_step6", batch=4, n_slots=5, heads=H, d_k=dk, d_v=dv, steps=4)
+    pool = Pool(plan, 5)
+    slots = SI.slot_ids(w)
+    pool.pack(to_dev(slots), to_dev(oracle_warmup(w, 24).astype(np.float32)), w.batch)
+    tiles = [(b, h) for b in range(w.batch) for h in range(H)]
+    rep = _compare_steps(pool, w, slots, 3, tiles)
+    print("adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
+    rep.assert_ok()
+    # a fourth step with a saturated value column on batch row 0
+    desc = oracle_desc(pool.desc)
+    inp = {k: v.copy() for k, v in SI.step_inputs(w, 3, SI.gate_params(w)).items()}
+    inp["v"][0, :, 7] = 4.0e9
+    sdev = to_dev(slots.astype(np.int32))
+    y = torch.empty((w.batch, H, dv), dtype=torch.float32, device="cuda")
+    before = {b: pool.slot_bytes_of(int(slots[b])) for b, _ in tiles}
+    pool.decode(sdev, w.batch, inputs_dev(inp), y)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    rep = Report()
+    for b, h in tiles:
+        check_decode_head(f"saturated b {b} h {h}", desc, h, pool.head_bytes(before[b], h),
+                          pool.head_bytes(pool.slot_bytes_of(int(slots[b])), h),
+                          head_inputs(inp, b, h), yh[b, h].astype(np.float64),
+                          pool.desc["w"][h].astype(np.float64), rep)
+    print("saturated step: adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
+    rep.assert_ok()
