@@ -11,8 +11,11 @@
 // and the head is copied out with 16-byte stores.  Because the rows are
 // sorted, the rows of one block that share a width are consecutive: the block
 // keeps one bit mask per width class and the byte offset of the class's first
-// row, so a row's width and offset are scalar values and every per-row branch
-// is a scalar branch to code specialised for that width.  Per-row inputs
+// row, so a row's width and offset are scalar values.  On 64-lane blocks the
+// reads take each row's address and width from a row table (arithmetic on
+// the width, no branch), a block of a single 4- or 8-bit width has read and
+// code passes of its own, and elsewhere the per-row branch of the code pass is
+// a scalar branch to code specialised for that width.  Per-row inputs
 // (d, k, q, w) are gathered through the storage permutation.  Per element,
 // with rho_s the row's retained dequantisation factor (d_s r_s / q_b on
 // integer rows, d_s on FP16 rows):

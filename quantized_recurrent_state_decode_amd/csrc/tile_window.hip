@@ -29,9 +29,11 @@
 // The window position is read first; the boundary, the token's inputs and
 // then the records and pairs held (16-byte loads into registers, a fixed
 // count per thread) all go out before any of them is waited on, and the
-// records are committed to LDS together.  Record dot products run one lane
-// per record over the wave's own rows; the rebuild at a flush reads the
-// records from LDS.
+// records are committed to LDS together.  Record and compensator dot
+// products over the wave's own rows take 16 or 32 lanes per set of units,
+// with the rows split into segments over the remaining lanes; the decay
+// suffix products come from a log-step scan over one wave's lanes, and the
+// rebuild at a flush reads the records from LDS.
 #include "tile_common.h"
 
 using namespace sqk;
