@@ -446,8 +446,14 @@ def main():
     cache.clear()
     torch.cuda.empty_cache()
     if host is not None:
-        out["cpu_baseline"] = cpu_baseline(w, desc, host, w.batch, 2, args.cpu_seconds,
-                                           args.cpu_single_seconds)
+        cb = cpu_baseline(w, desc, host, w.batch, 2, args.cpu_seconds, args.cpu_single_seconds)
+        if cb.get("value"):
+            # the same algorithmic bytes per step, and the GPU line over it
+            cb["equivalent_gbs"] = cb["value"] * abytes / 1e9
+            cb["gpu_over_cpu"] = out["value"] / cb["value"]
+        if isinstance(cb.get("single_core"), dict) and cb["single_core"].get("value"):
+            cb["single_core"]["equivalent_gbs"] = cb["single_core"]["value"] * abytes / 1e9
+        out["cpu_baseline"] = cb
     print(json.dumps(out))
 
 
