@@ -132,11 +132,16 @@ def adopt_fp16(pre, ora, gpu, clamp=True, abs_tol=0.0):
 
 
 def adopt_codes(pre, ora, gpu, tie=None):
-    """tie: per-element half-integer window in code units (default 1e-3)."""
+    """tie: per-element bound (code units, default 1e-3) on how far the GPU's
+    unrounded code may lie from the oracle's `pre`.  A GPU code is accepted if
+    it is a rounding of some value in that window, |gpu - pre| <= 1/2 + tie:
+    the oracle's own code, or, when `pre` lies within the window of a
+    half-integer, its neighbour across it (and, where the window exceeds half a
+    code, e.g. on a residual at the level of its own float32 error, any code
+    the window reaches)."""
     d = gpu - ora
-    frac = np.abs(np.abs(pre - np.floor(pre)) - 0.5)
     win = CODE_TIE if tie is None else np.maximum(CODE_TIE, tie)
-    ok = (d == 0) | ((np.abs(d) == 1) & (frac <= win))
+    ok = (d == 0) | (np.abs(gpu - pre) <= 0.5 + win)
     return np.where(ok, gpu, ora), int(((d != 0) & ok).sum()), ~ok
 
 
@@ -269,17 +274,29 @@ def check_window_quant(where, S, gpu, rep: Report, c_floor=Q.WINDOW_C_FLOOR, dR=
     rep.bad(where, "window codes", bad)
 
 
-def comp_adopter(where, gpu: dict, iters: int, dim: int, rep: Report):
+def comp_adopter(where, gpu: dict, iters: int, dim: int, rep: Report, noise: float = 0.0):
     """Teacher-forced check of the compensator pairs (LeapQuant notes Sec. 2.4):
     the GPU's stored FP16 pair h must be the oracle's binary16 rounding of its
     float64 fit, or a correct rounding of a value within the float32 error of
     the fit, taken as (2 iters + 1) dim 2^-24 of the pair vector's norm (each
     iteration is two dim-term sums, plus the final scaling).  The GPU's pair
     is adopted either way, so the residual and the next pairs follow the
-    stored values."""
+    stored values.
+
+    `noise` is the float32 error of the rebuilt state being fitted (Frobenius
+    norm).  A pair whose weight |k| |u| lies below it in both fits fits only
+    that error (a rank-deficient state, e.g. a zero gate at the window's last
+    token), so its direction is not unique: it is accepted when the GPU's pair
+    is as small, and adopted."""
     tau = (2 * iters + 1) * dim * 2.0 ** -24
 
     def adopt(h, k, u):
+        gk = np.asarray(gpu["Kc"][h], dtype=np.float64)
+        gu = np.asarray(gpu["Uc"][h], dtype=np.float64)
+        if (noise > 0.0 and np.linalg.norm(k) * np.linalg.norm(u) <= noise
+                and np.linalg.norm(gk) * np.linalg.norm(gu) <= noise):
+            rep.add("comp_noise_level", 1)
+            return gk.copy(), gu.copy()
         out = []
         for raw, g, name in ((k, gpu["Kc"][h], "Kc"), (u, gpu["Uc"][h], "Uc")):
             own = W.fp16_value(raw)
@@ -303,7 +320,23 @@ def check_decode_head(where, desc, h, before: bytes, after: bytes, inp: dict, y_
     mode = desc["mode"]
     if mode == "window":
         rank, iters = int(desc.get("rank", 0)), int(desc.get("iters", 0))
-        adopt = comp_adopter(where, st1, iters, max(d_k, desc["d_v"]), rep) if rank else None
+        adopt = None
+        if rank:
+            # float32 error of the rebuild that the pairs are fitted to: the
+            # flush check's elementwise bound 2 (2p + 2r + 6) 2^-24 per unit of
+            # the terms' magnitudes, here on a norm bound of those terms
+            p = int(desc["p"])
+            a_, b_ = abs(float(inp["gate"])), abs(float(inp["beta"]))
+            held = int(st0["ell"])
+            mag = (np.linalg.norm(W.boundary_residual(st0))
+                   + sum(np.linalg.norm(st0["kt"][j]) * np.linalg.norm(st0["u"][j])
+                         for j in range(held))
+                   + sum(np.linalg.norm(st0["Kc"][h_]) * np.linalg.norm(st0["Uc"][h_])
+                         for h_ in range(rank)))
+            nk = np.linalg.norm(inp["k"])
+            scale = a_ * mag + b_ * nk * (np.linalg.norm(inp["v"]) + a_ * mag * nk)
+            noise = 2 * (2 * p + 2 * rank + 6) * 2.0 ** -24 * scale
+            adopt = comp_adopter(where, st1, iters, max(d_k, desc["d_v"]), rep, noise=noise)
         r = W.window_step(st0, inp["q"], inp["k"], inp["v"], float(inp["beta"]),
                           float(inp["gate"]), int(desc["p"]), iters, adopt=adopt)
         rep.y(where, y_gpu, r["o"])

@@ -16,7 +16,7 @@ from parity import (Report, check_decode_head, check_quantized_head, check_windo
 pytestmark = pytest.mark.gpu
 
 
-def _run(pool, w, slots, steps, tiles=None, compare=None):
+def _run(pool, w, slots, steps, tiles=None, compare=None, edit=None):
     import torch
     desc = oracle_desc(pool.desc)
     sdev = to_dev(slots.astype(np.int32))
@@ -26,6 +26,9 @@ def _run(pool, w, slots, steps, tiles=None, compare=None):
     rep = Report()
     for t in range(steps):
         inp = SI.step_inputs(w, t, params)
+        if edit is not None:
+            inp = {k: v.copy() for k, v in inp.items()}
+            edit(t, inp)
         cmp = compare is None or t in compare
         before = {b: pool.slot_bytes_of(int(slots[b])) for b, _ in tiles} if cmp else None
         pool.decode(sdev, w.batch, inputs_dev(inp), y)
@@ -158,5 +161,33 @@ def test_full_size_window_sampled(rank):
     rng = np.random.default_rng(5)
     tiles = [(int(b), int(h)) for b, h in zip(rng.choice(w.batch, 16), rng.choice(32, 16))]
     rep = _run(pool, w, slots, 20, tiles=tiles, compare={15, 19})
+    print("adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
+    rep.assert_ok()
+
+
+@pytest.mark.parametrize("rank", [0, 1])
+def test_window_zero_gate_and_beta(rank):
+    """Tokens with alpha = 0 (the boundary and every earlier record vanish from
+    S, LeapQuant notes Sec. 2.3, Eq. 4 with a zero decay factor) and tokens
+    with beta = 0 (no write), including the token that fills a window and so
+    triggers the rebuild; all tiles teacher-forced.  A zero gate leaves the
+    rebuilt state of rank one or two, so with one pair the residual is at the
+    level of its own float32 error (its codes are then checked within that
+    bound).  More pairs would be fitted to the near-degenerate rounding
+    residual of the first, whose directions are not unique."""
+    p = 4
+    w = SI.workload("gdn_window16", batch=3, n_slots=4, heads=2, window=p, steps=10)
+    pool = Pool(_plan(2, 128, 128, p, rank, 3), 4)
+    slots = SI.slot_ids(w)
+    pool.pack(to_dev(slots), to_dev(oracle_warmup(w, 16).astype(np.float32)), w.batch)
+
+    def edit(t, inp):
+        if t in (1, 3, 6):            # token 3 fills the first window
+            inp["gate"][0, :] = 0.0
+            inp["gate"][2, 1] = 0.0
+        if t in (2, 3, 7):
+            inp["beta"][1, :] = 0.0
+
+    rep = _run(pool, w, slots, w.steps, edit=edit)
     print("adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
     rep.assert_ok()
