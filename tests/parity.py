@@ -396,10 +396,18 @@ def check_window_encode(where, desc, S, gpu: dict, rep: Report, init=None):
     pair fit (started from `init`, the head's previous pairs, or the all-ones
     vector) comes first and the residual is what is quantized."""
     rank, iters = int(desc.get("rank", 0)), int(desc.get("iters", 0))
+    dR = None
     if rank:
-        adopt = comp_adopter(where, gpu, iters, max(desc["d_k"], desc["d_v"]), rep)
-        S = W.encode_boundary(S, rank, iters, init, adopt=adopt)["R"]
-    check_window_quant(where, S, gpu, rep)
+        # the state the pairs are fitted to is exact here; the kernel forms the
+        # residual S - sum_h kc_h uc_h^T with `rank` fp32 multiply-adds per
+        # element, hence at most 2 rank 2^-24 of |S| + sum_h |kc_h| |uc_h|^T
+        noise = 2 * (2 * rank + 2) * 2.0 ** -24 * np.linalg.norm(S)
+        adopt = comp_adopter(where, gpu, iters, max(desc["d_k"], desc["d_v"]), rep, noise=noise)
+        enc = W.encode_boundary(S, rank, iters, init, adopt=adopt)
+        mag = np.abs(S) + np.abs(enc["Kc"]).T @ np.abs(enc["Uc"])
+        dR = 2 * rank * 2.0 ** -24 * mag
+        S = enc["R"]
+    check_window_quant(where, S, gpu, rep, dR=dR)
 
 
 def check_quantized_head(where, desc, h, X, packed: bytes, w, rep: Report):

@@ -100,7 +100,7 @@ def test_empty_batch_is_a_noop(mode):
     assert np.array_equal(pool.pool.cpu().numpy(), snap)
 
 
-@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("kind", ["gdn", "kda", "uniform", "window", "window_r2"])
 def test_zero_tiles_quantize(kind):
     """All-zero tiles: m_i = 0, so r_i and c0_j clamp to 2^-14, every code is
     0, D_j = 0 keeps c_j = c0_j, and FP16 pivot units store zeros; checked
@@ -111,9 +111,15 @@ def test_zero_tiles_quantize(kind):
     wts = C.impact_factors(rng.lognormal(0, 1.5, (H, d))).astype(np.float32)
     if kind == "gdn":
         plan = sq.sq_plan_create_step(sq.SQ_KIND_GDN, H, d, d, [4, 16, 8], wts)
-    else:
+    elif kind == "kda":
         plan = _kda_plan(rng, H, d)
         wts = sq.sq_plan_query(plan)["w"].astype(np.float32)
+    elif kind == "uniform":       # every row scale clamps to 2^-14, every code 0
+        plan = sq.sq_plan_create_uniform(H, d, d, 8)
+    elif kind == "window":        # C at its floor, B_j = 0 and column codes 0
+        plan = sq.sq_plan_create_window(H, d, d, 16)
+    else:                         # and the pair fit of a zero state gives zero pairs
+        plan = sq.sq_plan_create_window_lowrank(H, d, d, 16, 2, 3)
     pool = Pool(plan, 2)
     desc = oracle_desc(pool.desc)
     X = np.zeros((n, d, d), dtype=np.float32)
