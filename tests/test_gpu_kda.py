@@ -176,3 +176,55 @@ def test_kda_single_width_blocks(shape):
                           pool.desc["w"][h].astype(np.float64), rep)
     print("saturated step: adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
     rep.assert_ok()
+
+
+@pytest.mark.parametrize("shape", [(128, 128), (64, 128), (128, 64)])
+def test_kda_extreme_heads(shape):
+    """Heads at the extremes of the row widths: every row FP16 (the largest
+    head, staged in more than one round at 128 x 128), every row 8 bits,
+    every row 2 bits, and a head with a single integer row among FP16 rows;
+    decode teacher-forced on three steps, then quantize-only and unpack."""
+    import torch
+    dk, dv = shape
+    rng = np.random.default_rng(120 + dk + dv)
+    one_int = np.full(dk, 16)
+    one_int[dk // 2] = 4
+    bits = np.concatenate([np.full(dk, 16), np.full(dk, 8), np.full(dk, 2), one_int]).astype(np.int32)
+    H = 4
+    w8 = C.impact_factors(rng.lognormal(0.0, 1.5, (H, dk))).astype(np.float32)
+    plan = sq.sq_plan_create_step(sq.SQ_KIND_KDA, H, dk, dv, bits, w8)
+    w = SI.workload("kda_step6", batch=3, n_slots=4, heads=H, d_k=dk, d_v=dv, steps=3)
+    pool = Pool(plan, 4)
+    slots = SI.slot_ids(w)
+    pool.pack(to_dev(slots), to_dev(oracle_warmup(w, 16).astype(np.float32)), w.batch)
+    rep = _compare_steps(pool, w, slots, w.steps, [(b, h) for b in range(w.batch) for h in range(H)])
+    print("decode adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
+    rep.assert_ok()
+    # quantize-only of fresh tiles, and unpack of the pool against the oracle's dequantisation
+    desc = oracle_desc(pool.desc)
+    n = 8
+    X = (rng.standard_normal((n, dk, dv)) * rng.lognormal(0, 1.0, (n, dk, 1))).astype(np.float32)
+    heads = (np.arange(n) % H).astype(np.int32)
+    mhb = sq.sq_max_head_bytes(plan)
+    out = torch.zeros(n * mhb, dtype=torch.uint8, device="cuda")
+    sq.sq_quantize_tiles(plan, pool.dev_plan, to_dev(X), n, to_dev(heads), out)
+    torch.cuda.synchronize()
+    ob = out.cpu().numpy().tobytes()
+    rep = Report()
+    wq = pool.desc["w"]
+    for t in range(n):
+        h = int(heads[t])
+        check_quantized_head(f"tile {t}", desc, h, X[t].astype(np.float64),
+                             ob[t * mhb:(t + 1) * mhb], wq[h].astype(np.float64), rep)
+    print("quantize adoptions", dict(rep.count))
+    rep.assert_ok()
+    S_out = torch.empty((w.batch, H, dk, dv), dtype=torch.float32, device="cuda")
+    sq.sq_pool_unpack(plan, pool.dev_plan, pool.pool, 4, to_dev(slots.astype(np.int32)), w.batch,
+                      S_out)
+    torch.cuda.synchronize()
+    Sh = S_out.cpu().numpy()
+    for b in range(w.batch):
+        sb = pool.slot_bytes_of(int(slots[b]))
+        for h in range(H):
+            np.testing.assert_allclose(Sh[b, h], dequant_head(desc, h, pool.head_bytes(sb, h)),
+                                       rtol=1e-6, atol=1e-30)
