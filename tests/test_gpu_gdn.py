@@ -425,3 +425,49 @@ def test_full_size_fp32_dense_kda_sampled():
         got = S[int(slots[b]), h].cpu().numpy()
         assert np.linalg.norm(got - ref[0]) <= 1e-5 * np.linalg.norm(ref[0]), (b, h)
         assert np.linalg.norm(yh[b, h] - yr[0]) <= 1e-5 * np.linalg.norm(yr[0]), (b, h)
+
+
+@pytest.mark.parametrize("case", ["one_width", "all_pivots", "split_fallback"])
+def test_step_gdn_dispatch_paths(case):
+    """The decode launch shapes a STEP GDN plan can take, teacher-forced:
+    a plan of one width (its width-specialised kernel alone), a plan of FP16
+    pivot heads only, and a plan whose largest class fills the chip many times
+    over while the other classes' leading rows would exceed the grid's row
+    limit (B + leading rows > 65535), which decodes the largest class alone
+    and then the others in one merged launch."""
+    import torch
+    rng = np.random.default_rng(150)
+    if case == "one_width":
+        bits, B = [4] * 6, 7
+    elif case == "all_pivots":
+        bits, B = [16] * 3, 5
+    else:
+        bits, B = [4, 2, 6, 8, 16], 16384   # one head per class: 4 leading rows per batch row
+    H = len(bits)
+    w = SI.workload("gdn_mid_step6", batch=B, n_slots=B, heads=H, steps=1)
+    plan = sq.sq_plan_create_step(sq.SQ_KIND_GDN, H, 128, 128, bits, _impact(rng, H, 128))
+    pool = Pool(plan, B)
+    slots = SI.slot_ids(w)
+    S4 = oracle_warmup(SI.workload("gdn_mid_step6", batch=4, n_slots=4, heads=H), 16)
+    S = to_dev(S4.astype(np.float32)).repeat(-(-B // 4), 1, 1, 1)[:B].contiguous()
+    sdev = to_dev(slots.astype(np.int32))
+    pool.pack(sdev, S, B)
+    del S
+    torch.cuda.empty_cache()
+    tiles = [(b, h) for b in sorted({0, 1, B // 2, B - 1}) for h in range(H)]
+    desc = oracle_desc(pool.desc)
+    inp = SI.step_inputs(w, 0, SI.gate_params(w))
+    y = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    before = {b: pool.slot_bytes_of(int(slots[b])) for b, _ in tiles}
+    pool.decode(sdev, B, inputs_dev(inp), y)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    rep = Report()
+    for b, h in tiles:
+        check_decode_head(f"{case} b {b} h {h}", desc, h, pool.head_bytes(before[b], h),
+                          pool.head_bytes(pool.slot_bytes_of(int(slots[b])), h),
+                          head_inputs(inp, b, h), yh[b, h].astype(np.float64),
+                          pool.desc["w"][h].astype(np.float64), rep)
+    print(case, "adoptions", dict(rep.count), "max y rel", rep.max_y_rel)
+    rep.assert_ok()
+    assert np.all(np.isfinite(yh))
