@@ -30,7 +30,7 @@ EXPORTED = (
     "sq_plan_create_window", "sq_plan_create_window_lowrank", "sq_plan_query", "sq_plan_destroy", "sq_plan_device_bytes",
     "sq_plan_upload", "sq_pool_bytes", "sq_pool_init", "sq_pool_pack", "sq_pool_unpack",
     "sq_decode_step", "sq_window_flush", "sq_quantize_tiles", "sq_max_head_bytes",
-    "sq_dense_step", "sq_prefill_chunk", "sq_calib_gate_stats", "sq_impact_factors", "sq_calib_distortion",
+    "sq_dense_step", "sq_prefill_chunk", "sq_prefill_chunkwise", "sq_calib_gate_stats", "sq_impact_factors", "sq_calib_distortion",
     "sq_calib_distortion_noalloc", "sq_last_error",
 )
 
@@ -109,6 +109,8 @@ def lib() -> ctypes.CDLL:
                               _P, _P, _P],
             "sq_prefill_chunk": [_I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                                  _P],
+            "sq_prefill_chunkwise": [_I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                                     _P, _P],
             "sq_calib_gate_stats": [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P],
             "sq_impact_factors": [_I32, _I32, _P, ctypes.c_double, ctypes.c_double, _P],
             "sq_calib_distortion": [_P, _P, _I32, _P, _P, _I32, _P, _P],
@@ -313,6 +315,14 @@ def sq_prefill_chunk(kind, heads, d_k, d_v, batch, T, S, q, k, v, beta, gate, y,
     _check(lib().sq_prefill_chunk(kind, heads, d_k, d_v, batch, T, _ptr(S, f), _ptr(q, f),
                                   _ptr(k, f), _ptr(v, f), _ptr(beta, f), _ptr(gate, f),
                                   _ptr(y, f), _stream(stream)))
+
+
+def sq_prefill_chunkwise(kind, heads, d_k, d_v, batch, T, S, q, k, v, beta, gate, y,
+                         stream=None) -> None:
+    f = _f32()
+    _check(lib().sq_prefill_chunkwise(kind, heads, d_k, d_v, batch, T, _ptr(S, f), _ptr(q, f),
+                                      _ptr(k, f), _ptr(v, f), _ptr(beta, f), _ptr(gate, f),
+                                      _ptr(y, f), _stream(stream)))
 
 
 def sq_calib_gate_stats(kind, heads, d_k, n, q, k, beta, gate, log_sum, omega_sum,

@@ -781,19 +781,51 @@ extern "C" sq_status sq_calib_distortion_noalloc(const sq_plan* P, const void* d
   return sq_calib_distortion(P, dev_plan, n, S, ptr, per_row, dist_sum, st);
 }
 
+namespace {
+// Shared argument checks of the two prefill forms; 1 = nothing to do.
+sq_status prefill_args(const char* name, int32_t kind, int32_t H, int32_t dk, int32_t dv,
+                       int32_t B, int32_t T, const float* S, const float* q, const float* k,
+                       const float* v, const float* beta, const float* gate, const float* y,
+                       bool* empty) {
+  *empty = false;
+  if (kind != SQ_KIND_GDN && kind != SQ_KIND_KDA) return fail(SQ_EINVAL, "bad kind %d", kind);
+  sq_status s = check_dims(H, dk, dv);
+  if (s) return s;
+  if (B < 0 || T < 0) return fail(SQ_EINVAL, "bad arguments to %s", name);
+  if (B == 0 || T == 0) {  // the arrays may be null
+    *empty = true;
+    return ok();
+  }
+  if (!S || !q || !k || !v || !beta || !gate || !y) return fail(SQ_EINVAL, "bad arguments to %s", name);
+  if ((long long)B * H > 0x7fffffffLL)  // one workgroup per (sequence, head)
+    return fail(SQ_EINVAL, "%s: batch x heads must stay below 2^31", name);
+  return ok();
+}
+}  // namespace
+
 extern "C" sq_status sq_prefill_chunk(int32_t kind, int32_t H, int32_t dk, int32_t dv,
                                       int32_t B, int32_t T, float* S, const float* q,
                                       const float* k, const float* v, const float* beta,
                                       const float* gate, float* y, hipStream_t st) {
-  if (kind != SQ_KIND_GDN && kind != SQ_KIND_KDA) return fail(SQ_EINVAL, "bad kind %d", kind);
-  sq_status s = check_dims(H, dk, dv);
-  if (s) return s;
-  if (B < 0 || T < 0) return fail(SQ_EINVAL, "bad arguments to sq_prefill_chunk");
-  if (B == 0 || T == 0) return ok();  // the arrays may be null
-  if (!S || !q || !k || !v || !beta || !gate || !y)
-    return fail(SQ_EINVAL, "bad arguments to sq_prefill_chunk");
+  bool empty;
+  sq_status s = prefill_args("sq_prefill_chunk", kind, H, dk, dv, B, T, S, q, k, v, beta, gate, y,
+                             &empty);
+  if (s || empty) return s;
   hipError_t e = launch_prefill_chunk(kind, H, dk, dv, B, T, S, q, k, v, beta, gate, y, st);
   if (e != hipSuccess) return hip_fail(e, "launching prefill chunk");
+  return ok();
+}
+
+extern "C" sq_status sq_prefill_chunkwise(int32_t kind, int32_t H, int32_t dk, int32_t dv,
+                                          int32_t B, int32_t T, float* S, const float* q,
+                                          const float* k, const float* v, const float* beta,
+                                          const float* gate, float* y, hipStream_t st) {
+  bool empty;
+  sq_status s = prefill_args("sq_prefill_chunkwise", kind, H, dk, dv, B, T, S, q, k, v, beta,
+                             gate, y, &empty);
+  if (s || empty) return s;
+  hipError_t e = launch_prefill_chunkwise(kind, H, dk, dv, B, T, S, q, k, v, beta, gate, y, st);
+  if (e != hipSuccess) return hip_fail(e, "launching chunkwise prefill");
   return ok();
 }
 

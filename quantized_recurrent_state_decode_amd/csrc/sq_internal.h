@@ -105,6 +105,9 @@ hipError_t launch_calib_dist(const DevPlan& P, int n_tiles, const unsigned char*
 hipError_t launch_prefill_chunk(int kind, int H, int dk, int dv, int B, int T, float* S,
                                 const float* q, const float* k, const float* v, const float* beta,
                                 const float* gate, float* y, hipStream_t s);
+hipError_t launch_prefill_chunkwise(int kind, int H, int dk, int dv, int B, int T, float* S,
+                                    const float* q, const float* k, const float* v,
+                                    const float* beta, const float* gate, float* y, hipStream_t s);
 hipError_t launch_dense_step(int kind, int H, int dk, int dv, float* S, long long n_slots,
                              const int* slots, int B, const float* q, const float* k,
                              const float* v, const float* beta, const float* gate, float* y,

@@ -86,6 +86,15 @@ hipError_t launch_prefill_chunk(int kind, int H, int dk, int dv, int B, int T, f
   return hipErrorNoDevice;
 }
 
+hipError_t launch_prefill_chunkwise(int kind, int H, int dk, int dv, int B, int T, float* S,
+                                    const float* q, const float* k, const float* v,
+                                    const float* beta, const float* gate, float* y, hipStream_t) {
+  SQ_CHECK((kind == SQ_KIND_GDN || kind == SQ_KIND_KDA) && H > 0 && B > 0 && T > 0);
+  SQ_CHECK((dk == 64 || dk == 128) && (dv == 64 || dv == 128));
+  SQ_CHECK(S && q && k && v && beta && gate && y);
+  return hipErrorNoDevice;
+}
+
 hipError_t launch_dense_step(int kind, int H, int dk, int dv, float* S, long long n_slots,
                              const int* slots, int B, const float* q, const float* k,
                              const float* v, const float* beta, const float* gate, float* y,

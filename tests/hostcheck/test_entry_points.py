@@ -95,3 +95,5 @@ def test_dense_and_prefill_reach_their_launch(kind):
               STREAM)
         _ehip(sq.sq_prefill_chunk, kind, 4, d_k, d_v, 3, 17, DEV, DEV, DEV, DEV, DEV, DEV, DEV,
               STREAM)
+        _ehip(sq.sq_prefill_chunkwise, kind, 4, d_k, d_v, 3, 17, DEV, DEV, DEV, DEV, DEV, DEV,
+              DEV, STREAM)

@@ -243,6 +243,15 @@ def test_error_codes():
     assert lib.sq_pool_unpack(p, 1, 1, 1, None, 0, None, None) == sq.SQ_OK
     assert lib.sq_quantize_tiles(p, 1, None, 0, None, None, None) == sq.SQ_OK
     assert lib.sq_quantize_tiles(p, 1, None, 2, None, None, None) == sq.SQ_EINVAL
+    # both prefill forms: checked before any HIP call, T = 0 or batch 0 is a no-op
+    for fn in (lib.sq_prefill_chunk, lib.sq_prefill_chunkwise):
+        assert fn(2, 1, 64, 64, 1, 1, 1, 1, 1, 1, 1, 1, 1, None) == sq.SQ_EINVAL
+        assert fn(0, 1, 96, 64, 1, 1, 1, 1, 1, 1, 1, 1, 1, None) == sq.SQ_EUNSUPPORTED
+        assert fn(1, 1, 64, 64, 1, -1, 1, 1, 1, 1, 1, 1, 1, None) == sq.SQ_EINVAL
+        assert fn(0, 1, 64, 64, 1, 0, None, None, None, None, None, None, None, None) == sq.SQ_OK
+        assert fn(0, 1, 64, 64, 0, 5, None, None, None, None, None, None, None, None) == sq.SQ_OK
+        assert fn(0, 1, 64, 64, 1, 5, 1, 1, 1, None, 1, 1, 1, None) == sq.SQ_EINVAL
+        assert fn(0, 2, 64, 64, 2 ** 30, 5, 1, 1, 1, 1, 1, 1, 1, None) == sq.SQ_EINVAL
     # the plan, device tables and pool are still required
     assert lib.sq_decode_step(p, None, 1, 1, None, 0, None, None, None, None, None, None,
                               None) == sq.SQ_EINVAL

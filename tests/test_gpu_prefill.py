@@ -40,26 +40,96 @@ def _rel(a, b, axis):
     return np.linalg.norm(a - b, axis=axis) / np.maximum(np.linalg.norm(b, axis=axis), 1e-300)
 
 
+FORMS = {"serial": "sq_prefill_chunk", "chunkwise": "sq_prefill_chunkwise"}
+
+
+def _run(form, kind, H, dk, dv, B, T, S0, x):
+    """One call of the given prefill form on device copies; returns (y, S)."""
+    import torch
+    S = to_dev(np.ascontiguousarray(S0, dtype=np.float32))
+    y = torch.full((B, T, H, dv), float("nan"), dtype=torch.float32, device="cuda")
+    d = {k: to_dev(np.ascontiguousarray(v, dtype=np.float32)) for k, v in x.items()}
+    getattr(sq, FORMS[form])(sq.SQ_KIND_GDN if kind == "gdn" else sq.SQ_KIND_KDA, H, dk, dv, B, T,
+                             S, d["q"], d["k"], d["v"], d["beta"], d["gate"], y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), S.cpu().numpy()
+
+
+# T spans one token, a ragged single block, whole blocks of 32 and ragged
+# multi-block tails for the chunkwise form
+@pytest.mark.parametrize("form", list(FORMS))
 @pytest.mark.parametrize("kind,shape,T", [("gdn", (128, 128), 1), ("gdn", (128, 128), 130),
                                           ("kda", (128, 128), 37), ("gdn", (64, 64), 5),
-                                          ("kda", (128, 64), 64), ("gdn", (64, 128), 9)])
-def test_prefill_chunk_matches_recurrence(kind, shape, T):
-    import torch
+                                          ("kda", (128, 64), 64), ("gdn", (64, 128), 9),
+                                          ("kda", (64, 64), 97), ("gdn", (128, 64), 32),
+                                          ("kda", (64, 128), 33), ("kda", (128, 128), 160)])
+def test_prefill_chunk_matches_recurrence(form, kind, shape, T):
     dk, dv = shape
     w = SI.workload("gdn_mid_step6" if kind == "gdn" else "kda_step6", batch=3, n_slots=3,
                     heads=2, d_k=dk, d_v=dv)
     params = SI.gate_params(w)
     S0 = oracle_warmup(w, 12)
     x = _chunk(w, T, params)
-    S = to_dev(S0.astype(np.float32))
-    y = torch.empty((3, T, 2, dv), dtype=torch.float32, device="cuda")
-    d = {k: to_dev(v) for k, v in x.items()}
-    sq.sq_prefill_chunk(sq.SQ_KIND_GDN if kind == "gdn" else sq.SQ_KIND_KDA, 2, dk, dv, 3, T, S,
-                        d["q"], d["k"], d["v"], d["beta"], d["gate"], y)
-    torch.cuda.synchronize()
+    y, S = _run(form, kind, 2, dk, dv, 3, T, S0, x)
     y_ref, S_ref = _oracle(S0.astype(np.float32), x, kind, dk)
-    assert _rel(y.cpu().numpy(), y_ref, -1).max() <= Y_REL
-    assert _rel(S.cpu().numpy().reshape(6, -1), S_ref.reshape(6, -1), -1).max() <= Y_REL
+    assert _rel(y, y_ref, -1).max() <= Y_REL
+    assert _rel(S.reshape(6, -1), S_ref.reshape(6, -1), -1).max() <= Y_REL
+
+
+@pytest.mark.parametrize("form", list(FORMS))
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_prefill_degenerate_gates(form, kind):
+    """Gates of exactly 0 and 1 and write strengths of 0 and 1 inside one
+    sequence: a zero gate erases the state (every decay product across it is
+    0, with no division), beta = 0 leaves the token out, beta = 1 with a unit
+    key overwrites the key's direction."""
+    rng = np.random.default_rng(5)
+    dk = dv = 128
+    B, H, T = 2, 3, 75
+    w = SI.workload("gdn_mid_step6" if kind == "gdn" else "kda_step6", batch=B, n_slots=B,
+                    heads=H, d_k=dk, d_v=dv)
+    S0 = oracle_warmup(w, 8)
+    x = _chunk(w, T, SI.gate_params(w))
+    for t, val in ((3, 0.0), (40, 1.0), (64, 0.0)):      # whole-token gates
+        x["gate"][:, t] = val
+    x["beta"][:, 10] = 0.0
+    x["beta"][:, 50] = 1.0
+    if kind == "kda":                                    # single channels at 0 and 1
+        x["gate"][0, 20, 1, rng.integers(0, dk, 9)] = 0.0
+        x["gate"][1, 70, 2, rng.integers(0, dk, 9)] = 1.0
+    y, S = _run(form, kind, H, dk, dv, B, T, S0, x)
+    y_ref, S_ref = _oracle(S0.astype(np.float32), x, kind, dk)
+    assert np.isfinite(y).all() and np.isfinite(S).all()
+    assert _rel(y, y_ref, -1).max() <= Y_REL
+    assert _rel(S.reshape(B * H, -1), S_ref.reshape(B * H, -1), -1).max() <= Y_REL
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_chunkwise_prefill_at_bench_size(kind):
+    """The launch bench.py times for --prefill 256 (64 sequences x 16 heads
+    for GDN, 256 x 32 for KDA, d = 128): sampled (sequence, head) tiles
+    against the float64 recurrence over all 256 tokens, every tile against
+    the serial form."""
+    import torch
+    T = 256
+    w = SI.workload("gdn_mid_step6" if kind == "gdn" else "kda_step6")
+    B, H, dk, dv = w.batch, w.heads, w.d_k, w.d_v
+    rng = np.random.default_rng(17)
+    S0 = (rng.standard_normal((B, H, dk, dv)) * 0.05).astype(np.float32)
+    x = _chunk(w, T, SI.gate_params(w))
+    y_c, S_c = _run("chunkwise", kind, H, dk, dv, B, T, S0, x)
+    y_s, S_s = _run("serial", kind, H, dk, dv, B, T, S0, x)
+    torch.cuda.empty_cache()
+    assert np.isfinite(y_c).all() and np.isfinite(S_c).all()
+    # every tile: the two forms agree to the fp32 bar
+    assert _rel(y_c, y_s, -1).max() <= 2 * Y_REL
+    assert _rel(S_c.reshape(B * H, -1), S_s.reshape(B * H, -1), -1).max() <= 2 * Y_REL
+    # sampled tiles: the float64 recurrence
+    for b, h in ((0, 0), (B - 1, H - 1), (B // 2, H // 3)):
+        xs = {k: v[b:b + 1, :, h:h + 1] for k, v in x.items()}
+        y_ref, S_ref = _oracle(S0[b:b + 1, h:h + 1], xs, kind, dk)
+        assert _rel(y_c[b:b + 1, :, h:h + 1], y_ref, -1).max() <= Y_REL
+        assert _rel(S_c[b, h].ravel(), S_ref.ravel(), -1) <= Y_REL
 
 
 def test_prefill_between_unpack_and_pack():
