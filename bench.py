@@ -350,8 +350,11 @@ def main():
     ap.add_argument("--state-warmup", type=int, default=None,
                     help="fp32 steps that build the initial state (default: the workload's 128)")
     ap.add_argument("--prefill", type=int, default=0, metavar="T",
-                    help="measure sq_prefill_chunk instead: one chunk of T tokens per sequence "
-                         "over the workload's batch and heads (tokens/s)")
+                    help="measure the prefill instead: one chunk of T tokens per sequence over "
+                         "the workload's batch and heads (tokens/s), the matrix form "
+                         "(sq_prefill_chunkwise) with the token-serial form beside it")
+    ap.add_argument("--prefill-form", choices=("both", "chunkwise", "serial"), default="both",
+                    help="which prefill form(s) --prefill times")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before timing, copy MIB MiB device-to-device once (a plain copy of "
                          "known size for scaling HBM traffic counters)")
@@ -583,10 +586,17 @@ def measure(sq, w, args, steps=None, cache=None) -> dict:
 VALU_PEAK = 256 * 4 * 16 * 2.4e9   # non-packed fp32 lane-ops/s: CUs x SIMDs x lanes x clock
 
 
+MFMA_F32_PEAK = 157.3e12           # dense fp32 matrix-core FLOP/s (published)
+
+
 def measure_prefill(sq, w, args) -> dict:
     """One chunk of T tokens for every sequence of the workload's batch, on
-    dense fp32 states (sq_prefill_chunk, the middle step between
-    sq_pool_unpack and sq_pool_pack).  The chunk is arithmetic-bound: four
+    dense fp32 states (the middle step between sq_pool_unpack and
+    sq_pool_pack).  The matrix form (sq_prefill_chunkwise) is priced against
+    the fp32 matrix-core peak by its three state products, W S, (Q o g) S and
+    (K o G)^T U: 6 d_k d_v FLOP per token and tile (the intra-block L U, A
+    and L and the triangular solves are not counted).  The token-serial form
+    (sq_prefill_chunk) is priced against the vector issue peak by its four
     fp32 lane-ops per state element and token (decayed update, write term,
     readout, next key retrieval)."""
     import torch
@@ -600,34 +610,57 @@ def measure_prefill(sq, w, args) -> dict:
     S = torch.zeros((B, H, dk, dv), dtype=torch.float32, device="cuda")
     y = torch.empty((B, T, H, dv), dtype=torch.float32, device="cuda")
     kind = 0 if w.kind == "gdn" else 1
-
-    def chunk():
-        sq.sq_prefill_chunk(kind, H, dk, dv, B, T, S, x["q"], x["k"], x["v"], x["beta"],
-                            x["gate"], y)
-
-    for _ in range(max(args.warmup // 10, 1)):
-        chunk()
-    torch.cuda.synchronize()
     n = max(args.steps // 32, 2)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(n):
-        chunk()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / n
+    warm = max(args.warmup // 10, 1)
+
+    def timed(fn) -> float:
+        def chunk():
+            fn(kind, H, dk, dv, B, T, S, x["q"], x["k"], x["v"], x["beta"], x["gate"], y)
+        for _ in range(warm):
+            chunk()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(n):
+            chunk()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / n
+
     ops = 4.0 * dk * dv * B * H * T
-    return {"metric": "prefill tokens/s (one chunk per sequence, state in registers)",
-            "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": n,
-            "warmup": max(args.warmup // 10, 1), "ms_per_step": ms, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-            "config": {"workload": w.name, "batch": B, "heads": H, "d_k": dk, "d_v": dv,
-                       "kind": w.kind, "chunk_tokens": T},
-            "roofline": {"bound": "alu", "achieved": ops / (ms * 1e-3) / 1e12,
-                         "peak": VALU_PEAK / 1e12, "unit": "T lane-ops/s",
-                         "frac": ops / (ms * 1e-3) / VALU_PEAK, "traffic": None,
-                         "kernel": "prefill_kernel<d_k,d_v>", "launch_ms": ms,
-                         "ops_per_launch": ops}}
+    flops = 6.0 * dk * dv * B * H * T
+    serial = None
+    if args.prefill_form in ("both", "serial"):
+        ms = timed(sq.sq_prefill_chunk)
+        serial = {"kernel": "prefill_kernel<d_k,d_v>", "tokens_per_s": B * T / (ms * 1e-3),
+                  "launch_ms": ms,
+                  "roofline": {"bound": "alu", "achieved": ops / (ms * 1e-3) / 1e12,
+                               "peak": VALU_PEAK / 1e12, "unit": "T lane-ops/s",
+                               "frac": ops / (ms * 1e-3) / VALU_PEAK, "traffic": None,
+                               "ops_per_launch": ops}}
+    out = {"metric": "prefill tokens/s (one chunk per sequence, state in registers)",
+           "n_gpus": 1, "steps": n, "warmup": warm, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": w.name, "batch": B, "heads": H, "d_k": dk, "d_v": dv,
+                      "kind": w.kind, "chunk_tokens": T}}
+    if args.prefill_form == "serial":
+        out.update({"value": serial["tokens_per_s"], "unit": "tokens/s",
+                    "ms_per_step": serial["launch_ms"], "form": "serial",
+                    "roofline": dict(serial["roofline"], kernel=serial["kernel"],
+                                     launch_ms=serial["launch_ms"])})
+        return out
+    ms = timed(sq.sq_prefill_chunkwise)
+    kname = "chunk_prefill_kernel<d_k,d_v,%s>" % ("true" if kind else "false")
+    out.update({"value": B * T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+                "form": "chunkwise",
+                "roofline": {"bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12,
+                             "peak": MFMA_F32_PEAK / 1e12, "unit": "TFLOP/s",
+                             "frac": flops / (ms * 1e-3) / MFMA_F32_PEAK, "traffic": None,
+                             "kernel": kname, "launch_ms": ms, "flops_per_launch": flops}})
+    if serial is not None:
+        out["serial"] = serial
+        out["chunkwise_over_serial"] = serial["launch_ms"] / ms
+    return out
 
 
 def _summary(w, m, kernel) -> dict:

@@ -34,27 +34,23 @@ using namespace sqk;
 
 namespace {
 
-constexpr int CH = 32;        // tokens per chunk
-constexpr int CP = CH + 4;    // padded row of a [.][CH] array
-
-template <int DK, int DV, bool KDA>
+template <int DK, int DV, bool KDA, int CH>
 struct alignas(16) ChunkSmem {
-  static constexpr int KP = DK + 4, VP = DV + 4;
-  float K[CH][KP];    // keys; after the walk W (in place)
-  float Q[CH][KP];    // queries; after the walk Q o g (in place)
-  float V[CH][VP];    // values; after the solve U0 (in place)
-  float KT[DK][CP];   // (K o G_C.)^T: keys decayed to the chunk end, transposed
-  float A[CH][CP];    // strictly lower A (row t, column s)
-  float L[CH][CP];    // lower L, zero above the diagonal of its 16 x 16 blocks
-  float glast[DK];    // g over the whole chunk
-  float be[CH];
-  float al[CH];       // GDN: the chunk's gates alpha_t
-  float D[KDA ? CH : 1][KDA ? KP : 1];  // KDA: the chunk's gates d_t
-
-  __device__ __forceinline__ float gate(int t, int c) const {
-    if constexpr (KDA) return D[t][c];
-    else return al[t];
-  }
+  static constexpr int KP = DK + 4, CP = CH + 4;   // padded rows
+  float K[CH][KP];    // keys; KDA: beta_t g_t o k_t after the walk (in place)
+  float Q[CH][KP];    // queries; KDA: g_t o q_t after the walk (in place)
+  float V[CH][DV];    // values
+  float A[CH][CP];    // strictly lower A (GDN: k_t . k_s until it is scaled)
+  float L[CH][CP];    // lower L, zero above the diagonal (GDN: q_t . k_s until scaled)
+  float T[CH][CP];    // (I + A)^-1, unit lower triangular
+  float be[CH];       // beta_t
+  float glast[DK];    // g over the whole block (GDN: entry 0)
+  // GDN: the scalar gates, their prefix and suffix products and G_ts
+  float al[KDA ? 1 : CH], gp[KDA ? 1 : CH], ge[KDA ? 1 : CH];
+  float G[KDA ? 1 : CH][KDA ? 1 : CP];
+  // KDA: the channel gates and (K o G_end)^T, keys decayed to the block end
+  float D[KDA ? CH : 1][KDA ? KP : 1];
+  float KT[KDA ? DK : 1][KDA ? CP : 1];
 };
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
@@ -62,31 +58,53 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 }
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
-// x <- (I + A)^-1 x for one column held in registers (A unit lower
-// triangular, its strictly lower part in LDS; every lane reads the same row).
-template <int N>
-__device__ __forceinline__ void unit_lower_solve(const float (&A)[CH][CP], float (&x)[N]) {
+// x <- (I + A)^-1 x for one column held in registers (A strictly lower in
+// LDS, every lane reading the same row).
+template <int N, int CP>
+__device__ __forceinline__ void unit_lower_solve(const float (*A)[CP], float (&x)[N]) {
 #pragma unroll
   for (int t = 1; t < N; ++t) {
-    float acc = x[t];
+    float acc0 = x[t], acc1 = 0.f;
 #pragma unroll
     for (int s4 = 0; s4 < t; s4 += 4) {
       const f32x4 a = ld4(&A[t][s4]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (s4 + e < t) acc = fmaf(-a[e], x[s4 + e], acc);
+      for (int e = 0; e < 4; ++e) {
+        if (s4 + e >= t) continue;
+        if (e & 1) acc1 = fmaf(-a[e], x[s4 + e], acc1);
+        else acc0 = fmaf(-a[e], x[s4 + e], acc0);
+      }
     }
-    x[t] = acc;
+    x[t] = acc0 + acc1;
   }
 }
 
-template <int DK, int DV, bool KDA>
-__global__ __launch_bounds__(256) void chunk_prefill_kernel(int H, int T, float* S, const float* q,
-                                                            const float* k, const float* v,
-                                                            const float* beta, const float* gate,
-                                                            float* y) {
-  constexpr int IB = DK / 16, JB = DV / 64, TB = CH / 16, CPG = DK / 16;
-  __shared__ ChunkSmem<DK, DV, KDA> sm;
+// Column j of (I + A)^-1 into T.
+template <int CH, int CP>
+__device__ __forceinline__ void inverse_column(const float (*A)[CP], float (*T)[CP], int j) {
+  float x[CH];
+#pragma unroll
+  for (int t = 0; t < CH; ++t) x[t] = t == j ? 1.f : 0.f;
+  unit_lower_solve<CH, CP>(A, x);
+#pragma unroll
+  for (int t = 0; t < CH; ++t) T[t][j] = x[t];
+}
+
+// Sum over the LPP lanes that share a key (16: a DPP row; 32: half a wave,
+// valid in its upper 16 lanes).
+template <int LPP>
+__device__ __forceinline__ float pair_sum(float v) {
+  if constexpr (LPP == 16) return row16_sum(v);
+  else return half32_sum_hi(v);
+}
+
+template <int DK, int DV, bool KDA, int CH>
+__global__ __launch_bounds__(256, KDA ? 3 : 2) void chunk_prefill_kernel(
+    int H, int T, float* S, const float* q, const float* k, const float* v, const float* beta,
+    const float* gate, float* y) {
+  using SM = ChunkSmem<DK, DV, KDA, CH>;
+  constexpr int IB = DK / 16, JB = DV / 64, TB = CH / 16;
+  __shared__ SM sm;
   const int tile = blockIdx.x, bi = tile / H, h = tile - bi * H;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, g = l >> 4;
   const int jw = w * (DV / 4);   // first state column of this wave
@@ -102,9 +120,9 @@ __global__ __launch_bounds__(256) void chunk_prefill_kernel(int H, int T, float*
       for (int r = 0; r < 4; ++r) st[ib][jb][r] = St[(16 * ib + 4 * g + r) * DV + jw + 16 * jb + l16];
 
   for (int c0 = 0; c0 < T; c0 += CH) {
-    // ---- stage the chunk (tokens past T read as k = q = v = 0, beta = 0, gate 1)
+    // ---- stage the block (tokens past T read as k = q = v = 0, beta = 0, gate 1)
 #pragma unroll
-    for (int m = 0; m < CH * DK / 4 / 256; ++m) {
+    for (int m = 0; m < CH * DK / 1024; ++m) {
       const int e = tid + 256 * m, t = e / (DK / 4), c4 = 4 * (e % (DK / 4));
       f32x4 kv = {0.f, 0.f, 0.f, 0.f}, qv = kv, dv = {1.f, 1.f, 1.f, 1.f};
       if (c0 + t < T) {
@@ -118,7 +136,7 @@ __global__ __launch_bounds__(256) void chunk_prefill_kernel(int H, int T, float*
       if constexpr (KDA) *reinterpret_cast<f32x4*>(&sm.D[t][c4]) = dv;
     }
 #pragma unroll
-    for (int m = 0; m < CH * DV / 4 / 256; ++m) {
+    for (int m = 0; m < CH * DV / 1024; ++m) {
       const int e = tid + 256 * m, t = e / (DV / 4), c4 = 4 * (e % (DV / 4));
       f32x4 vv = {0.f, 0.f, 0.f, 0.f};
       if (c0 + t < T) vv = ld4(v + ((tok0 + c0 + t) * H + h) * DV + c4);
@@ -132,24 +150,85 @@ __global__ __launch_bounds__(256) void chunk_prefill_kernel(int H, int T, float*
     }
     __syncthreads();
 
-    // ---- A and L: lanes of a 16-lane row share a key s and split the channels
-    {
-      const int pr = tid >> 4, cg = tid & 15, cb = cg * CPG;
+    if constexpr (!KDA) {
+      // ---- GDN: k_t . k_s and q_t . k_s on the matrix cores (one 16 x 16
+      // block of the lower triangle per wave), G_ts and the gate products on
+      // the last wave
+      constexpr int NB = TB * (TB + 1) / 2;
+      if (w < NB) {
+        const int tb = w == 0 ? 0 : 1, sb = w == 2 ? 1 : 0;
+        f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int s = half ? CH - 1 - pr : pr;
-        if (cg == 0)
-          for (int t = s & ~15; t < s; ++t) sm.L[t][s] = 0.f;
-        float ks[CPG], P[CPG];
+        for (int ib = 0; ib < IB; ++ib) {
+          const f32x4 kt = ld4(&sm.K[16 * tb + l16][16 * ib + 4 * g]);
+          const f32x4 ks = ld4(&sm.K[16 * sb + l16][16 * ib + 4 * g]);
+          const f32x4 qt = ld4(&sm.Q[16 * tb + l16][16 * ib + 4 * g]);
 #pragma unroll
-        for (int c = 0; c < CPG; ++c) {
-          ks[c] = sm.K[s][cb + c];
-          P[c] = 1.f;
+          for (int r = 0; r < 4; ++r) {
+            kk = mfma4(kt[r], ks[r], kk);
+            qk = mfma4(qt[r], ks[r], qk);
+          }
         }
-        float ps = 1.f;
-        for (int t = s; t < CH; ++t) {
-          float a = 0.f, b = 0.f;
-          if constexpr (KDA) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sm.A[16 * tb + 4 * g + r][16 * sb + l16] = kk[r];
+          sm.L[16 * tb + 4 * g + r][16 * sb + l16] = qk[r];
+        }
+      } else if (w == 3 && l < CH) {
+        const int s = l;
+        float al[CH];
+#pragma unroll
+        for (int t4 = 0; t4 < CH; t4 += 4) {
+          const f32x4 a4 = ld4(&sm.al[t4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) al[t4 + e] = a4[e];
+        }
+        float P = 1.f, gpv = 1.f;
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+          if (t > s) P *= al[t];
+          if (t <= s) gpv *= al[t];
+          sm.G[t][s] = t >= s ? P : 0.f;
+        }
+        sm.ge[s] = P;           // prod_{r > s} alpha_r
+        sm.gp[s] = gpv;         // prod_{r <= s} alpha_r
+        if (s == CH - 1) sm.glast[0] = gpv;
+      }
+      __syncthreads();
+      // ---- A_ts = beta_t G_ts k_t.k_s (s < t), L_ts = G_ts q_t.k_s (s <= t),
+      // then T = (I + A)^-1, all on wave 0
+      if (w == 0) {
+#pragma unroll
+        for (int m = 0; m < CH * CH / 64; ++m) {
+          const int e = l + 64 * m, t = e / CH, s = e - t * CH;
+          const float gts = sm.G[t][s];
+          sm.A[t][s] = s < t ? sm.be[t] * gts * sm.A[t][s] : 0.f;
+          sm.L[t][s] = s <= t ? gts * sm.L[t][s] : 0.f;
+        }
+        wave_sync();
+        if (l < CH) inverse_column<CH, SM::CP>(sm.A, sm.T, l);
+      }
+      __syncthreads();
+    } else {
+      // ---- KDA: A and L on the vector units; the LPP lanes of a key s
+      // split the channels, and pairs (s, CH-1-s) balance the triangle
+      constexpr int LPP = 512 / CH, CPG = DK / LPP;
+      {
+        const int pr = tid / LPP, cg = tid % LPP, cb = cg * CPG;
+        const bool writer = cg == (LPP == 16 ? 0 : 16);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int s = half ? CH - 1 - pr : pr;
+          if (writer)
+            for (int t = s & ~15; t < s; ++t) sm.L[t][s] = 0.f;
+          float ks[CPG], P[CPG];
+#pragma unroll
+          for (int c = 0; c < CPG; ++c) {
+            ks[c] = sm.K[s][cb + c];
+            P[c] = 1.f;
+          }
+          for (int t = s; t < CH; ++t) {
+            float a = 0.f, b = 0.f;
             if (t > s) {
 #pragma unroll
               for (int c = 0; c < CPG; ++c) P[c] *= sm.D[t][cb + c];
@@ -160,78 +239,95 @@ __global__ __launch_bounds__(256) void chunk_prefill_kernel(int H, int T, float*
               a = fmaf(sm.K[t][cb + c], kp, a);
               b = fmaf(sm.Q[t][cb + c], kp, b);
             }
-          } else {
-            if (t > s) ps *= sm.al[t];
-#pragma unroll
-            for (int c = 0; c < CPG; ++c) {
-              a = fmaf(sm.K[t][cb + c], ks[c], a);
-              b = fmaf(sm.Q[t][cb + c], ks[c], b);
+            a = pair_sum<LPP>(a);
+            b = pair_sum<LPP>(b);
+            if (writer) {
+              sm.A[t][s] = sm.be[t] * a;   // the diagonal entry is never read
+              sm.L[t][s] = b;
             }
-            a *= ps;
-            b *= ps;
-          }
-          a = row16_sum(a);
-          b = row16_sum(b);
-          if (cg == 0) {
-            sm.A[t][s] = sm.be[t] * a;   // the diagonal entry is never read
-            sm.L[t][s] = b;
           }
         }
       }
-    }
-    __syncthreads();
-
-    // ---- decay walks and the unit-triangular solves, one column per lane
-    if (tid < DK) {
-      const int c = tid;
-      float ge = 1.f;
+      __syncthreads();
+      // ---- decay walks, one key channel per lane, and T = (I + A)^-1 on the
+      // last wave
+      if (tid < DK) {
+        const int c = tid;
+        float gev = 1.f;
 #pragma unroll
-      for (int t = CH - 1; t >= 0; --t) {
-        sm.KT[c][t] = sm.K[t][c] * ge;
-        ge *= sm.gate(t, c);
+        for (int t = CH - 1; t >= 0; --t) {
+          sm.KT[c][t] = sm.K[t][c] * gev;
+          gev *= sm.D[t][c];
+        }
+        sm.glast[c] = gev;
+        float gpv = 1.f;
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+          gpv *= sm.D[t][c];
+          sm.K[t][c] = sm.be[t] * gpv * sm.K[t][c];
+          sm.Q[t][c] *= gpv;
+        }
+      } else if (w == 3 && l < CH) {
+        inverse_column<CH, SM::CP>(sm.A, sm.T, l);
       }
-      sm.glast[c] = ge;
-      float x[CH], gp = 1.f;
-#pragma unroll
-      for (int t = 0; t < CH; ++t) {
-        gp *= sm.gate(t, c);
-        x[t] = sm.be[t] * sm.K[t][c] * gp;
-        sm.Q[t][c] *= gp;
-      }
-      unit_lower_solve<CH>(sm.A, x);
-#pragma unroll
-      for (int t = 0; t < CH; ++t) sm.K[t][c] = x[t];
-    } else if (tid < DK + DV) {
-      const int j = tid - DK;
-      float x[CH];
-#pragma unroll
-      for (int t = 0; t < CH; ++t) x[t] = sm.be[t] * sm.V[t][j];
-      unit_lower_solve<CH>(sm.A, x);
-#pragma unroll
-      for (int t = 0; t < CH; ++t) sm.V[t][j] = x[t];
+      __syncthreads();
     }
-    __syncthreads();
 
-    // ---- the state products on the matrix cores
-    f32x4 u[TB][JB], yv[TB][JB];
+    // ---- the state products on the matrix cores.  Z = diag(beta) V - R S
+    // with R = diag(beta) (K o g), Y = (Q o g) S + L U, U = T Z.
+    f32x4 z[TB][JB], yv[TB][JB], u[TB][JB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) z[tb][jb] = yv[tb][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ib = 0; ib < IB; ++ib) {   // z <- R S, yv <- (Q o g) S
+      f32x4 wa[TB], qa[TB];
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        wa[tb] = ld4(&sm.K[16 * tb + l16][16 * ib + 4 * g]);
+        qa[tb] = ld4(&sm.Q[16 * tb + l16][16 * ib + 4 * g]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int jb = 0; jb < JB; ++jb) {
+            z[tb][jb] = mfma4(wa[tb][r], st[ib][jb][r], z[tb][jb]);
+            yv[tb][jb] = mfma4(qa[tb][r], st[ib][jb][r], yv[tb][jb]);
+          }
+    }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tb + 4 * g + r;
+        const float bt = sm.be[t];
+        const float gt = KDA ? 1.f : sm.gp[t];
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+          const float vt = sm.V[t][jw + 16 * jb + l16];
+          if constexpr (KDA) {
+            z[tb][jb][r] = fmaf(bt, vt, -z[tb][jb][r]);
+          } else {  // GDN: the row factors beta_t g_t and g_t applied here
+            z[tb][jb][r] = bt * fmaf(-gt, z[tb][jb][r], vt);
+            yv[tb][jb][r] *= gt;
+          }
+        }
+      }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb) {
-        f32x4 ws = {0.f, 0.f, 0.f, 0.f}, yi = ws;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ib = 0; ib < IB; ++ib) {
-          const f32x4 wa = ld4(&sm.K[16 * tb + l16][16 * ib + 4 * g]);
-          const f32x4 qa = ld4(&sm.Q[16 * tb + l16][16 * ib + 4 * g]);
+        for (int sb = 0; sb <= tb; ++sb) {
+          const f32x4 ta = ld4(&sm.T[16 * tb + l16][16 * sb + 4 * g]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            ws = mfma4(wa[r], st[ib][jb][r], ws);
-            yi = mfma4(qa[r], st[ib][jb][r], yi);
-          }
+          for (int r = 0; r < 4; ++r) acc = mfma4(ta[r], z[sb][jb][r], acc);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) u[tb][jb][r] = sm.V[16 * tb + 4 * g + r][jw + 16 * jb + l16] - ws[r];
-        yv[tb][jb] = yi;
+        u[tb][jb] = acc;
       }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
@@ -249,41 +345,66 @@ __global__ __launch_bounds__(256) void chunk_prefill_kernel(int H, int T, float*
           if (c0 + t < T) y[((tok0 + c0 + t) * H + h) * DV + jw + 16 * jb + l16] = yv[tb][jb][r];
         }
       }
+    // ---- S <- diag(g_end) S + (K o G_end)^T U
+    if constexpr (!KDA) {  // GDN: G_end is a factor per token, applied to U
+#pragma unroll
+      for (int sb = 0; sb < TB; ++sb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = sm.ge[16 * sb + 4 * g + r];
+#pragma unroll
+          for (int jb = 0; jb < JB; ++jb) u[sb][jb][r] *= e;
+        }
+    }
+    const float gl0 = KDA ? 0.f : sm.glast[0];
 #pragma unroll
     for (int ib = 0; ib < IB; ++ib) {
-      const f32x4 gl = ld4(&sm.glast[16 * ib + 4 * g]);
+      f32x4 gl, ka[TB];
+      if constexpr (KDA) gl = ld4(&sm.glast[16 * ib + 4 * g]);
+      else gl = f32x4{gl0, gl0, gl0, gl0};
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb) {
+      for (int sb = 0; sb < TB; ++sb) {
+        if constexpr (KDA) {
+          ka[sb] = ld4(&sm.KT[16 * ib + l16][16 * sb + 4 * g]);
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) st[ib][jb][r] *= gl[r];
-#pragma unroll
-        for (int sb = 0; sb < TB; ++sb) {
-          const f32x4 ka = ld4(&sm.KT[16 * ib + l16][16 * sb + 4 * g]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) st[ib][jb] = mfma4(ka[r], u[sb][jb][r], st[ib][jb]);
+          for (int r = 0; r < 4; ++r) ka[sb][r] = sm.K[16 * sb + 4 * g + r][16 * ib + l16];
         }
       }
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        st[ib][jb] *= gl;
+#pragma unroll
+        for (int sb = 0; sb < TB; ++sb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) st[ib][jb] = mfma4(ka[sb][r], u[sb][jb][r], st[ib][jb]);
+      }
     }
-    __syncthreads();   // the next chunk overwrites every array
+    __syncthreads();   // the next block overwrites every array
   }
 
+  // (the lane offset passes through an empty asm so that the compiler does
+  // not keep the initial load's 64 addresses alive across the loop)
+  float* So = St + opaque(4 * g * DV + jw + l16);
 #pragma unroll
   for (int ib = 0; ib < IB; ++ib)
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) St[(16 * ib + 4 * g + r) * DV + jw + 16 * jb + l16] = st[ib][jb][r];
+      for (int r = 0; r < 4; ++r) So[(16 * ib + r) * DV + 16 * jb] = st[ib][jb][r];
 }
 
+// Tokens per block: 32 for GDN (two workgroups per CU fit in LDS), 16 for
+// KDA (its channel gates and decayed keys double the block's LDS).
 template <int DK, int DV>
 hipError_t launch(int kind, int H, int B, int T, float* S, const float* q, const float* k,
                   const float* v, const float* beta, const float* gate, float* y, hipStream_t s) {
   if (kind == SQ_KIND_KDA)
-    hipLaunchKernelGGL((chunk_prefill_kernel<DK, DV, true>), dim3(B * H), dim3(256), 0, s, H, T, S,
-                       q, k, v, beta, gate, y);
+    hipLaunchKernelGGL((chunk_prefill_kernel<DK, DV, true, 16>), dim3(B * H), dim3(256), 0, s, H,
+                       T, S, q, k, v, beta, gate, y);
   else
-    hipLaunchKernelGGL((chunk_prefill_kernel<DK, DV, false>), dim3(B * H), dim3(256), 0, s, H, T, S,
-                       q, k, v, beta, gate, y);
+    hipLaunchKernelGGL((chunk_prefill_kernel<DK, DV, false, 32>), dim3(B * H), dim3(256), 0, s, H,
+                       T, S, q, k, v, beta, gate, y);
   return hipGetLastError();
 }
 
