@@ -351,16 +351,15 @@ sq_status sq_prefill_chunk(int32_t kind, int32_t heads, int32_t d_k, int32_t d_v
                            hipStream_t stream);
 
 /* The same chunk in matrix form ([SQ] App. F.1's chunk kernel; the
- * recurrence of [SQ] Sec. 3, Eq. 1 unrolled over blocks of 32 tokens): per
+ * recurrence of [SQ] Sec. 3, Eq. 1 unrolled over blocks of 16 tokens): per
  * block, the decay products, the strictly lower A_ts = beta_t sum_c k_tc
- * G_tsc k_sc and L_ts = sum_c q_tc G_tsc k_sc (G_ts = prod_{s<r<=t} d_r) and
- * two unit-triangular solves give W = (I+A)^-1 diag(beta)(K o g) and
- * U0 = (I+A)^-1 diag(beta) V; then U = U0 - W S, Y = (Q o g) S + L U and
- * S <- diag(g_end) S + (K o G_end)^T U run on the fp32 matrix cores.  Same
- * arguments, layouts, ownership and errors as sq_prefill_chunk; the results
- * equal it up to rounding order (no intermediate leaves the chip: the
- * workgroup of a (sequence, head) keeps the state in registers and the
- * block's intermediates in LDS). */
+ * G_tsc k_sc, the lower L_ts = sum_c q_tc G_tsc k_sc (G_ts = prod_{s<r<=t}
+ * d_r) and T = (I+A)^-1; then U = T (diag(beta) V - diag(beta)(K o g) S),
+ * Y = (Q o g) S + L U and S <- diag(g_end) S + (K o G_end)^T U on the fp32
+ * matrix cores.  Same arguments, layouts, ownership and errors as
+ * sq_prefill_chunk; the results equal it up to rounding order (no
+ * intermediate leaves the chip: the workgroup of a (sequence, head) keeps
+ * the state in registers and the block's intermediates in LDS). */
 sq_status sq_prefill_chunkwise(int32_t kind, int32_t heads, int32_t d_k, int32_t d_v,
                                int32_t batch, int32_t T, float* S, const float* q, const float* k,
                                const float* v, const float* beta, const float* gate, float* y,

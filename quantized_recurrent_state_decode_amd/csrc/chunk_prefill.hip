@@ -2,7 +2,7 @@
 //
 // The serving flow runs a prompt through a chunk kernel between unpacking the
 // active states and packing the boundary states (STEPQuant App. F.1).  Over a
-// chunk of C tokens starting from state S0, the recurrence
+// block of C tokens starting from state S0, the recurrence
 //   S_t = D_t S_{t-1} + k_t u_t^T,   u_t = beta_t (v_t - (D_t S_{t-1})^T k_t),
 //   y_t = S_t^T q_t                    (STEPQuant Sec. 3, Eq. 1),
 // unrolls with the decay products g_t = prod_{r<=t} d_r (per key row) and
@@ -10,24 +10,30 @@
 //   (I + A) U = diag(beta) V - diag(beta) (K o g) S0,
 //   A_ts = beta_t sum_c k_tc G_tsc k_sc            (s < t),
 //   Y    = (Q o g) S0 + L U,  L_ts = sum_c q_tc G_tsc k_sc   (s <= t),
-//   S_C  = diag(g_C) S0 + (K o G_C.)^T U,
-// so with W = (I + A)^-1 diag(beta) (K o g) and U0 = (I + A)^-1 diag(beta) V,
-// U = U0 - W S0.  The three state products W S0, (Q o g) S0 and (K o G)^T U
-// and the intra-chunk L U are fp32 matrix-core products (v_mfma_f32_16x16x4);
-// the decay products, A, L and the unit-triangular solves are vector work.
+//   S_C  = diag(g_C) S0 + (K o G_C.)^T U.
+// With T = (I + A)^-1 (unit lower triangular, one column per lane) and
+// R = diag(beta) (K o g): U = T (diag(beta) V - R S0).  The products R S0,
+// (Q o g) S0, T Z, L U and (K o G_C.)^T U are fp32 matrix-core products
+// (v_mfma_f32_16x16x4); G enters as exact running products, never as a
+// ratio of prefix products, so gates of 0 stay exact.  For GDN the decays are
+// one factor per token: k_t.k_s and q_t.k_s are matrix-core products too, and
+// g, beta and G_C. scale rows of the products in registers instead of copies
+// of K and Q.  For KDA the decays differ per key channel: A and L are summed
+// on the vector units with a running product per channel, and a walk per
+// channel writes beta g o k, g o q and the keys decayed to the block end.
 // The result equals the token-serial recurrence up to rounding order.
 //
 // One workgroup of 4 waves runs one (sequence, head) tile through all its
-// chunks.  The state stays in registers in the matrix-core accumulator
+// blocks.  The state stays in registers in the matrix-core accumulator
 // layout: wave w owns state columns [w d_v/4, (w+1) d_v/4), and a lane holds
 // rows 16 ib + 4 (lane / 16) + r (r = 0..3) of column 16 jb + lane % 16 of
 // each 16 x 16 block.  Because a product's reduction index may be permuted
-// freely, that same register serves as the B operand of (W S0), whose k-step r
-// of row block ib takes rows 16 ib + 4 (lane / 16) + r, and the U block that
-// (W S0) produces serves as the B operand of L U and (K o G)^T U the same way.
-// Every B operand is a register; every A operand is a 16-byte LDS read.  The
-// columns of the state evolve independently (D_t acts on rows), so the four
-// waves need no exchange in the product phase.
+// freely, that same register serves as the B operand of R S0, whose k-step r
+// of row block ib takes rows 16 ib + 4 (lane / 16) + r, and the Z and U
+// blocks the products leave in that layout serve as B operands of T Z, L U
+// and (K o G_C.)^T U the same way.  Every B operand is a register; every A
+// operand is an LDS read.  The columns of the state evolve independently
+// (D_t acts on rows), so the four waves need no exchange in the products.
 #include "tile_common.h"
 
 using namespace sqk;
@@ -35,22 +41,23 @@ using namespace sqk;
 namespace {
 
 template <int DK, int DV, bool KDA, int CH>
-struct alignas(16) ChunkSmem {
+struct ChunkSmem {
   static constexpr int KP = DK + 4, CP = CH + 4;   // padded rows
-  float K[CH][KP];    // keys; KDA: beta_t g_t o k_t after the walk (in place)
-  float Q[CH][KP];    // queries; KDA: g_t o q_t after the walk (in place)
-  float V[CH][DV];    // values
-  float A[CH][CP];    // strictly lower A (GDN: k_t . k_s until it is scaled)
-  float L[CH][CP];    // lower L, zero above the diagonal (GDN: q_t . k_s until scaled)
-  float T[CH][CP];    // (I + A)^-1, unit lower triangular
-  float be[CH];       // beta_t
-  float glast[DK];    // g over the whole block (GDN: entry 0)
-  // GDN: the scalar gates, their prefix and suffix products and G_ts
-  float al[KDA ? 1 : CH], gp[KDA ? 1 : CH], ge[KDA ? 1 : CH];
-  float G[KDA ? 1 : CH][KDA ? 1 : CP];
+  alignas(16) float K[CH][KP];    // keys; KDA: beta_t g_t o k_t after the walk (in place)
+  alignas(16) float Q[CH][KP];    // queries; KDA: g_t o q_t after the walk (in place)
+  alignas(16) float V[CH][DV];    // values
+  alignas(16) float A[CH][CP];    // strictly lower A
+  alignas(16) float L[CH][CP];    // lower L, zero above the diagonal
+  alignas(16) float T[CH][CP];    // (I + A)^-1, unit lower triangular
+  alignas(16) float be[CH];       // beta_t
+  alignas(16) float glast[DK];    // g over the whole block (GDN: entry 0)
+  // GDN: the scalar gates and their prefix and suffix products
+  alignas(16) float al[KDA ? 1 : CH];
+  alignas(16) float gp[KDA ? 1 : CH];
+  alignas(16) float ge[KDA ? 1 : CH];
   // KDA: the channel gates and (K o G_end)^T, keys decayed to the block end
-  float D[KDA ? CH : 1][KDA ? KP : 1];
-  float KT[KDA ? DK : 1][KDA ? CP : 1];
+  alignas(16) float D[KDA ? CH : 1][KDA ? KP : 1];
+  alignas(16) float KT[KDA ? DK : 1][KDA ? CP : 1];
 };
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
@@ -99,7 +106,7 @@ __device__ __forceinline__ float pair_sum(float v) {
 }
 
 template <int DK, int DV, bool KDA, int CH>
-__global__ __launch_bounds__(256, KDA ? 3 : 2) void chunk_prefill_kernel(
+__global__ __launch_bounds__(256, 3) void chunk_prefill_kernel(
     int H, int T, float* S, const float* q, const float* k, const float* v, const float* beta,
     const float* gate, float* y) {
   using SM = ChunkSmem<DK, DV, KDA, CH>;
@@ -169,45 +176,42 @@ __global__ __launch_bounds__(256, KDA ? 3 : 2) void chunk_prefill_kernel(
             qk = mfma4(qt[r], ks[r], qk);
           }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sm.A[16 * tb + 4 * g + r][16 * sb + l16] = kk[r];
-          sm.L[16 * tb + 4 * g + r][16 * sb + l16] = qk[r];
-        }
-      } else if (w == 3 && l < CH) {
-        const int s = l;
-        float al[CH];
+        // this lane's entries: t = t0 + r (r = 0..3), s; G_ts = prod_{s<r'<=t} alpha_r'
+        const int t0 = 16 * tb + 4 * g, s = 16 * sb + l16;
+        float P = 1.f;
 #pragma unroll
         for (int t4 = 0; t4 < CH; t4 += 4) {
           const f32x4 a4 = ld4(&sm.al[t4]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) al[t4 + e] = a4[e];
+          for (int e = 0; e < 4; ++e) P *= (t4 + e > s && t4 + e <= t0) ? a4[e] : 1.f;
         }
-        float P = 1.f, gpv = 1.f;
+        const f32x4 at = ld4(&sm.al[t0]), bt = ld4(&sm.be[t0]);
 #pragma unroll
-        for (int t = 0; t < CH; ++t) {
-          if (t > s) P *= al[t];
-          if (t <= s) gpv *= al[t];
-          sm.G[t][s] = t >= s ? P : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + r;
+          if (r > 0 && t > s) P *= at[r];
+          sm.A[t][s] = s < t ? bt[r] * P * kk[r] : 0.f;
+          sm.L[t][s] = s <= t ? P * qk[r] : 0.f;
         }
-        sm.ge[s] = P;           // prod_{r > s} alpha_r
-        sm.gp[s] = gpv;         // prod_{r <= s} alpha_r
+      } else if (w == 3 && l < CH) {   // the gate products of the block
+        const int s = l;
+        float gpv = 1.f, gev = 1.f;
+#pragma unroll
+        for (int t4 = 0; t4 < CH; t4 += 4) {
+          const f32x4 a4 = ld4(&sm.al[t4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (t4 + e <= s) gpv *= a4[e];
+            else gev *= a4[e];
+          }
+        }
+        sm.gp[s] = gpv;   // prod_{r <= s} alpha_r
+        sm.ge[s] = gev;   // prod_{r > s} alpha_r
         if (s == CH - 1) sm.glast[0] = gpv;
       }
       __syncthreads();
-      // ---- A_ts = beta_t G_ts k_t.k_s (s < t), L_ts = G_ts q_t.k_s (s <= t),
-      // then T = (I + A)^-1, all on wave 0
-      if (w == 0) {
-#pragma unroll
-        for (int m = 0; m < CH * CH / 64; ++m) {
-          const int e = l + 64 * m, t = e / CH, s = e - t * CH;
-          const float gts = sm.G[t][s];
-          sm.A[t][s] = s < t ? sm.be[t] * gts * sm.A[t][s] : 0.f;
-          sm.L[t][s] = s <= t ? gts * sm.L[t][s] : 0.f;
-        }
-        wave_sync();
-        if (l < CH) inverse_column<CH, SM::CP>(sm.A, sm.T, l);
-      }
+      // ---- T = (I + A)^-1 on wave 0
+      if (w == 0 && l < CH) inverse_column<CH, SM::CP>(sm.A, sm.T, l);
       __syncthreads();
     } else {
       // ---- KDA: A and L on the vector units; the LPP lanes of a key s
@@ -394,8 +398,10 @@ __global__ __launch_bounds__(256, KDA ? 3 : 2) void chunk_prefill_kernel(
       for (int r = 0; r < 4; ++r) So[(16 * ib + r) * DV + 16 * jb] = st[ib][jb][r];
 }
 
-// Tokens per block: 32 for GDN (two workgroups per CU fit in LDS), 16 for
-// KDA (its channel gates and decayed keys double the block's LDS).
+// Blocks of 16 tokens: 30 KB (GDN) and 48 KB (KDA) of LDS and at most 168
+// registers per lane hold three workgroups per CU, whose phases overlap.
+// (Blocks of 32 measured 13-22 % slower on the large batches: they fit two
+// workgroups, and the longer triangular solve runs on one wave.)
 template <int DK, int DV>
 hipError_t launch(int kind, int H, int B, int T, float* S, const float* q, const float* k,
                   const float* v, const float* beta, const float* gate, float* y, hipStream_t s) {
@@ -403,7 +409,7 @@ hipError_t launch(int kind, int H, int B, int T, float* S, const float* q, const
     hipLaunchKernelGGL((chunk_prefill_kernel<DK, DV, true, 16>), dim3(B * H), dim3(256), 0, s, H,
                        T, S, q, k, v, beta, gate, y);
   else
-    hipLaunchKernelGGL((chunk_prefill_kernel<DK, DV, false, 32>), dim3(B * H), dim3(256), 0, s, H,
+    hipLaunchKernelGGL((chunk_prefill_kernel<DK, DV, false, 16>), dim3(B * H), dim3(256), 0, s, H,
                        T, S, q, k, v, beta, gate, y);
   return hipGetLastError();
 }

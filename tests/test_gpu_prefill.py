@@ -55,8 +55,8 @@ def _run(form, kind, H, dk, dv, B, T, S0, x):
     return y.cpu().numpy(), S.cpu().numpy()
 
 
-# T spans one token, a ragged single block, whole blocks of 32 and ragged
-# multi-block tails for the chunkwise form
+# T spans one token, ragged single blocks, whole blocks and ragged
+# multi-block tails for the chunkwise form (blocks of 16 tokens)
 @pytest.mark.parametrize("form", list(FORMS))
 @pytest.mark.parametrize("kind,shape,T", [("gdn", (128, 128), 1), ("gdn", (128, 128), 130),
                                           ("kda", (128, 128), 37), ("gdn", (64, 64), 5),
