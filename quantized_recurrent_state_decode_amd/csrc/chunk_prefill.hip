@@ -225,23 +225,19 @@ __global__ __launch_bounds__(256, 3) void chunk_prefill_kernel(
           const int s = half ? CH - 1 - pr : pr;
           if (writer)
             for (int t = s & ~15; t < s; ++t) sm.L[t][s] = 0.f;
-          float ks[CPG], P[CPG];
+          float kp[CPG];   // k_s decayed to token t: k_sc G_tsc, a running product
 #pragma unroll
-          for (int c = 0; c < CPG; ++c) {
-            ks[c] = sm.K[s][cb + c];
-            P[c] = 1.f;
-          }
+          for (int c = 0; c < CPG; ++c) kp[c] = sm.K[s][cb + c];
           for (int t = s; t < CH; ++t) {
             float a = 0.f, b = 0.f;
             if (t > s) {
 #pragma unroll
-              for (int c = 0; c < CPG; ++c) P[c] *= sm.D[t][cb + c];
+              for (int c = 0; c < CPG; ++c) kp[c] *= sm.D[t][cb + c];
             }
 #pragma unroll
             for (int c = 0; c < CPG; ++c) {
-              const float kp = ks[c] * P[c];
-              a = fmaf(sm.K[t][cb + c], kp, a);
-              b = fmaf(sm.Q[t][cb + c], kp, b);
+              a = fmaf(sm.K[t][cb + c], kp[c], a);
+              b = fmaf(sm.Q[t][cb + c], kp[c], b);
             }
             a = pair_sum<LPP>(a);
             b = pair_sum<LPP>(b);
@@ -253,8 +249,9 @@ __global__ __launch_bounds__(256, 3) void chunk_prefill_kernel(
         }
       }
       __syncthreads();
-      // ---- decay walks, one key channel per lane, and T = (I + A)^-1 on the
-      // last wave
+      // ---- decay walks, two lanes per key channel (the keys decayed to the
+      // block end, then beta g o k in place; g o q), and T = (I + A)^-1 on
+      // the last wave
       if (tid < DK) {
         const int c = tid;
         float gev = 1.f;
@@ -269,11 +266,17 @@ __global__ __launch_bounds__(256, 3) void chunk_prefill_kernel(
         for (int t = 0; t < CH; ++t) {
           gpv *= sm.D[t][c];
           sm.K[t][c] = sm.be[t] * gpv * sm.K[t][c];
+        }
+      } else if (tid < 2 * DK) {
+        const int c = tid - DK;
+        float gpv = 1.f;
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+          gpv *= sm.D[t][c];
           sm.Q[t][c] *= gpv;
         }
-      } else if (w == 3 && l < CH) {
-        inverse_column<CH, SM::CP>(sm.A, sm.T, l);
       }
+      if (w == 3 && l < CH) inverse_column<CH, SM::CP>(sm.A, sm.T, l);
       __syncthreads();
     }
 

@@ -104,6 +104,24 @@ def test_prefill_degenerate_gates(form, kind):
     assert _rel(S.reshape(B * H, -1), S_ref.reshape(B * H, -1), -1).max() <= Y_REL
 
 
+@pytest.mark.parametrize("form", list(FORMS))
+@pytest.mark.parametrize("kind,shape", [("gdn", (128, 128)), ("kda", (128, 64))])
+def test_prefill_long_sequence(form, kind, shape):
+    """One long prompt (2,048 tokens, 128 blocks of the chunkwise form) from
+    the warm-up state: the error of the block products must not build up
+    over the blocks."""
+    dk, dv = shape
+    B, H, T = 1, 2, 2048
+    w = SI.workload("gdn_mid_step6" if kind == "gdn" else "kda_step6", batch=B, n_slots=B,
+                    heads=H, d_k=dk, d_v=dv)
+    S0 = oracle_warmup(w, 16)
+    x = _chunk(w, T, SI.gate_params(w))
+    y, S = _run(form, kind, H, dk, dv, B, T, S0, x)
+    y_ref, S_ref = _oracle(S0.astype(np.float32), x, kind, dk)
+    assert _rel(y, y_ref, -1).max() <= Y_REL
+    assert _rel(S.reshape(B * H, -1), S_ref.reshape(B * H, -1), -1).max() <= Y_REL
+
+
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
 def test_chunkwise_prefill_at_bench_size(kind):
     """The launch bench.py times for --prefill 256 (64 sequences x 16 heads
