@@ -150,7 +150,8 @@ def test_chunkwise_prefill_at_bench_size(kind):
         assert _rel(S_c[b, h].ravel(), S_ref.ravel(), -1) <= Y_REL
 
 
-def test_prefill_between_unpack_and_pack():
+@pytest.mark.parametrize("form", list(FORMS))
+def test_prefill_between_unpack_and_pack(form):
     """A STEP pool (every width and an FP16 head): unpack the live slots, run a
     20-token chunk, pack the boundary states back.  The chunk's outputs and
     final states follow the recurrence from the unpacked states, and the pack
@@ -172,8 +173,8 @@ def test_prefill_between_unpack_and_pack():
     x = _chunk(w, T, SI.gate_params(w))
     dx = {k: to_dev(v) for k, v in x.items()}
     y = torch.empty((3, T, H, d), dtype=torch.float32, device="cuda")
-    sq.sq_prefill_chunk(sq.SQ_KIND_GDN, H, d, d, 3, T, S, dx["q"], dx["k"], dx["v"], dx["beta"],
-                        dx["gate"], y)
+    getattr(sq, FORMS[form])(sq.SQ_KIND_GDN, H, d, d, 3, T, S, dx["q"], dx["k"], dx["v"],
+                             dx["beta"], dx["gate"], y)
     torch.cuda.synchronize()
     S_end = S.cpu().numpy()
     y_ref, S_ref = _oracle(S_start, x, "gdn", d)
