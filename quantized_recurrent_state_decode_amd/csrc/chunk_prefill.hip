@@ -97,12 +97,23 @@ __device__ __forceinline__ void inverse_column(const float (*A)[CP], float (*T)[
   for (int t = 0; t < CH; ++t) T[t][j] = x[t];
 }
 
-// Sum over the LPP lanes that share a key (16: a DPP row; 32: half a wave,
-// valid in its upper 16 lanes).
+// Two sums over the LPP lanes that share a key (16: a DPP row; 32: two rows)
+// in one reduction: the even lane of each pair keeps a, the odd lane b, then
+// the rotations by 2, 4 and 8 within a row keep each lane's parity, and the
+// row exchange adds the other row.  Even lanes return the sum of a, odd
+// lanes the sum of b.
 template <int LPP>
-__device__ __forceinline__ float pair_sum(float v) {
-  if constexpr (LPP == 16) return row16_sum(v);
-  else return half32_sum_hi(v);
+__device__ __forceinline__ float pair_sum2(float a, float b, bool odd) {
+  float v = (odd ? b : a) + dpp_f<0xB1>(odd ? a : b);   // quad_perm xor 1
+  v += dpp_f<0x122>(v);                                  // row_ror:2
+  v += dpp_f<0x124>(v);                                  // row_ror:4
+  v += dpp_f<0x128>(v);                                  // row_ror:8
+  if constexpr (LPP == 32) {
+    float x, y;
+    swap16(v, x, y);
+    v = x + y;
+  }
+  return v;
 }
 
 template <int DK, int DV, bool KDA, int CH>
@@ -215,35 +226,53 @@ __global__ __launch_bounds__(256, 3) void chunk_prefill_kernel(
       __syncthreads();
     } else {
       // ---- KDA: A and L on the vector units; the LPP lanes of a key s
-      // split the channels, and pairs (s, CH-1-s) balance the triangle
+      // split the channels and carry k_s decayed to token t (k_sc G_tsc, a
+      // running product), pairs (s, CH-1-s) balance the triangle, and the
+      // rows of token t + 1 are read while token t is reduced
       constexpr int LPP = 512 / CH, CPG = DK / LPP;
       {
         const int pr = tid / LPP, cg = tid % LPP, cb = cg * CPG;
-        const bool writer = cg == (LPP == 16 ? 0 : 16);
+        const bool odd = cg & 1;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int s = half ? CH - 1 - pr : pr;
-          if (writer)
-            for (int t = s & ~15; t < s; ++t) sm.L[t][s] = 0.f;
-          float kp[CPG];   // k_s decayed to token t: k_sc G_tsc, a running product
+          if (cg < 16) {   // L is zero above the diagonal of its 16 x 16 blocks
+            const int t = (s & ~15) + cg;
+            if (t < s) sm.L[t][s] = 0.f;
+          }
+          float kp[CPG], kn[CPG], qn[CPG], dn[CPG];
 #pragma unroll
-          for (int c = 0; c < CPG; ++c) kp[c] = sm.K[s][cb + c];
+          for (int c = 0; c < CPG; ++c) {
+            kp[c] = kn[c] = sm.K[s][cb + c];
+            qn[c] = sm.Q[s][cb + c];
+            dn[c] = 1.f;
+          }
           for (int t = s; t < CH; ++t) {
-            float a = 0.f, b = 0.f;
-            if (t > s) {
-#pragma unroll
-              for (int c = 0; c < CPG; ++c) kp[c] *= sm.D[t][cb + c];
-            }
+            float kt[CPG], qt[CPG];
 #pragma unroll
             for (int c = 0; c < CPG; ++c) {
-              a = fmaf(sm.K[t][cb + c], kp[c], a);
-              b = fmaf(sm.Q[t][cb + c], kp[c], b);
+              kt[c] = kn[c];
+              qt[c] = qn[c];
+              kp[c] *= dn[c];   // 1 at t = s
             }
-            a = pair_sum<LPP>(a);
-            b = pair_sum<LPP>(b);
-            if (writer) {
-              sm.A[t][s] = sm.be[t] * a;   // the diagonal entry is never read
-              sm.L[t][s] = b;
+            if (t + 1 < CH) {
+#pragma unroll
+              for (int c = 0; c < CPG; ++c) {
+                kn[c] = sm.K[t + 1][cb + c];
+                qn[c] = sm.Q[t + 1][cb + c];
+                dn[c] = sm.D[t + 1][cb + c];
+              }
+            }
+            float a = 0.f, b = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPG; ++c) {
+              a = fmaf(kt[c], kp[c], a);
+              b = fmaf(qt[c], kp[c], b);
+            }
+            const float sum = pair_sum2<LPP>(a, b, odd);
+            if (cg < 2) {   // lane 0 writes A (the diagonal entry is never read), lane 1 L
+              if (odd) sm.L[t][s] = sum;
+              else sm.A[t][s] = sm.be[t] * sum;
             }
           }
         }
