@@ -355,6 +355,9 @@ def main():
                          "(sq_prefill_chunkwise) with the token-serial form beside it")
     ap.add_argument("--prefill-form", choices=("both", "chunkwise", "serial"), default="both",
                     help="which prefill form(s) --prefill times")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill block of the default line (both prefill forms on the "
+                         "64 x 16-head GDN and 64 x 32-head KDA shapes)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before timing, copy MIB MiB device-to-device once (a plain copy of "
                          "known size for scaling HBM traffic counters)")
@@ -442,6 +445,8 @@ def main():
     if w.name == DEFAULT_WORKLOAD and not args.no_configs:
         out["configs"] = configs_block(sq, args, cache)
         out["cache_assisted"] = cache_assisted(sq, args, cache)
+    if w.name == DEFAULT_WORKLOAD and not args.no_prefill:
+        out["prefill"] = prefill_block(sq, args)
     if w.name == DEFAULT_WORKLOAD and not args.no_compare:
         out["same_hardware"] = same_hardware(sq, args, out["value"], cache)
     elif w.name in DENSE_TWIN and not args.no_compare:
@@ -710,6 +715,26 @@ def configs_block(sq, args, cache) -> dict:
         if name == "tiny_gdn_int8":
             res[name]["note"] = "one 64 x 64 tile per step: launch-latency bound, steps/s only"
         del m
+        torch.cuda.empty_cache()
+    return res
+
+
+def prefill_block(sq, args) -> list:
+    """The prefill chunk beside the decode line: both forms (matrix form on
+    the fp32 matrix cores, token-serial on the vector units) on one chunk per
+    sequence, 8 timed launches each."""
+    import argparse as _ap
+    import torch
+    from synth import inputs as SI
+    res = []
+    for name, over, T in (("gdn_mid_step6", {}, 256),
+                          ("kda_step6", {"batch": 64, "n_slots": 64}, 128)):
+        a = _ap.Namespace(**vars(args))
+        a.prefill, a.prefill_form, a.steps, a.warmup = T, "both", 256, 50
+        r = measure_prefill(sq, SI.workload(name, **over), a)
+        res.append({"config": r["config"], "tokens_per_s": r["value"], "launch_ms": r["ms_per_step"],
+                    "roofline": r["roofline"], "serial": r["serial"],
+                    "chunkwise_over_serial": r["chunkwise_over_serial"]})
         torch.cuda.empty_cache()
     return res
 
