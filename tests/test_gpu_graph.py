@@ -4,7 +4,8 @@ then replays the graph three times; between replays the same three steps run
 eagerly on the twin, with synchronisations.  After every replay the two pools
 and the readouts must be bit-identical.  Cases: the split GDN launch (pool
 shape), a uniform plan, KDA rows of mixed widths, and the window, whose
-rebuild at p = 4 falls inside the captured steps."""
+rebuild at p = 4 falls inside the captured steps.  The prefill forms are
+captured and replayed the same way."""
 import numpy as np
 import pytest
 
@@ -70,5 +71,52 @@ def test_graph_replays_match_eager(kind):
         torch.cuda.synchronize()
         assert torch.equal(pa.pool, pb.pool), f"pools differ after replay {r}"
         assert torch.equal(ya, yb), f"readouts differ after replay {r}"
+        assert bool(torch.isfinite(ya).all())
+    del g
+
+
+@pytest.mark.parametrize("form,kind", [("sq_prefill_chunkwise", "gdn"), ("sq_prefill_chunkwise", "kda"),
+                                       ("sq_prefill_chunk", "gdn")])
+def test_prefill_graph_replays_match_eager(form, kind):
+    """Two prefill chunks (37 tokens: two whole blocks and a ragged one of the
+    matrix form) captured on one state and replayed three times; between
+    replays the same chunks run eagerly on a twin state.  States and outputs
+    must be bit-identical after every replay (neither form allocates, clears
+    memory or sums with atomics)."""
+    import torch
+    B, H, d, T = 3, 4, 128, 37
+    w = SI.workload("gdn_mid_step6" if kind == "gdn" else "kda_step6", batch=B, n_slots=B,
+                    heads=H)
+    params = SI.gate_params(w)
+    chunks = []
+    for c in range(2):
+        steps = [SI.step_inputs(w, c * T + t, params) for t in range(T)]
+        chunks.append({k: to_dev(np.ascontiguousarray(np.stack([s[k] for s in steps], axis=1)))
+                       for k in steps[0]})
+    gen = torch.Generator(device="cuda").manual_seed(97)
+    Sa = 0.05 * torch.randn((B, H, d, d), generator=gen, device="cuda")
+    Sb = Sa.clone()
+    ya = torch.zeros((2, B, T, H, d), dtype=torch.float32, device="cuda")
+    yb = torch.zeros_like(ya)
+    knd = sq.SQ_KIND_GDN if kind == "gdn" else sq.SQ_KIND_KDA
+    fn = getattr(sq, form)
+
+    def run(S, y):
+        for c, x in enumerate(chunks):
+            fn(knd, H, d, d, B, T, S, x["q"], x["k"], x["v"], x["beta"], x["gate"], y[c])
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(Sa, ya)
+    torch.cuda.synchronize()
+    assert torch.equal(Sa, Sb), "capture must not execute the chunks"
+    for r in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        run(Sb, yb)
+        torch.cuda.synchronize()
+        assert torch.equal(Sa, Sb), f"states differ after replay {r}"
+        assert torch.equal(ya, yb), f"outputs differ after replay {r}"
         assert bool(torch.isfinite(ya).all())
     del g
