@@ -62,7 +62,9 @@ def _run(form, kind, H, dk, dv, B, T, S0, x):
                                           ("kda", (128, 128), 37), ("gdn", (64, 64), 5),
                                           ("kda", (128, 64), 64), ("gdn", (64, 128), 9),
                                           ("kda", (64, 64), 97), ("gdn", (128, 64), 32),
-                                          ("kda", (64, 128), 33), ("kda", (128, 128), 160)])
+                                          ("kda", (64, 128), 33), ("kda", (128, 128), 160),
+                                          ("kda", (128, 128), 1), ("kda", (64, 64), 16),
+                                          ("gdn", (64, 64), 17)])
 def test_prefill_chunk_matches_recurrence(form, kind, shape, T):
     dk, dv = shape
     w = SI.workload("gdn_mid_step6" if kind == "gdn" else "kda_step6", batch=3, n_slots=3,
